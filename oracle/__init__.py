@@ -1,0 +1,155 @@
+"""int3-g64 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+A thin ctypes binding over liboracle.so (plain scalar C in oracle.c).  Only the
+test suite, the smoke check and the benchmark's CPU-baseline leg may import
+this package; the product library never does.  Every function mirrors one in
+oracle.h, which cites the passage of the pages each one follows.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.SO):
+            _build.build()
+        L = C.CDLL(_build.SO)
+        P, I64, I32, F32 = C.c_void_p, C.c_int64, C.c_int, C.c_float
+        L.qto_groups.restype = I64
+        L.qto_groups.argtypes = [I64]
+        L.qto_packed_bytes.restype = I64
+        L.qto_packed_bytes.argtypes = [I64, I64]
+        L.qto_grid_factor.restype = F32
+        L.qto_grid_factor.argtypes = [I32, I32, F32, F32]
+        L.qto_quantize_g64.argtypes = [P, I64, I64, P, I32, F32, F32, P, P, P, P]
+        L.qto_pack_i3.argtypes = [P, I64, I64, P]
+        L.qto_unpack_i3.argtypes = [P, I64, I64, P]
+        L.qto_matvec_f64.argtypes = [P, P, I64, I64, P, P, P]
+        L.qto_matmul_f64_sampled.argtypes = [P, P, I64, I64, P, I64, I64, P, P, P, P]
+        L.qto_matvec_f32.argtypes = [P, P, I64, I64, P, P]
+        L.qto_hessian_diag.argtypes = [P, I64, I64, P, P]
+        L.qto_rowint_recon.argtypes = [P, I64, I64, I32, P]
+        L.qto_dequant_f64.argtypes = [P, P, I64, I64, P]
+        for f in ("qto_quantize_g64", "qto_pack_i3", "qto_unpack_i3", "qto_matvec_f64",
+                  "qto_matmul_f64_sampled", "qto_matvec_f32", "qto_hessian_diag",
+                  "qto_rowint_recon", "qto_dequant_f64"):
+            getattr(L, f).restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def groups(I: int) -> int:
+    return int(lib().qto_groups(I))
+
+
+def packed_bytes(O: int, I: int) -> int:
+    return int(lib().qto_packed_bytes(O, I))
+
+
+def grid_factor(k: int, n: int, lo: float, hi: float) -> float:
+    return float(lib().qto_grid_factor(k, n, lo, hi))
+
+
+def quantize_g64(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0,
+                 return_errs: bool = False):
+    """-> (scales[O,G] f32, codes[O,I] int8, grid_idx[O,G] uint8[, errs[O,G,n]])."""
+    W = _c(W, np.float32)
+    O, I = W.shape
+    G = groups(I)
+    d = None if d is None else _c(d, np.float32)
+    scales = np.empty((O, G), np.float32)
+    codes = np.empty((O, I), np.int8)
+    gidx = np.empty((O, G), np.uint8)
+    n = max(n_grid, 1)
+    errs = np.empty((O, G, n), np.float32) if return_errs else None
+    lib().qto_quantize_g64(_p(W), O, I, _p(d), n_grid, lo, hi, _p(scales), _p(codes),
+                           _p(gidx), _p(errs))
+    if return_errs:
+        return scales, codes, gidx, errs
+    return scales, codes, gidx
+
+
+def pack_i3(codes):
+    codes = _c(codes, np.int8)
+    O, I = codes.shape
+    out = np.empty(packed_bytes(O, I), np.uint8)
+    lib().qto_pack_i3(_p(codes), O, I, _p(out))
+    return out
+
+
+def unpack_i3(packed, O: int, I: int):
+    packed = _c(packed, np.uint8)
+    assert packed.size == packed_bytes(O, I)
+    out = np.empty((O, I), np.int8)
+    lib().qto_unpack_i3(_p(packed), O, I, _p(out))
+    return out
+
+
+def dequant_f64(packed, scales, O: int, I: int):
+    packed, scales = _c(packed, np.uint8), _c(scales, np.float32)
+    out = np.empty((O, I), np.float64)
+    lib().qto_dequant_f64(_p(packed), _p(scales), O, I, _p(out))
+    return out
+
+
+def matvec_f64(packed, scales, O: int, I: int, x):
+    """-> (y[O] f64, absy[O] f64)."""
+    packed, scales, x = _c(packed, np.uint8), _c(scales, np.float32), _c(x, np.float32)
+    y = np.empty(O, np.float64)
+    a = np.empty(O, np.float64)
+    lib().qto_matvec_f64(_p(packed), _p(scales), O, I, _p(x), _p(y), _p(a))
+    return y, a
+
+
+def matmul_f64_sampled(packed, scales, O: int, I: int, X, t_idx, o_idx):
+    """Y[t,o] of X[B,I] @ W_hat^T at the sample points -> (y, absy)."""
+    packed, scales, X = _c(packed, np.uint8), _c(scales, np.float32), _c(X, np.float32)
+    t_idx, o_idx = _c(t_idx, np.int64), _c(o_idx, np.int64)
+    n = t_idx.size
+    y = np.empty(n, np.float64)
+    a = np.empty(n, np.float64)
+    lib().qto_matmul_f64_sampled(_p(packed), _p(scales), O, I, _p(X), X.shape[0], n,
+                                 _p(t_idx), _p(o_idx), _p(y), _p(a))
+    return y, a
+
+
+def matvec_f32(packed, scales, O: int, I: int, x):
+    packed, scales, x = _c(packed, np.uint8), _c(scales, np.float32), _c(x, np.float32)
+    y = np.empty(O, np.float32)
+    lib().qto_matvec_f32(_p(packed), _p(scales), O, I, _p(x), _p(y))
+    return y
+
+
+def hessian_diag(X, d_in=None):
+    X = _c(X, np.float32)
+    T, I = X.shape
+    d_in = None if d_in is None else _c(d_in, np.float64)
+    out = np.empty(I, np.float64)
+    lib().qto_hessian_diag(_p(X), T, I, _p(d_in), _p(out))
+    return out
+
+
+def rowint_recon(W, bits: int = 4):
+    W = _c(W, np.float32)
+    O, I = W.shape
+    out = np.empty((O, I), np.float64)
+    lib().qto_rowint_recon(_p(W), O, I, bits, _p(out))
+    return out

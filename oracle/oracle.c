@@ -1,0 +1,249 @@
+/*
+ * int3-g64 CPU oracle -- TEST INFRASTRUCTURE ONLY (see oracle.h).
+ *
+ * Plain scalar C.  Build: gcc -O2 -ffp-contract=off -fno-fast-math.  Every f32
+ * expression below is written one operation per statement so that the value
+ * of each rounding step is the one the text describes.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+
+#define GROUP 64
+
+int64_t qto_groups(int64_t I) { return (I + GROUP - 1) / GROUP; }
+
+/* Pull request page, "Design": 24 bytes per row per 64-input group. */
+int64_t qto_packed_bytes(int64_t O, int64_t I) { return O * qto_groups(I) * 24; }
+
+/* NeUQI page, first paragraph: a grid search over candidate scales.  The grid
+ * is read as n equally spaced points of the closed interval [lo, hi]
+ * (numpy.linspace semantics: start + k*step, the last point set to stop). */
+float qto_grid_factor(int k, int n, float lo, float hi) {
+    if (k == n - 1) return hi;
+    double step = ((double)hi - (double)lo) / (double)(n - 1);
+    double f = (double)lo + (double)k * step;
+    return (float)f;
+}
+
+/* Round-to-nearest-even of the correctly rounded f32 quotient w/s, clamped
+ * to the code range [-4, 3] of the pull request page ("Design", Layout). */
+static int code_for(float w, float s) {
+    if (s == 0.0f) return 0;
+    float q = w / s;
+    float r = rintf(q); /* default rounding mode: to nearest, ties to even */
+    if (r < -4.0f) r = -4.0f;
+    if (r > 3.0f) r = 3.0f;
+    return (int)r;
+}
+
+void qto_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
+                      int n_grid, float lo, float hi, float* scales,
+                      int8_t* codes, uint8_t* grid_idx, float* errs) {
+    const int64_t G = qto_groups(I);
+    const int ncand = n_grid == 0 ? 1 : n_grid;
+    for (int64_t o = 0; o < O; ++o) {
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t c0 = g * GROUP;
+            const int n = (int)((I - c0) < GROUP ? (I - c0) : GROUP);
+            const float* w = W + o * I + c0;
+
+            /* base scale: absmax over the group's real values, times 1/4
+             * (a 3-bit symmetric quantizer: 2^(3-1) = 4 levels per side) */
+            float amax = 0.0f;
+            for (int j = 0; j < n; ++j) {
+                float a = fabsf(w[j]);
+                if (a > amax) amax = a;
+            }
+            const float base = amax * 0.25f;
+
+            int best_k = 0;
+            float best_e = 0.0f;
+            for (int k = 0; k < ncand; ++k) {
+                const float f = n_grid == 0 ? 1.0f : qto_grid_factor(k, n_grid, lo, hi);
+                const float s = base * f;
+                /* weighted squared reconstruction error of every slot;
+                 * padding slots of a short tail group contribute zero */
+                float a[GROUP];
+                for (int j = 0; j < GROUP; ++j) {
+                    if (j < n) {
+                        const int q = code_for(w[j], s);
+                        const float t = s * (float)q;
+                        const float r = w[j] - t;
+                        const float r2 = r * r;
+                        a[j] = d ? d[c0 + j] * r2 : r2;
+                    } else {
+                        a[j] = 0.0f;
+                    }
+                }
+                /* pairwise halving sum: a[j] += a[j+m], m = 32, 16, ..., 1 */
+                for (int m = GROUP / 2; m >= 1; m /= 2)
+                    for (int j = 0; j < m; ++j) a[j] = a[j] + a[j + m];
+                const float e = a[0];
+                if (errs) errs[(o * G + g) * ncand + k] = e;
+                if (k == 0 || e < best_e) { /* lowest k wins ties */
+                    best_e = e;
+                    best_k = k;
+                }
+            }
+            const float f = n_grid == 0 ? 1.0f : qto_grid_factor(best_k, n_grid, lo, hi);
+            const float s = base * f;
+            scales[o * G + g] = s;
+            if (grid_idx) grid_idx[o * G + g] = (uint8_t)best_k;
+            for (int j = 0; j < n; ++j) codes[o * I + c0 + j] = (int8_t)code_for(w[j], s);
+        }
+    }
+}
+
+/* Pull request page, "Design", Layout: low plane first (2 bits per value, 16
+ * bytes), then the high plane (1 bit per value, 8 bytes), of u = v + 4.
+ * Reading of the bit order (the pages print no byte): value 4b+i sits in bits
+ * 2i..2i+1 of low byte b, value 8c+i in bit i of high byte c.  Padding slots of
+ * a short tail group hold v = 0. */
+void qto_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o) {
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t c0 = g * GROUP;
+            const int n = (int)((I - c0) < GROUP ? (I - c0) : GROUP);
+            uint8_t* p = packed + (o * G + g) * 24;
+            for (int b = 0; b < 24; ++b) p[b] = 0;
+            for (int j = 0; j < GROUP; ++j) {
+                const int v = j < n ? codes[o * I + c0 + j] : 0;
+                const int u = v + 4;
+                p[j / 4] |= (uint8_t)((u & 3) << (2 * (j % 4)));
+                p[16 + j / 8] |= (uint8_t)(((u >> 2) & 1) << (j % 8));
+            }
+        }
+    }
+}
+
+/* stored code of slot j of one 24-byte group, as v = u - 4 */
+static int code_at(const uint8_t* p, int j) {
+    const int lo = (p[j / 4] >> (2 * (j % 4))) & 3;
+    const int hi = (p[16 + j / 8] >> (j % 8)) & 1;
+    return (lo | (hi << 2)) - 4;
+}
+
+void qto_unpack_i3(const uint8_t* packed, int64_t O, int64_t I, int8_t* codes) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o)
+        for (int64_t i = 0; i < I; ++i)
+            codes[o * I + i] = (int8_t)code_at(packed + (o * G + i / GROUP) * 24, (int)(i % GROUP));
+}
+
+void qto_dequant_f64(const uint8_t* packed, const float* scales, int64_t O,
+                     int64_t I, double* What) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o)
+        for (int64_t i = 0; i < I; ++i) {
+            const int64_t g = i / GROUP;
+            const int v = code_at(packed + (o * G + g) * 24, (int)(i % GROUP));
+            What[o * I + i] = (double)scales[o * G + g] * (double)v;
+        }
+}
+
+/* fp64 dequantize-then-multiply (test method of the pull request page,
+ * "Tests": the kernel against dequant-matmul). */
+void qto_matvec_f64(const uint8_t* packed, const float* scales, int64_t O,
+                    int64_t I, const float* x, double* y, double* absy) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o) {
+        double acc = 0.0, aacc = 0.0;
+        for (int64_t i = 0; i < I; ++i) {
+            const int64_t g = i / GROUP;
+            const int v = code_at(packed + (o * G + g) * 24, (int)(i % GROUP));
+            const double w = (double)scales[o * G + g] * (double)v;
+            const double p = w * (double)x[i];
+            acc += p;
+            aacc += fabs(p);
+        }
+        y[o] = acc;
+        if (absy) absy[o] = aacc;
+    }
+}
+
+void qto_matmul_f64_sampled(const uint8_t* packed, const float* scales,
+                            int64_t O, int64_t I, const float* X, int64_t B,
+                            int64_t n, const int64_t* t_idx,
+                            const int64_t* o_idx, double* y, double* absy) {
+    const int64_t G = qto_groups(I);
+    (void)B;
+    (void)O;
+    for (int64_t k = 0; k < n; ++k) {
+        const int64_t t = t_idx[k], o = o_idx[k];
+        double acc = 0.0, aacc = 0.0;
+        for (int64_t i = 0; i < I; ++i) {
+            const int64_t g = i / GROUP;
+            const int v = code_at(packed + (o * G + g) * 24, (int)(i % GROUP));
+            const double w = (double)scales[o * G + g] * (double)v;
+            const double p = w * (double)X[t * I + i];
+            acc += p;
+            aacc += fabs(p);
+        }
+        y[k] = acc;
+        if (absy) absy[k] = aacc;
+    }
+}
+
+/* Pull request page, "Design", Kernel bullet: exact-f32 path with per-group
+ * scale accumulation. */
+void qto_matvec_f32(const uint8_t* packed, const float* scales, int64_t O,
+                    int64_t I, const float* x, float* y) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o) {
+        float yo = 0.0f;
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t c0 = g * GROUP;
+            const int n = (int)((I - c0) < GROUP ? (I - c0) : GROUP);
+            const uint8_t* p = packed + (o * G + g) * 24;
+            float acc = 0.0f;
+            for (int j = 0; j < n; ++j) {
+                const float prod = (float)code_at(p, j) * x[c0 + j];
+                acc = acc + prod;
+            }
+            const float part = scales[o * G + g] * acc;
+            yo = yo + part;
+        }
+        y[o] = yo;
+    }
+}
+
+/* tt-stack page, pipeline table step 1: H = sum_t X^T X; its diagonal is the
+ * per-column sum of squares over tokens.  Accumulated in double. */
+void qto_hessian_diag(const float* X, int64_t T, int64_t I,
+                      const double* d_in, double* d_out) {
+    for (int64_t j = 0; j < I; ++j) d_out[j] = d_in ? d_in[j] : 0.0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < I; ++j) {
+            const double v = (double)X[t * I + j];
+            d_out[j] += v * v;
+        }
+}
+
+/* Per-row b-bit absmax RTN (the shipped per-row int4 format that the pull
+ * request page compares against). */
+void qto_rowint_recon(const float* W, int64_t O, int64_t I, int bits,
+                      double* recon) {
+    const int half = 1 << (bits - 1);
+    for (int64_t o = 0; o < O; ++o) {
+        const float* w = W + o * I;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < I; ++i) {
+            float a = fabsf(w[i]);
+            if (a > amax) amax = a;
+        }
+        const float s = amax / (float)half;
+        for (int64_t i = 0; i < I; ++i) {
+            float q = 0.0f;
+            if (s != 0.0f) {
+                float qq = w[i] / s;
+                q = rintf(qq);
+                if (q < (float)-half) q = (float)-half;
+                if (q > (float)(half - 1)) q = (float)(half - 1);
+            }
+            recon[o * I + i] = (double)s * (double)q;
+        }
+    }
+}
