@@ -1,0 +1,338 @@
+"""Benchmark of the int3-g64 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|gemv]
+
+Headline (one JSON line on stdout): the decode GEMV, W[2048x7168] int3-g64
+with f32 scales times x[7168] f32, batch 1.  A step is one dequantize-multiply
+of the whole matrix; consecutive steps read 64 distinct copies of the packed
+weights (64 x 6.46 MB = 413 MB, more than the 256 MB Infinity Cache), so every
+step streams its weights from HBM.  value = algorithmic bytes per step
+(packed weights + scales + x + y = 6,459,392 B) x steps / elapsed time.
+
+The other rows of the hot path are timed as "legs" on their own workloads:
+the Hessian diagonal and the weighted scale search (W[5120x17408],
+X[8192x17408]), plain quantize + pack at the decode shape, the grouped MoE
+GEMV (128 experts, 32 tokens, top-8) and the bf16 MFMA prefill GEMM
+(X[512x7168] x W[18432x7168]).  Every input is seeded synthetic data
+(workloads.py) resident on the GPU before its timed region starts.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+# Vector ALU: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.3 T lane-instructions/s
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+N_COPIES = 64
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--legs", default="all", choices=["all", "gemv"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def sha_of(*rel):
+    h = hashlib.sha256()
+    for r in rel:
+        with open(os.path.join(ROOT, r), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(name, bytes_alg):
+    """Measured HBM bytes per launch from profiles/<name>_traffic.json, if the
+    kernel source is unchanged since the counters were taken; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_sha") != sha_of(*rec.get("sources", [])):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, n, torch):
+    """Average duration of fn() over n back-to-back launches, and of single
+    launches bracketed by their own event pair (same stream as the kernels)."""
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(n):
+        fn(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    return total_ms / n
+
+
+def per_launch_ms(fn, n, torch):
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(st)
+        fn(i)
+        b.record(st)
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(np.mean(d)), float(np.median(d))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dequant_matmul_int3_amd as qt
+    import workloads
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    legs = {}
+
+    # ------------------------------------------------------------ decode GEMV
+    W, x = workloads.decode()
+    O, I = W.shape
+    G = qt.qt_groups(I)
+    log(f"decode GEMV {O}x{I}: quantize + pack on the GPU")
+    Wd = torch.from_numpy(W).to(dev)
+    xd = torch.from_numpy(x).to(dev)
+    s, c, _ = qt.qt_quantize_g64(Wd)
+    p = qt.qt_pack_i3(c)
+    torch.cuda.synchronize()
+    packs = torch.empty((N_COPIES, p.numel()), dtype=torch.uint8, device=dev)
+    scs = torch.empty((N_COPIES, O, G), dtype=torch.float32, device=dev)
+    packs.copy_(p.expand(N_COPIES, -1))
+    scs.copy_(s.expand(N_COPIES, -1, -1))
+    y = torch.empty(O, dtype=torch.float32, device=dev)
+    bytes_step = p.numel() + s.numel() * 4 + I * 4 + O * 4
+
+    def gemv(i):
+        j = i % N_COPIES
+        qt.qt_matvec_i3(packs[j], scs[j], O, I, xd, y)
+
+    log(f"decode GEMV: warmup {args.warmup}, timed {args.steps} steps")
+    for i in range(args.warmup):
+        gemv(i)
+    torch.cuda.synchronize()
+    ms_step = time_launches(gemv, args.steps, torch)
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+    kmean, kmed = per_launch_ms(gemv, 512, torch)
+    achieved = bytes_step / (kmean * 1e-3) / 1e9
+    tr = traffic_for("gemv_decode", bytes_step)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": tr, "kernel": "gemv_batch_kernel<32,4,1>",
+                "launch_ms_mean": round(kmean, 5), "launch_ms_median": round(kmed, 5),
+                "bytes_per_launch": bytes_step}
+    log(f"  {ms_step * 1e3:.2f} us/step back-to-back = {value:.0f} GB/s; "
+        f"single-launch {kmean * 1e3:.2f} us = {achieved:.0f} GB/s")
+    del packs, scs
+
+    if args.legs == "all":
+        legs.update(run_legs(torch, qt, workloads, dev))
+
+    cpu = cpu_baseline(W, x, args.cpu_seconds, bytes_step)
+
+    line = {
+        "metric": "int3-g64 GEMV effective HBM GB/s (% of peak) at I=7168; quantize groups/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV: W[2048x7168] int3-g64 (f32 scales) x x[7168] f32, "
+                               "batch 1, 64 rotating weight copies",
+                   "O": O, "I": I, "batch": 1, "rotating_copies": N_COPIES,
+                   "bytes_per_step": bytes_step},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    if "quantize_search" in legs:
+        line["quantize_groups_per_s"] = legs["quantize_search"]["groups_per_s"]
+    print(json.dumps(line), flush=True)
+
+
+def run_legs(torch, qt, workloads, dev):
+    legs = {}
+    # -------------------------------------------------------- quantize + pack (decode, RTN)
+    W, _ = workloads.decode()
+    O, I = W.shape
+    G = qt.qt_groups(I)
+    Wd = torch.from_numpy(W).to(dev)
+    s = torch.empty((O, G), dtype=torch.float32, device=dev)
+    c = torch.empty((O, I), dtype=torch.int8, device=dev)
+    p = torch.empty(qt.qt_packed_bytes(O, I), dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: qt.qt_quantize_g64(Wd, None, 0, scales=s, codes=c,
+                                                   want_grid_idx=False), 50, torch)
+    bytes_q = O * I * 4 + O * I + O * G * 4
+    legs["quantize_rtn_decode"] = {"ms": round(ms, 5), "groups_per_s": round(O * G / (ms * 1e-3)),
+                                   "GB_s": round(bytes_q / (ms * 1e-3) / 1e9, 1),
+                                   "bound": "hbm", "frac": round(bytes_q / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    ms = time_launches(lambda i: qt.qt_pack_i3(c, p), 50, torch)
+    bytes_p = O * I + p.numel()
+    legs["pack_decode"] = {"ms": round(ms, 5), "GB_s": round(bytes_p / (ms * 1e-3) / 1e9, 1),
+                           "bound": "hbm", "frac": round(bytes_p / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"leg quantize/pack decode: {legs['quantize_rtn_decode']} {legs['pack_decode']}")
+    del Wd, s, c, p
+
+    # -------------------------------------------------------- Hessian diagonal + search
+    log("leg search: generating X[8192x17408], W[5120x17408]")
+    X = workloads.search_x()
+    Xd = torch.from_numpy(X).to(dev)
+    del X
+    T, I = Xd.shape
+    d = torch.empty(I, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, qt.qt_hessian_workspace_bytes(T, I)), dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: qt.qt_hessian_diag(Xd, d, workspace=ws), 20, torch)
+    hb = T * I * 4 + I * 4
+    legs["hessian_diag"] = {"ms": round(ms, 5), "GB_s": round(hb / (ms * 1e-3) / 1e9, 1),
+                            "bound": "hbm", "frac": round(hb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"leg hessian: {legs['hessian_diag']}")
+    del Xd, ws
+    W = workloads.search_w()
+    O, I = W.shape
+    G = qt.qt_groups(I)
+    Wd = torch.from_numpy(W).to(dev)
+    del W
+    s = torch.empty((O, G), dtype=torch.float32, device=dev)
+    c = torch.empty((O, I), dtype=torch.int8, device=dev)
+    k = torch.empty((O, G), dtype=torch.uint8, device=dev)
+    qt.qt_quantize_g64(Wd, d, 64, 0.5, 1.0, scales=s, codes=c, grid_idx=k)
+    ms = time_launches(lambda i: qt.qt_quantize_g64(Wd, d, 64, 0.5, 1.0, scales=s, codes=c,
+                                                   grid_idx=k), 3, torch)
+    ngroups = O * G
+    # per group: 64 candidates x 64 slots x 9 operations (divide, round, max,
+    # min, multiply, subtract, multiply, multiply, add)
+    ops = ngroups * 64 * 64 * 9
+    legs["quantize_search"] = {"ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)),
+                               "bound": "alu", "achieved_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
+                               "peak_Tops": round(VALU_PEAK_TOPS, 2),
+                               "frac": round(ops / (ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
+                               "op_count": "9 per slot per candidate (division as one)"}
+    log(f"leg search: {legs['quantize_search']}")
+    del Wd, s, c, k, d
+
+    # -------------------------------------------------------- grouped MoE GEMV
+    E = workloads.MOE_EXPERTS
+    log("leg moe: generating and quantizing 128 experts x (up, down)")
+    (Ou, Iu), (Od, Id) = workloads.MOE_UP_SHAPE, workloads.MOE_DOWN_SHAPE
+    pu = torch.empty((E, qt.qt_packed_bytes(Ou, Iu)), dtype=torch.uint8, device=dev)
+    su = torch.empty((E, Ou, qt.qt_groups(Iu)), dtype=torch.float32, device=dev)
+    pdn = torch.empty((E, qt.qt_packed_bytes(Od, Id)), dtype=torch.uint8, device=dev)
+    sdn = torch.empty((E, Od, qt.qt_groups(Id)), dtype=torch.float32, device=dev)
+    for which, pk, sc in (("up", pu, su), ("down", pdn, sdn)):
+        for e0 in range(0, E, 16):
+            mats = workloads.moe_experts_parallel(which, range(e0, e0 + 16), workers=16)
+            for j, m in enumerate(mats):
+                md = torch.from_numpy(m).to(dev)
+                s_, c_, _ = qt.qt_quantize_g64(md, want_grid_idx=False)
+                sc[e0 + j].copy_(s_)
+                qt.qt_pack_i3(c_, pk[e0 + j])
+            torch.cuda.synchronize()
+    Xm, top = workloads.moe_tokens()
+    tok, exp, offs = workloads.route_pairs(top, E)
+    P = tok.size
+    Xmd = torch.from_numpy(Xm).to(dev)
+    tokd = torch.from_numpy(tok).to(dev)
+    offd = torch.from_numpy(offs).to(dev)
+    h = torch.empty((P, Ou), dtype=torch.float32, device=dev)
+    yo = torch.empty((P, Od), dtype=torch.float32, device=dev)
+
+    def moe_step(i):
+        qt.qt_matvec_i3_grouped(pu, su, E, Ou, Iu, Xmd, offd, P, pair_row=tokd, Y=h)
+        qt.qt_matvec_i3_grouped(pdn, sdn, E, Od, Id, h, offd, P, Y=yo)
+
+    for i in range(5):
+        moe_step(i)
+    ms = time_launches(moe_step, 20, torch)
+    hit = int(np.count_nonzero(np.diff(offs)))
+    per_exp = pu.shape[1] + su[0].numel() * 4 + pdn.shape[1] + sdn[0].numel() * 4
+    mb = hit * per_exp + Xm.nbytes + P * (Ou + Od) * 4 * 2
+    legs["moe_grouped"] = {"ms": round(ms, 4), "experts_hit": hit, "pairs": int(P),
+                           "GB_s": round(mb / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
+                           "frac": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "bytes_per_step": int(mb)}
+    log(f"leg moe: {legs['moe_grouped']}")
+    del pu, su, pdn, sdn, h, yo
+
+    # -------------------------------------------------------- prefill GEMM (bf16 MFMA)
+    log("leg prefill: generating and quantizing W[18432x7168]")
+    O, I = workloads.PREFILL_SHAPE
+    G = qt.qt_groups(I)
+    pp = torch.empty(qt.qt_packed_bytes(O, I), dtype=torch.uint8, device=dev)
+    sp = torch.empty((O, G), dtype=torch.float32, device=dev)
+    for slab in range(O // 1024):
+        m = torch.from_numpy(workloads.prefill_w([slab])).to(dev)
+        s_, c_, _ = qt.qt_quantize_g64(m, want_grid_idx=False)
+        sp[slab * 1024:(slab + 1) * 1024].copy_(s_)
+        qt.qt_pack_i3(c_, pp[slab * 1024 * G * 24:(slab + 1) * 1024 * G * 24])
+    Xb = workloads.prefill_x()
+    Xbd = torch.from_numpy(Xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    B = Xbd.shape[0]
+    Y = torch.empty((B, O), dtype=torch.float32, device=dev)
+    for i in range(3):
+        qt.qt_matmul_i3(pp, sp, O, I, Xbd, Y)
+    ms = time_launches(lambda i: qt.qt_matmul_i3(pp, sp, O, I, Xbd, Y), 20, torch)
+    flops = 2.0 * B * O * I
+    tf = flops / (ms * 1e-3) / 1e12
+    legs["prefill_gemm"] = {"ms": round(ms, 4), "TFLOP_s": round(tf, 1), "bound": "mfma",
+                            "peak_TFLOP_s": BF16_PEAK_TFLOPS, "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    log(f"leg prefill: {legs['prefill_gemm']}")
+    return legs
+
+
+def cpu_baseline(W, x, seconds, bytes_step):
+    """The CPU oracle's fp64 dequantize-then-multiply of the same decode
+    matrix, repeated for about `seconds` on one host core."""
+    import oracle
+
+    O, I = W.shape
+    s, c, _ = oracle.quantize_g64(W)
+    p = oracle.pack_i3(c)
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        oracle.matvec_f64(p, s, O, I, x)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(bytes_step * n / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} fp64 dequantize-then-multiply passes over the decode matrix "
+                      f"W[{O}x{I}] ({dt:.1f} s, single thread)"}
+
+
+if __name__ == "__main__":
+    main()

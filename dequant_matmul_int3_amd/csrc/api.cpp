@@ -1,0 +1,210 @@
+// C-ABI layer of libqt.so: host-side argument validation, then one launch
+// (or a short fixed sequence of launches) on the caller's stream.  See qt.h
+// for the contract of every entry point.
+#include "qt.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "qt_internal.h"
+
+namespace {
+
+using qt::kGroup;
+using qt::kGroupBytes;
+
+// Overflow-checked product a*b*c of non-negative sizes; -1 on overflow.
+int64_t mul3(int64_t a, int64_t b, int64_t c) {
+    __int128 p = (__int128)a * b * c;
+    if (p > INT64_MAX) return -1;
+    return (int64_t)p;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Byte ranges [p, p+n) and [q, q+m) overlap.
+bool overlap(const void* p, int64_t n, const void* q, int64_t m) {
+    if (!p || !q || n <= 0 || m <= 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+qt_status shape_ok(int64_t O, int64_t I) {
+    if (O < 1 || I < 1 || I > QT_MAX_I) return QT_ERR_SHAPE;
+    if (mul3(O, (I + kGroup - 1) / kGroup, kGroupBytes) < 0 || mul3(O, I, 4) < 0)
+        return QT_ERR_SHAPE;
+    return QT_OK;
+}
+
+qt_status launched(hipError_t e) { return e == hipSuccess ? QT_OK : QT_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int64_t qt_groups(int64_t I) { return I < 1 ? 0 : (I + kGroup - 1) / kGroup; }
+
+int64_t qt_packed_bytes(int64_t O, int64_t I) {
+    if (O < 1 || I < 1) return 0;
+    const int64_t b = mul3(O, qt_groups(I), kGroupBytes);
+    return b < 0 ? 0 : b;
+}
+
+const char* qt_status_str(qt_status s) {
+    switch (s) {
+        case QT_OK: return "ok";
+        case QT_ERR_NULL: return "a required pointer is NULL";
+        case QT_ERR_SHAPE: return "a size is out of range";
+        case QT_ERR_ALIGN: return "a pointer is misaligned";
+        case QT_ERR_DTYPE: return "unsupported element type";
+        case QT_ERR_ARG: return "an argument is out of range";
+        case QT_ERR_ALIAS: return "an output overlaps an input";
+        case QT_ERR_LAUNCH: return "kernel launch failed";
+        case QT_ERR_WORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+size_t qt_hessian_workspace_bytes(int64_t T, int64_t I) {
+    if (T < 1 || I < 1 || I > QT_MAX_I) return 0;
+    const int slabs = qt::hessian_slabs(T, I);
+    if (slabs <= 1) return 0;
+    const int64_t b = mul3(slabs, I, 4);
+    return b < 0 ? 0 : (size_t)b;
+}
+
+qt_status qt_hessian_diag(const void* X, qt_dtype xt, int64_t T, int64_t I, float* d,
+                          int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+    if (!X || !d) return QT_ERR_NULL;
+    if (xt != QT_F32 && xt != QT_BF16) return QT_ERR_DTYPE;
+    if (T < 1 || I < 1 || I > QT_MAX_I) return QT_ERR_SHAPE;
+    const int64_t esz = xt == QT_F32 ? 4 : 2;
+    const int64_t xbytes = mul3(T, I, esz);
+    if (xbytes < 0) return QT_ERR_SHAPE;
+    if (accumulate != 0 && accumulate != 1) return QT_ERR_ARG;
+    if (!aligned(X, (uintptr_t)esz) || !aligned(d, 4)) return QT_ERR_ALIGN;
+    const size_t need = qt_hessian_workspace_bytes(T, I);
+    if (need > 0) {
+        if (!workspace || ws_bytes < need) return QT_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return QT_ERR_ALIGN;
+    }
+    if (overlap(d, I * 4, X, xbytes)) return QT_ERR_ALIAS;
+    if (need > 0 && (overlap(workspace, (int64_t)need, X, xbytes) ||
+                     overlap(workspace, (int64_t)need, d, I * 4)))
+        return QT_ERR_ALIAS;
+    return launched(qt::launch_hessian_diag(X, xt == QT_BF16, T, I, d, accumulate,
+                                            static_cast<float*>(workspace), as_stream(stream)));
+}
+
+qt_status qt_quantize_g64(const float* W, int64_t O, int64_t I, const float* d, int32_t n_grid,
+                          float lo, float hi, float* scales, int8_t* codes, uint8_t* grid_idx,
+                          void* stream) {
+    if (!W || !scales || !codes) return QT_ERR_NULL;
+    qt_status st = shape_ok(O, I);
+    if (st != QT_OK) return st;
+    if (n_grid != 0 && (n_grid < 2 || n_grid > qt::kMaxGrid)) return QT_ERR_ARG;
+    if (n_grid != 0 && !(lo > 0.0f && lo <= hi && hi < __builtin_inff())) return QT_ERR_ARG;
+    if (!aligned(W, 4) || !aligned(scales, 4) || (d && !aligned(d, 4))) return QT_ERR_ALIGN;
+    const int64_t G = qt_groups(I);
+    const int64_t wb = O * I * 4, sb = O * G * 4, cb = O * I, gb = O * G;
+    if (overlap(scales, sb, W, wb) || overlap(codes, cb, W, wb) ||
+        overlap(scales, sb, codes, cb) || (d && (overlap(scales, sb, d, I * 4) ||
+                                                 overlap(codes, cb, d, I * 4))) ||
+        (grid_idx && (overlap(grid_idx, gb, W, wb) || overlap(grid_idx, gb, scales, sb) ||
+                      overlap(grid_idx, gb, codes, cb) || (d && overlap(grid_idx, gb, d, I * 4)))))
+        return QT_ERR_ALIAS;
+
+    // Candidate factors: n_grid equally spaced points of [lo, hi], formed in
+    // double and rounded once; the last one is hi itself.  n_grid == 0 is the
+    // single plain absmax/4 scale (factor 1).
+    qt::GridTable tab{};
+    int ncand = 1;
+    if (n_grid == 0) {
+        tab.f[0] = 1.0f;
+    } else {
+        ncand = n_grid;
+        const double step = ((double)hi - (double)lo) / (double)(n_grid - 1);
+        for (int k = 0; k < n_grid; ++k) tab.f[k] = (float)((double)lo + (double)k * step);
+        tab.f[n_grid - 1] = hi;
+    }
+    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, tab, scales, codes, grid_idx,
+                                            as_stream(stream)));
+}
+
+qt_status qt_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed, void* stream) {
+    if (!codes || !packed) return QT_ERR_NULL;
+    qt_status st = shape_ok(O, I);
+    if (st != QT_OK) return st;
+    if (!aligned(packed, 16)) return QT_ERR_ALIGN;
+    if (overlap(packed, qt_packed_bytes(O, I), codes, O * I)) return QT_ERR_ALIAS;
+    return launched(qt::launch_pack_i3(codes, O, I, packed, as_stream(stream)));
+}
+
+qt_status qt_matvec_i3(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                       const float* x, float* y, void* stream) {
+    if (!packed || !scales || !x || !y) return QT_ERR_NULL;
+    qt_status st = shape_ok(O, I);
+    if (st != QT_OK) return st;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(x, 4) || !aligned(y, 4))
+        return QT_ERR_ALIGN;
+    const int64_t G = qt_groups(I);
+    if (overlap(y, O * 4, packed, O * G * kGroupBytes) || overlap(y, O * 4, scales, O * G * 4) ||
+        overlap(y, O * 4, x, I * 4))
+        return QT_ERR_ALIAS;
+    return launched(qt::launch_gemv_batch(packed, scales, O, I, x, false, 1, y,
+                                          as_stream(stream)));
+}
+
+qt_status qt_matmul_i3(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                       const void* X, qt_dtype xt, int64_t B, float* Y, void* stream) {
+    if (!packed || !scales || !X || !Y) return QT_ERR_NULL;
+    if (xt != QT_F32 && xt != QT_BF16) return QT_ERR_DTYPE;
+    qt_status st = shape_ok(O, I);
+    if (st != QT_OK) return st;
+    // the MFMA grid has one block row per 128 tokens (65535 rows at most)
+    if (B < 1 || B > 65535LL * 128) return QT_ERR_SHAPE;
+    const int64_t esz = xt == QT_F32 ? 4 : 2;
+    const int64_t xb = mul3(B, I, esz), yb = mul3(B, O, 4);
+    if (xb < 0 || yb < 0) return QT_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(Y, 4)) return QT_ERR_ALIGN;
+    if (!aligned(X, xt == QT_BF16 ? 16 : 4)) return QT_ERR_ALIGN;
+    const int64_t G = qt_groups(I);
+    if (overlap(Y, yb, packed, O * G * kGroupBytes) || overlap(Y, yb, scales, O * G * 4) ||
+        overlap(Y, yb, X, xb))
+        return QT_ERR_ALIAS;
+    if (xt == QT_BF16 && B >= 16)
+        return launched(qt::launch_gemm_mfma(packed, scales, O, I,
+                                             static_cast<const uint16_t*>(X), B, Y,
+                                             as_stream(stream)));
+    return launched(qt::launch_gemv_batch(packed, scales, O, I, X, xt == QT_BF16, B, Y,
+                                          as_stream(stream)));
+}
+
+qt_status qt_matvec_i3_grouped(const uint8_t* packed, const float* scales, int32_t E, int64_t O,
+                               int64_t I, const float* X, int64_t n_x_rows,
+                               const int32_t* pair_row, const int32_t* expert_offsets, int32_t P,
+                               float* Y, void* stream) {
+    if (!packed || !scales || !X || !expert_offsets || !Y) return QT_ERR_NULL;
+    qt_status st = shape_ok(O, I);
+    if (st != QT_OK) return st;
+    if (E < 1 || E > 65535 || P < 1 || n_x_rows < 1) return QT_ERR_SHAPE;
+    if (!pair_row && n_x_rows < P) return QT_ERR_SHAPE;
+    const int64_t G = qt_groups(I);
+    const int64_t pk = mul3(E, O * G, kGroupBytes), sk = mul3(E, O * G, 4);
+    const int64_t xb = mul3(n_x_rows, I, 4), yb = mul3(P, O, 4);
+    if (pk < 0 || sk < 0 || xb < 0 || yb < 0) return QT_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(X, 4) || !aligned(Y, 4) ||
+        !aligned(expert_offsets, 4) || (pair_row && !aligned(pair_row, 4)))
+        return QT_ERR_ALIGN;
+    if (overlap(Y, yb, packed, pk) || overlap(Y, yb, scales, sk) || overlap(Y, yb, X, xb) ||
+        overlap(Y, yb, expert_offsets, (int64_t)(E + 1) * 4) ||
+        (pair_row && overlap(Y, yb, pair_row, (int64_t)P * 4)))
+        return QT_ERR_ALIAS;
+    return launched(qt::launch_gemv_grouped(packed, scales, E, O, I, X, n_x_rows, pair_row,
+                                            expert_offsets, P, Y, as_stream(stream)));
+}
+
+}  // extern "C"

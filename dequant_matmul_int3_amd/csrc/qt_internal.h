@@ -1,0 +1,45 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Arguments here are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qt {
+
+constexpr int kGroup = 64;       // inputs per group
+constexpr int kGroupBytes = 24;  // 16 B low plane + 8 B high plane
+constexpr int kMaxGrid = 256;    // largest candidate grid of the scale search
+
+// Candidate factors of the scale search, passed by value as a kernel argument.
+struct GridTable {
+    float f[kMaxGrid];
+};
+
+hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
+                               int ncand, const GridTable& tab, float* scales,
+                               int8_t* codes, uint8_t* grid_idx, hipStream_t s);
+
+hipError_t launch_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed,
+                          hipStream_t s);
+
+// Dequantize-multiply of `ntok` input rows against one O x I matrix, exact-f32
+// path.  X rows are f32 (bf16 == false) or bf16 bit patterns (bf16 == true).
+hipError_t launch_gemv_batch(const uint8_t* packed, const float* scales, int64_t O,
+                             int64_t I, const void* X, bool bf16, int64_t ntok,
+                             float* Y, hipStream_t s);
+
+hipError_t launch_gemv_grouped(const uint8_t* packed, const float* scales, int32_t E,
+                               int64_t O, int64_t I, const float* X, int64_t n_x_rows,
+                               const int32_t* pair_row, const int32_t* expert_offsets,
+                               int32_t P, float* Y, hipStream_t s);
+
+// bf16 MFMA path, B >= 16.
+hipError_t launch_gemm_mfma(const uint8_t* packed, const float* scales, int64_t O,
+                            int64_t I, const uint16_t* X, int64_t B, float* Y,
+                            hipStream_t s);
+
+int hessian_slabs(int64_t T, int64_t I);
+hipError_t launch_hessian_diag(const void* X, bool bf16, int64_t T, int64_t I, float* d,
+                               int accumulate, float* workspace, hipStream_t s);
+
+}  // namespace qt

@@ -1,0 +1,189 @@
+"""ctypes binding of libqt.so with the same names as include/qt.h.
+
+Argument marshalling only: shapes and dtypes of torch tensors are turned into
+pointers and sizes, optional outputs are allocated with torch on the tensors'
+device, and the call is enqueued on torch's current HIP stream (or the stream
+given).  Every step of the computation runs in the library's kernels; there is
+no fallback: if libqt.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+QT_F32 = 0
+QT_BF16 = 1
+
+_SO = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqt.so")
+_lib = None
+
+_SIGS = {
+    "qt_groups": (C.c_int64, [C.c_int64]),
+    "qt_packed_bytes": (C.c_int64, [C.c_int64, C.c_int64]),
+    "qt_status_str": (C.c_char_p, [C.c_int]),
+    "qt_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
+    "qt_hessian_diag": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_void_p,
+                                  C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qt_quantize_g64": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
+                                  C.c_float, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_void_p]),
+    "qt_pack_i3": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]),
+    "qt_matvec_i3": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
+                               C.c_void_p, C.c_void_p]),
+    "qt_matmul_i3": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
+                               C.c_int, C.c_int64, C.c_void_p, C.c_void_p]),
+    "qt_matvec_i3_grouped": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                       C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
+                                       C.c_void_p, C.c_void_p]),
+}
+
+
+class QtError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({qt_status_str(status)})")
+
+
+def lib():
+    """Load libqt.so (built in-tree by dequant_matmul_int3_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            raise ImportError(f"{_SO} is not built; run `python -m dequant_matmul_int3_amd.build`")
+        L = C.CDLL(_SO)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is not None:
+        return C.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libqt takes device tensors only")
+        if not t.is_contiguous():
+            raise ValueError("libqt takes contiguous tensors only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QtError(status, where)
+
+
+def qt_status_str(status: int) -> str:
+    return lib().qt_status_str(status).decode()
+
+
+def qt_groups(I: int) -> int:
+    return int(lib().qt_groups(I))
+
+
+def qt_packed_bytes(O: int, I: int) -> int:
+    return int(lib().qt_packed_bytes(O, I))
+
+
+def qt_hessian_workspace_bytes(T: int, I: int) -> int:
+    return int(lib().qt_hessian_workspace_bytes(T, I))
+
+
+def qt_hessian_diag(X, d=None, accumulate: bool = False, workspace=None, stream=None):
+    """d[j] (+)= sum_t X[t,j]^2 for X [T, I] f32 or bf16 -> d [I] f32."""
+    T, I = X.shape
+    if d is None:
+        d = torch.zeros(I, dtype=torch.float32, device=X.device)
+    ws_need = qt_hessian_workspace_bytes(T, I)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=X.device)
+    dev = _dev(X, d, workspace)
+    xt = QT_BF16 if X.dtype == torch.bfloat16 else QT_F32 if X.dtype == torch.float32 else -1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qt_hessian_diag(_ptr(X), xt, T, I, _ptr(d), int(accumulate), _ptr(workspace),
+                                 ws_bytes, _stream(stream, dev)), "qt_hessian_diag")
+    return d
+
+
+def qt_quantize_g64(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0,
+                    scales=None, codes=None, grid_idx=None, want_grid_idx: bool = True,
+                    stream=None):
+    """W [O, I] f32 -> (scales [O, G] f32, codes [O, I] int8, grid_idx [O, G] uint8 or None)."""
+    O, I = W.shape
+    G = qt_groups(I)
+    if scales is None:
+        scales = torch.empty((O, G), dtype=torch.float32, device=W.device)
+    if codes is None:
+        codes = torch.empty((O, I), dtype=torch.int8, device=W.device)
+    if grid_idx is None and want_grid_idx:
+        grid_idx = torch.empty((O, G), dtype=torch.uint8, device=W.device)
+    dev = _dev(W, d, scales, codes, grid_idx)
+    if W.dtype != torch.float32 or (d is not None and d.dtype != torch.float32):
+        raise ValueError("W and d must be float32")
+    _check(lib().qt_quantize_g64(_ptr(W), O, I, _ptr(d), n_grid, lo, hi, _ptr(scales),
+                                 _ptr(codes), _ptr(grid_idx), _stream(stream, dev)),
+           "qt_quantize_g64")
+    return scales, codes, grid_idx
+
+
+def qt_pack_i3(codes, packed=None, stream=None):
+    """codes [O, I] int8 -> packed [O*G*24] uint8."""
+    O, I = codes.shape
+    if packed is None:
+        packed = torch.empty(qt_packed_bytes(O, I), dtype=torch.uint8, device=codes.device)
+    dev = _dev(codes, packed)
+    _check(lib().qt_pack_i3(_ptr(codes), O, I, _ptr(packed), _stream(stream, dev)), "qt_pack_i3")
+    return packed
+
+
+def qt_matvec_i3(packed, scales, O: int, I: int, x, y=None, stream=None):
+    """y [O] f32 = W x for x [I] f32."""
+    if y is None:
+        y = torch.empty(O, dtype=torch.float32, device=x.device)
+    dev = _dev(packed, scales, x, y)
+    _check(lib().qt_matvec_i3(_ptr(packed), _ptr(scales), O, I, _ptr(x), _ptr(y),
+                              _stream(stream, dev)), "qt_matvec_i3")
+    return y
+
+
+def qt_matmul_i3(packed, scales, O: int, I: int, X, Y=None, stream=None):
+    """Y [B, O] f32 = X W^T for X [B, I] f32 or bf16."""
+    B = X.shape[0]
+    if Y is None:
+        Y = torch.empty((B, O), dtype=torch.float32, device=X.device)
+    dev = _dev(packed, scales, X, Y)
+    xt = QT_BF16 if X.dtype == torch.bfloat16 else QT_F32 if X.dtype == torch.float32 else -1
+    _check(lib().qt_matmul_i3(_ptr(packed), _ptr(scales), O, I, _ptr(X), xt, B, _ptr(Y),
+                              _stream(stream, dev)), "qt_matmul_i3")
+    return Y
+
+
+def qt_matvec_i3_grouped(packed, scales, E: int, O: int, I: int, X, expert_offsets, P: int,
+                         pair_row=None, Y=None, stream=None):
+    """Y [P, O] f32: Y[p] = W_{e(p)} X[row(p)] for pairs sorted by expert."""
+    if Y is None:
+        Y = torch.empty((P, O), dtype=torch.float32, device=X.device)
+    dev = _dev(packed, scales, X, expert_offsets, pair_row, Y)
+    _check(lib().qt_matvec_i3_grouped(_ptr(packed), _ptr(scales), E, O, I, _ptr(X), X.shape[0],
+                                      _ptr(pair_row), _ptr(expert_offsets), P, _ptr(Y),
+                                      _stream(stream, dev)), "qt_matvec_i3_grouped")
+    return Y

@@ -1,0 +1,175 @@
+/*
+ * qt.h -- int3-g64 quantize / pack / dequantize-multiply on MI355X (gfx950).
+ *
+ * C ABI of libqt.so.  Plain pointers and sizes only; no framework types.
+ *
+ * Format (the "int3-g64 (fmt=5)" pull request page, section "Design", Layout
+ * bullet): a weight matrix W[O x I] (O output rows, I inputs, y = W x) is cut,
+ * per row, into G = ceil(I/64) groups of 64 inputs; group g covers columns
+ * [64g, min(64g+64, I)) and the last one may be short.  Every group packs to
+ * 24 bytes: a 16-byte low plane holding u & 3 and an 8-byte high plane holding
+ * u >> 2, where u = v + 4 and the code v lies in [-4, 3].  Inside the planes,
+ * value 4b+i of the group sits in bits 2i..2i+1 of low byte b and value 8c+i in
+ * bit i of high byte c; the padding slots of a short group hold v = 0.  Groups
+ * are stored row-major: group (o, g) starts at byte (o*G + g)*24.  One f32
+ * scale per group lives in a separate row-major tensor scales[O x G]; the
+ * weight the pair denotes is scales[o,g] * v.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise; all tensors are
+ *     contiguous and row-major; the caller owns every buffer.  The library
+ *     never allocates or frees device memory and keeps no mutable global
+ *     state, so calls are reentrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns before the work completes; results are
+ *     valid once the caller has synchronised that stream.
+ *   - Arguments are validated on the host first.  On any error nothing is
+ *     enqueued and a nonzero qt_status is returned.  A failed launch returns
+ *     QT_ERR_LAUNCH.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.  No exception crosses this interface.
+ *   - Alignment: `packed` 16 bytes; f32 and int32 buffers 4 bytes; bf16
+ *     buffers 16 bytes.  Outputs must not overlap inputs (QT_ERR_ALIAS).
+ *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
+ *   - Results are deterministic: no kernel uses floating-point atomics, and
+ *     repeated calls on the same inputs give bit-identical outputs.
+ */
+#ifndef QT_H
+#define QT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QT_OK = 0,
+    QT_ERR_NULL = 1,      /* a required pointer is NULL                      */
+    QT_ERR_SHAPE = 2,     /* a size is out of range or overflows             */
+    QT_ERR_ALIGN = 3,     /* a pointer is not aligned as required            */
+    QT_ERR_DTYPE = 4,     /* unsupported element type                        */
+    QT_ERR_ARG = 5,       /* another argument is out of range                */
+    QT_ERR_ALIAS = 6,     /* an output overlaps an input                     */
+    QT_ERR_LAUNCH = 7,    /* the kernel launch failed                        */
+    QT_ERR_WORKSPACE = 8  /* workspace missing or too small                  */
+} qt_status;
+
+typedef enum { QT_F32 = 0, QT_BF16 = 1 } qt_dtype;
+
+/* Largest I accepted by every entry point (columns are indexed in 32 bits). */
+#define QT_MAX_I 2147483647LL
+
+/* Host: number of groups per row, ceil(I/64) (0 for I < 1). */
+int64_t qt_groups(int64_t I);
+
+/* Host: bytes of the packed weights of an O x I matrix, O*ceil(I/64)*24
+ * (the byte count stated on the pull request page's format-detection
+ * comment).  0 for a non-positive size. */
+int64_t qt_packed_bytes(int64_t O, int64_t I);
+
+/* Host: human-readable name of a status code (static storage). */
+const char* qt_status_str(qt_status s);
+
+/*
+ * Importance weights: d[j] = sum_t X[t,j]^2, the diagonal of H = sum X^T X
+ * (the tt-stack issue page, pipeline table step 1: H accumulated per linear
+ * input over the calibration tokens, fp32 accumulation on the device).
+ *   X          [T x I], element type xt (QT_F32 or QT_BF16)
+ *   d          [I] f32 output; accumulate = 0: d = sum, 1: d += sum
+ *   workspace  device scratch of at least qt_hessian_workspace_bytes(T, I)
+ *              bytes (4-byte aligned); may be NULL when that size is 0
+ * Partial sums over token slabs go to the workspace and are added in a fixed
+ * order, so the result does not depend on scheduling.
+ */
+size_t qt_hessian_workspace_bytes(int64_t T, int64_t I);
+qt_status qt_hessian_diag(const void* X, qt_dtype xt, int64_t T, int64_t I,
+                          float* d, int accumulate, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Per-group scale choice and code emission (pull request page, "Why this
+ * format" item 1: a 3-bit group-64 absmax quantizer; NeUQI accuracy page,
+ * first paragraph: a grid search over scales weighted by activation
+ * importance).  For every group with real values w_j (j < n):
+ *   base = max_j |w_j| * 0.25                              (f32)
+ *   candidate k: s_k = base * f_k, f_k = f32(lo + k*(hi-lo)/(n_grid-1)),
+ *                f_{n_grid-1} = hi; with n_grid = 0 the single candidate
+ *                is s = base
+ *   q_j(s) = 0 if s == 0, else clamp(rne(w_j / s), -4, 3)  (IEEE division)
+ *   E_k = sum_j d_j * (w_j - s_k*q_j)^2, every operation a rounded f32
+ *         operation without fused multiply-add, summed by halving
+ *         (a[j] += a[j+m] for m = 32, 16, ..., 1 over the 64 slots, padding
+ *         slots contributing 0)
+ *   k* = the smallest k with the least E_k
+ * Outputs scales[o,g] = s_{k*}, codes[o, 64g+j] = q_j(s_{k*}),
+ * grid_idx[o,g] = k*.  Codes, scales and k* are bit-exact functions of the
+ * inputs.
+ *   W        [O x I] f32
+ *   d        [I] f32 importance (>= 0), or NULL for all ones
+ *   n_grid   0, or 2..256 candidates; lo, hi with 0 < lo <= hi (ignored for 0)
+ *   scales   [O x G] f32 out; codes [O x I] int8 out;
+ *   grid_idx [O x G] uint8 out, or NULL
+ */
+qt_status qt_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
+                          int32_t n_grid, float lo, float hi, float* scales,
+                          int8_t* codes, uint8_t* grid_idx, void* stream);
+
+/*
+ * Bit-plane packer (pull request page, "Design", Layout bullet): codes
+ * [O x I] int8 in [-4, 3] -> packed [O*G*24] bytes in the layout described at
+ * the top of this header, short groups padded with v = 0.  Codes outside
+ * [-4, 3] are masked to their low 3 bits of v + 4.
+ */
+qt_status qt_pack_i3(const int8_t* codes, int64_t O, int64_t I,
+                     uint8_t* packed, void* stream);
+
+/*
+ * Dequantize-and-multiply, one vector (pull request page, "Design", Kernel
+ * bullet: an exact-f32 path with per-group scale accumulation):
+ *   y[o] = sum_g scales[o,g] * sum_{j<n_g} v[o,64g+j] * x[64g+j]
+ * computed in f32 (products and sums rounded in f32; agreement with the fp64
+ * dequantize-then-multiply value is within 1e-5 of sum_i |w_oi * x_i|).
+ *   packed [O*G*24], scales [O x G] f32, x [I] f32, y [O] f32 out.
+ */
+qt_status qt_matvec_i3(const uint8_t* packed, const float* scales, int64_t O,
+                       int64_t I, const float* x, float* y, void* stream);
+
+/*
+ * Dequantize-and-multiply, a batch: Y[t,o] = sum_i X[t,i] * w[o,i], t < B.
+ *   X [B x I] of type xt, Y [B x O] f32 out.
+ *   xt == QT_F32, or B < 16: the exact-f32 path of qt_matvec_i3 (bf16 inputs
+ *     are widened exactly to f32); tolerance 1e-5 as above.
+ *   xt == QT_BF16 and B >= 16: MFMA path.  The codes enter the matrix cores
+ *     as exact bf16 values, each 64-input group is reduced in f32 and then
+ *     scaled by its f32 scale; tolerance 2e-3 of sum_i |w_oi * X_ti|.
+ */
+qt_status qt_matmul_i3(const uint8_t* packed, const float* scales, int64_t O,
+                       int64_t I, const void* X, qt_dtype xt, int64_t B,
+                       float* Y, void* stream);
+
+/*
+ * Grouped dequantize-and-multiply for mixture-of-experts decode (the pull
+ * request page's setting: every routed expert's weights are read once per
+ * step).  E experts of identical shape O x I, stored back to back:
+ *   packed  [E][O*G*24], scales [E][O x G]
+ *   pairs p = 0..P-1 are sorted by expert; the pairs of expert e are
+ *   p in [expert_offsets[e], expert_offsets[e+1]); expert_offsets [E+1]
+ *   int32 on the device with expert_offsets[0] = 0, nondecreasing,
+ *   expert_offsets[E] = P.
+ *   X       input rows; row of pair p is X[pair_row[p]] when pair_row is
+ *           not NULL (int32 [P], values in [0, n_x_rows)), else X[p].
+ *   Y       [P x O] f32 out: Y[p] = W_{e(p)} X[row(p)], f32 as qt_matvec_i3.
+ * Everything runs in one launch; experts with no pair cost no weight reads.
+ */
+qt_status qt_matvec_i3_grouped(const uint8_t* packed, const float* scales,
+                               int32_t E, int64_t O, int64_t I,
+                               const float* X, int64_t n_x_rows,
+                               const int32_t* pair_row,
+                               const int32_t* expert_offsets, int32_t P,
+                               float* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QT_H */

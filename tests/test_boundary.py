@@ -1,0 +1,136 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol and
+rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import dequant_matmul_int3_amd as qt
+from dequant_matmul_int3_amd import qt as qtmod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qt.h")
+
+QT_OK, QT_ERR_NULL, QT_ERR_SHAPE, QT_ERR_ALIGN, QT_ERR_DTYPE, QT_ERR_ARG, QT_ERR_ALIAS = range(7)
+QT_ERR_WORKSPACE = 8
+
+# fake device addresses: validation must reject these calls before any
+# dereference or launch
+A = 0x7F0000000000
+B = 0x7F1000000000
+Cc = 0x7F2000000000
+D = 0x7F3000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_named_entry_points():
+    names = declared_functions()
+    for n in ("qt_quantize_g64", "qt_pack_i3", "qt_matvec_i3", "qt_matmul_i3", "qt_hessian_diag"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = qt.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) <= set(qtmod._SIGS), "binding misses a declared function"
+
+
+def test_sizes():
+    assert qt.qt_groups(0) == 0 and qt.qt_groups(1) == 1 and qt.qt_groups(64) == 1
+    assert qt.qt_groups(65) == 2 and qt.qt_groups(7200) == 113
+    assert qt.qt_packed_bytes(2048, 7168) == 5505024
+    assert qt.qt_packed_bytes(2048, 7200) == 2048 * 113 * 24
+    assert qt.qt_packed_bytes(0, 5) == 0 and qt.qt_packed_bytes(3, -1) == 0
+    assert qt.qt_packed_bytes(1 << 62, 1 << 20) == 0  # overflow is reported as 0
+    assert qt.qt_hessian_workspace_bytes(100, 64) == 0  # a single slab needs none
+    assert qt.qt_hessian_workspace_bytes(8192, 17408) >= 8192 // 128 * 17408 * 4
+    for s in range(9):
+        assert qt.qt_status_str(s)
+
+
+L = None
+
+
+def setup_module(_):
+    global L
+    L = qt.lib()
+
+
+def test_quantize_rejects():
+    f = L.qt_quantize_g64
+    assert f(None, 4, 64, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_NULL
+    assert f(A, 0, 64, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_SHAPE
+    assert f(A, 4, 0, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_SHAPE
+    assert f(A, 4, 1 << 31, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_SHAPE
+    assert f(A, 4, 64, None, 1, 0.5, 1.0, B, Cc, None, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 257, 0.5, 1.0, B, Cc, None, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 64, 0.0, 1.0, B, Cc, None, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 64, 1.0, 0.5, B, Cc, None, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 64, 0.5, float("inf"), B, Cc, None, None) == QT_ERR_ARG
+    assert f(A + 2, 4, 64, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_ALIGN
+    assert f(A, 4, 64, D + 1, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_ALIGN
+    assert f(A, 4, 64, None, 0, 0.5, 1.0, A + 16, Cc, None, None) == QT_ERR_ALIAS
+    assert f(A, 4, 64, None, 0, 0.5, 1.0, B, B + 8, None, None) == QT_ERR_ALIAS
+    assert f(A, 4, 64, None, 0, 0.5, 1.0, B, Cc, A + 100, None) == QT_ERR_ALIAS
+
+
+def test_pack_rejects():
+    f = L.qt_pack_i3
+    assert f(None, 2, 64, B, None) == QT_ERR_NULL
+    assert f(A, -1, 64, B, None) == QT_ERR_SHAPE
+    assert f(A, 2, 64, B + 8, None) == QT_ERR_ALIGN
+    assert f(A, 2, 64, A + 16, None) == QT_ERR_ALIAS
+
+
+def test_matvec_rejects():
+    f = L.qt_matvec_i3
+    assert f(A, B, 4, 64, Cc, None, None) == QT_ERR_NULL
+    assert f(A, B, 4, 0, Cc, D, None) == QT_ERR_SHAPE
+    assert f(A + 8, B, 4, 64, Cc, D, None) == QT_ERR_ALIGN
+    assert f(A, B + 2, 4, 64, Cc, D, None) == QT_ERR_ALIGN
+    assert f(A, B, 4, 64, Cc, A + 32, None) == QT_ERR_ALIAS
+    assert f(A, B, 4, 64, Cc, Cc + 4, None) == QT_ERR_ALIAS
+
+
+def test_matmul_rejects():
+    f = L.qt_matmul_i3
+    assert f(A, B, 4, 64, None, 0, 2, D, None) == QT_ERR_NULL
+    assert f(A, B, 4, 64, Cc, 7, 2, D, None) == QT_ERR_DTYPE
+    assert f(A, B, 4, 64, Cc, 0, 0, D, None) == QT_ERR_SHAPE
+    assert f(A, B, 4, 64, Cc, 0, 65535 * 128 + 1, D, None) == QT_ERR_SHAPE
+    assert f(A, B, 4, 64, Cc + 8, 1, 32, D, None) == QT_ERR_ALIGN
+    assert f(A, B, 4, 64, Cc, 1, 32, Cc + 64, None) == QT_ERR_ALIAS
+
+
+def test_grouped_rejects():
+    f = L.qt_matvec_i3_grouped
+    assert f(A, B, 8, 4, 64, Cc, 4, None, None, 4, D, None) == QT_ERR_NULL
+    assert f(A, B, 0, 4, 64, Cc, 4, None, A, 4, D, None) == QT_ERR_SHAPE
+    assert f(A, B, 8, 4, 64, Cc, 3, None, A + (1 << 30), 4, D, None) == QT_ERR_SHAPE
+    assert f(A, B, 8, 4, 64, Cc, 4, D + 2, A + (1 << 30), 4, D + 4096, None) == QT_ERR_ALIGN
+    assert f(A, B, 8, 4, 64, Cc, 4, None, A + (1 << 30), 4, B + 64, None) == QT_ERR_ALIAS
+
+
+def test_hessian_rejects():
+    f = L.qt_hessian_diag
+    assert f(None, 0, 8, 64, B, 0, None, 0, None) == QT_ERR_NULL
+    assert f(A, 3, 8, 64, B, 0, None, 0, None) == QT_ERR_DTYPE
+    assert f(A, 0, 0, 64, B, 0, None, 0, None) == QT_ERR_SHAPE
+    assert f(A, 0, 8, 64, B, 2, None, 0, None) == QT_ERR_ARG
+    assert f(A + 2, 0, 8, 64, B, 0, None, 0, None) == QT_ERR_ALIGN
+    assert f(A, 0, 8192, 64, B, 0, None, 0, None) == QT_ERR_WORKSPACE
+    assert f(A, 0, 8192, 64, B, 0, Cc, 16, None) == QT_ERR_WORKSPACE
+    assert f(A, 0, 8, 64, A + 64, 0, None, 0, None) == QT_ERR_ALIAS
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        qt.qt_pack_i3(torch.zeros((2, 64), dtype=torch.int8))

@@ -1,0 +1,296 @@
+"""HIP path against the CPU oracle, element by element, through the C ABI.
+
+Bit-exact: codes, scales, chosen grid indices, packed bytes.  Floating point:
+the exact-f32 multiply paths within 1e-5 and the bf16 MFMA path within 2e-3 of
+sum_i |w_oi x_i| (componentwise against the fp64 dequantize-then-multiply).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_int3_amd as qt
+import oracle
+import workloads
+from tests.gpu_util import bits, dev, dev_bf16, host, say
+from tests.parity import componentwise_err, np_decode_planes
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_MFMA = 2e-3
+
+
+def gpu_quantize_pack(W, d=None, n_grid=0, lo=0.5, hi=1.0):
+    Wd = dev(W)
+    dd = None if d is None else dev(d)
+    s, c, k = qt.qt_quantize_g64(Wd, dd, n_grid, lo, hi)
+    p = qt.qt_pack_i3(c)
+    return host(s), host(c), host(k), host(p), (p, s)
+
+
+def check_quantize(W, d=None, n_grid=0, lo=0.5, hi=1.0):
+    O, I = W.shape
+    say(f"quantize+pack O={O} I={I} n_grid={n_grid}")
+    s, c, k, p, devbufs = gpu_quantize_pack(W, d, n_grid, lo, hi)
+    so, co, ko = oracle.quantize_g64(W, d, n_grid, lo, hi)
+    po = oracle.pack_i3(co)
+    assert np.array_equal(bits(s), bits(so)), "scales differ"
+    assert np.array_equal(c, co), "codes differ"
+    assert np.array_equal(k, ko), "grid indices differ"
+    assert np.array_equal(p, po), "packed bytes differ"
+    return so, co, po, devbufs
+
+
+# ---------------------------------------------------------------- quantize / pack
+def test_tiny_quantize_pack_matvec_and_outlier_rows():
+    W, x, rows = workloads.tiny()
+    O, I = W.shape
+    so, co, po, (pd, sd) = check_quantize(W)
+    say("matvec tiny")
+    y = host(qt.qt_matvec_i3(pd, sd, O, I, dev(x)))
+    yr, ar = oracle.matvec_f64(po, so, O, I, x)
+    assert componentwise_err(y, yr, ar) <= TOL_F32
+    # outlier rows: the GPU-produced int3-g64 reconstruction beats per-row int4
+    what = np_decode_planes(host(pd), O, I).astype(np.float64) * np.repeat(
+        host(sd).astype(np.float64), 64, axis=1)[:, :I]
+    r3 = what[rows] - W[rows]
+    r4 = oracle.rowint_recon(W, 4)[rows] - W[rows]
+    assert np.sqrt(np.mean(r3 ** 2)) < np.sqrt(np.mean(r4 ** 2))
+
+
+@pytest.mark.parametrize("tail", [False, True])
+def test_decode_quantize_pack_matvec(tail):
+    W, x = workloads.decode(tail)
+    O, I = W.shape
+    so, co, po, (pd, sd) = check_quantize(W)
+    say(f"matvec decode I={I}")
+    y1 = qt.qt_matvec_i3(pd, sd, O, I, dev(x))
+    y2 = qt.qt_matvec_i3(pd, sd, O, I, dev(x))
+    y1, y2 = host(y1), host(y2)
+    assert np.array_equal(bits(y1), bits(y2)), "matvec is not deterministic"
+    yr, ar = oracle.matvec_f64(po, so, O, I, x)
+    err = componentwise_err(y1, yr, ar)
+    say(f"  componentwise err {err:.3e}")
+    assert err <= TOL_F32
+
+
+SHAPES = [(1, 1), (1, 64), (3, 65), (17, 100), (33, 129), (5, 7200), (300, 64), (7, 1000),
+          (129, 640), (2, 4097)]
+
+
+@pytest.mark.parametrize("O,I", SHAPES)
+def test_ragged_quantize_pack_matvec(O, I):
+    W = workloads.generic_weights(O, I, seed=O * 7919 + I)
+    so, co, po, (pd, sd) = check_quantize(W)
+    x = workloads.generic_vector(I, seed=I)
+    say(f"matvec ragged O={O} I={I}")
+    y = host(qt.qt_matvec_i3(pd, sd, O, I, dev(x)))
+    yr, ar = oracle.matvec_f64(po, so, O, I, x)
+    assert componentwise_err(y, yr, ar) <= TOL_F32
+
+
+@pytest.mark.parametrize("n_grid,lo,hi", [(64, 0.5, 1.0), (2, 0.5, 1.0), (256, 0.3, 1.2),
+                                          (17, 0.75, 0.75)])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_search_bit_exact(n_grid, lo, hi, weighted):
+    O, I = 64, 1000
+    W = workloads.generic_weights(O, I, seed=n_grid)
+    W[3, :64] = 0.0  # an all-zero group
+    d = None
+    if weighted:
+        d = np.exp(workloads.generic_vector(I, seed=5)).astype(np.float32)
+        d[7] = 0.0
+    check_quantize(W, d, n_grid, lo, hi)
+
+
+def test_search_ties_and_special_groups():
+    # groups built so that many candidates tie exactly (equal magnitudes on a
+    # power-of-two grid); the lowest k must win on both sides
+    O, I = 8, 256
+    W = np.zeros((O, I), np.float32)
+    W[0] = 0.5
+    W[1, ::2] = -0.25
+    W[2] = np.tile(np.array([1.0, -1.0, 0.5, -0.5], np.float32), I // 4)
+    W[3, 5] = 3.0e-39  # a subnormal group maximum
+    W[4] = workloads.generic_weights(1, I, seed=3)[0] * np.float32(1e30)
+    W[5, 100] = -1.0
+    W[6] = np.float32(1e-30)
+    W[7] = workloads.generic_weights(1, I, seed=4)[0]
+    check_quantize(W, None, 64, 0.5, 1.0)
+    check_quantize(W, np.full(I, 2.0, np.float32), 64, 0.5, 1.0)
+
+
+@pytest.mark.parametrize("O,I", [(5, 64), (9, 100), (64, 7200), (3, 1)])
+def test_pack_random_codes(O, I):
+    rng = workloads.rng_for("generic", 31, O, I)
+    codes = rng.integers(-4, 4, size=(O, I)).astype(np.int8)
+    say(f"pack O={O} I={I}")
+    p = host(qt.qt_pack_i3(dev(codes)))
+    assert np.array_equal(p, oracle.pack_i3(codes))
+
+
+# ---------------------------------------------------------------- matvec properties
+def test_matvec_one_hot_is_exact():
+    O, I = 64, 300
+    W = workloads.generic_weights(O, I, seed=12)
+    so, co, po, (pd, sd) = check_quantize(W)
+    for i in (0, 63, 64, 200, 299):
+        x = np.zeros(I, np.float32)
+        x[i] = 1.0
+        say(f"one-hot i={i}")
+        y = host(qt.qt_matvec_i3(pd, sd, O, I, dev(x)))
+        assert np.array_equal(y, so[:, i // 64] * co[:, i].astype(np.float32))
+
+
+def test_matvec_zero_weights():
+    O, I = 16, 200
+    W = np.zeros((O, I), np.float32)
+    so, co, po, (pd, sd) = check_quantize(W)
+    y = host(qt.qt_matvec_i3(pd, sd, O, I, dev(workloads.generic_vector(I))))
+    assert np.all(y == 0)
+
+
+# ---------------------------------------------------------------- batched multiply
+def _packed_for(O, I, seed):
+    W = workloads.generic_weights(O, I, seed=seed)
+    so, co, _ = oracle.quantize_g64(W)
+    po = oracle.pack_i3(co)
+    return so, po
+
+
+def _matmul_ref(po, so, O, I, X):
+    B = X.shape[0]
+    t = np.repeat(np.arange(B), O)
+    o = np.tile(np.arange(O), B)
+    y, a = oracle.matmul_f64_sampled(po, so, O, I, X, t, o)
+    return y.reshape(B, O), a.reshape(B, O)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 9, 15, 16, 17, 40])
+def test_matmul_f32_exact_path(B):
+    O, I = 70, 650
+    so, po = _packed_for(O, I, seed=B)
+    X = workloads.generic_matrix(B, I, seed=B)
+    say(f"matmul f32 B={B}")
+    Y = host(qt.qt_matmul_i3(dev(po), dev(so), O, I, dev(X)))
+    yr, ar = _matmul_ref(po, so, O, I, X)
+    assert componentwise_err(Y, yr, ar) <= TOL_F32
+
+
+@pytest.mark.parametrize("B", [1, 7, 15])
+def test_matmul_bf16_small_batch_exact_path(B):
+    O, I = 50, 300
+    so, po = _packed_for(O, I, seed=100 + B)
+    Xb = workloads.bf16_bits_rne(workloads.generic_matrix(B, I, seed=B))
+    say(f"matmul bf16 small B={B}")
+    Y = host(qt.qt_matmul_i3(dev(po), dev(so), O, I, dev_bf16(Xb)))
+    yr, ar = _matmul_ref(po, so, O, I, workloads.bf16_bits_to_f32(Xb))
+    assert componentwise_err(Y, yr, ar) <= TOL_F32
+
+
+@pytest.mark.parametrize("B,O,I", [(16, 128, 64), (17, 200, 300), (130, 129, 640),
+                                   (300, 64, 1000), (256, 256, 7168), (33, 40, 68),
+                                   (20, 31, 5)])
+def test_matmul_bf16_mfma_path(B, O, I):
+    so, po = _packed_for(O, I, seed=B + O + I)
+    Xb = workloads.bf16_bits_rne(workloads.generic_matrix(B, I, seed=B + I))
+    say(f"matmul bf16 mfma B={B} O={O} I={I}")
+    Yd1 = qt.qt_matmul_i3(dev(po), dev(so), O, I, dev_bf16(Xb))
+    Yd2 = qt.qt_matmul_i3(dev(po), dev(so), O, I, dev_bf16(Xb))
+    Y, Y2 = host(Yd1), host(Yd2)
+    assert np.array_equal(bits(Y), bits(Y2)), "matmul is not deterministic"
+    yr, ar = _matmul_ref(po, so, O, I, workloads.bf16_bits_to_f32(Xb))
+    err = componentwise_err(Y, yr, ar)
+    say(f"  componentwise err {err:.3e}")
+    assert err <= TOL_MFMA
+
+
+def test_matmul_b1_equals_matvec():
+    O, I = 100, 777
+    so, po = _packed_for(O, I, seed=2)
+    x = workloads.generic_vector(I, seed=3)
+    y1 = host(qt.qt_matvec_i3(dev(po), dev(so), O, I, dev(x)))
+    y2 = host(qt.qt_matmul_i3(dev(po), dev(so), O, I, dev(x[None, :])))
+    assert np.array_equal(bits(y1), bits(y2[0]))
+
+
+# ---------------------------------------------------------------- grouped (MoE)
+def _grouped_case(E, O, I, T, topk, seed):
+    rng = workloads.rng_for("generic", 500 + seed, E, O, I)
+    logits = rng.random((T, E))
+    top = np.argsort(-logits, axis=1, kind="stable")[:, :topk].astype(np.int32)
+    tok, exp, offs = workloads.route_pairs(top, E)
+    Ws = [workloads.generic_weights(O, I, seed=1000 * seed + e) for e in range(E)]
+    q = [oracle.quantize_g64(w) for w in Ws]
+    so = np.stack([a[0] for a in q])
+    po = np.stack([oracle.pack_i3(a[1]) for a in q])
+    X = workloads.generic_matrix(T, I, seed=seed)
+    return tok, exp, offs, so, po, X
+
+
+@pytest.mark.parametrize("E,O,I,T,topk", [(4, 40, 300, 6, 2), (16, 64, 1000, 32, 8),
+                                          (3, 100, 64, 40, 3), (8, 33, 7200, 5, 1)])
+def test_grouped_matvec(E, O, I, T, topk):
+    tok, exp, offs, so, po, X = _grouped_case(E, O, I, T, topk, seed=E + T)
+    P = tok.size
+    say(f"grouped E={E} O={O} I={I} P={P}")
+    Y = host(qt.qt_matvec_i3_grouped(dev(po), dev(so), E, O, I, dev(X), dev(offs), P,
+                                     pair_row=dev(tok)))
+    for p in range(P):
+        e, t = exp[p], tok[p]
+        yr, ar = oracle.matvec_f64(po[e], so[e], O, I, X[t])
+        assert componentwise_err(Y[p], yr, ar) <= TOL_F32, (p, e, t)
+    # rows taken by pair index (no pair_row): the down-projection form
+    H = workloads.generic_matrix(P, I, seed=77)
+    Y2 = host(qt.qt_matvec_i3_grouped(dev(po), dev(so), E, O, I, dev(H), dev(offs), P))
+    for p in range(P):
+        yr, ar = oracle.matvec_f64(po[exp[p]], so[exp[p]], O, I, H[p])
+        assert componentwise_err(Y2[p], yr, ar) <= TOL_F32
+
+
+def test_grouped_empty_experts_and_one_pair():
+    E, O, I = 6, 20, 130
+    tok = np.array([3], np.int32)
+    offs = np.array([0, 0, 0, 1, 1, 1, 1], np.int32)
+    Ws = [workloads.generic_weights(O, I, seed=e) for e in range(E)]
+    q = [oracle.quantize_g64(w) for w in Ws]
+    so = np.stack([a[0] for a in q])
+    po = np.stack([oracle.pack_i3(a[1]) for a in q])
+    X = workloads.generic_matrix(4, I, seed=1)
+    Y = host(qt.qt_matvec_i3_grouped(dev(po), dev(so), E, O, I, dev(X), dev(offs), 1,
+                                     pair_row=dev(tok)))
+    yr, ar = oracle.matvec_f64(po[2], so[2], O, I, X[3])
+    assert componentwise_err(Y[0], yr, ar) <= TOL_F32
+
+
+# ---------------------------------------------------------------- Hessian diagonal
+@pytest.mark.parametrize("T,I", [(1, 1), (7, 100), (128, 64), (129, 1000), (1000, 333),
+                                 (4096, 2048)])
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+def test_hessian_diag(T, I, xt):
+    X = workloads.generic_matrix(T, I, seed=T + I) * np.exp(
+        workloads.generic_vector(I, seed=9))[None, :].astype(np.float32)
+    X = X.astype(np.float32)
+    if xt == "bf16":
+        Xb = workloads.bf16_bits_rne(X)
+        Xh = workloads.bf16_bits_to_f32(Xb)
+        Xd = dev_bf16(Xb)
+    else:
+        Xh, Xd = X, dev(X)
+    say(f"hessian T={T} I={I} {xt}")
+    d = host(qt.qt_hessian_diag(Xd))
+    ref = oracle.hessian_diag(Xh)
+    assert np.all(np.abs(d - ref) <= 1e-5 * ref + 1e-30)
+    # accumulate: two halves equal one pass
+    h = T // 2
+    if h > 0:
+        dd = qt.qt_hessian_diag(Xd[:h].contiguous())
+        qt.qt_hessian_diag(Xd[h:].contiguous(), d=dd, accumulate=True)
+        assert np.all(np.abs(host(dd) - ref) <= 1e-5 * ref + 1e-30)
+
+
+def test_hessian_constant_columns_closed_form():
+    T, I = 3000, 256
+    X = np.ones((T, I), np.float32)
+    d = host(qt.qt_hessian_diag(dev(X)))
+    assert np.array_equal(d, np.full(I, float(T), np.float32))
