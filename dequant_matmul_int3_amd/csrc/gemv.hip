@@ -12,19 +12,18 @@
 //    row, lane q taking groups q, q+LPR, q+2*LPR, ... of the current chunk.
 //  * The inputs of the current chunk of groups are staged in LDS as f32, one
 //    68-float slot per group (4 floats of padding shift consecutive groups by 4
-//    banks), together with each group's input sum.  All rows of a wave read the
-//    same addresses, which LDS broadcasts.
+//    banks).  All rows of a wave read the same addresses, which LDS broadcasts.
 //  * A lane fetches its groups' 24 packed bytes (three 8-byte loads) and
 //    scales before the chunk's inputs are staged, so the HBM latency overlaps
 //    the staging.
 //  * Unpacking is byte-parallel: for low-plane word L (16 codes, code 4b+i in
 //    bits 8b+2i..8b+2i+1) and the 16 matching high bits spread one nibble per
 //    byte, ((L >> 2i) & 0x03030303) | (high bits at bit 2) gives four u = v+4
-//    values, one per byte, which v_cvt_f32_ubyte{0..3} turn into floats.
-//  * sum_j v_j x_j = sum_j u_j x_j - 4 * sum_j x_j, the second term taken from
-//    the staged group sum.  Four interleaved accumulators per token hide FMA
-//    latency; the LPR partial row sums are combined by a fixed xor butterfly,
-//    so results are deterministic.
+//    values, one per byte; one v_perm_b32 table lookup maps them to the signed
+//    bytes v, which convert to f32 exactly.  Products v*x are formed with
+//    fused multiply-adds into four interleaved accumulators per token (hiding
+//    FMA latency); the LPR partial row sums are combined by a fixed xor
+//    butterfly, so results are deterministic.
 #include <algorithm>
 
 #include "qt_internal.h"
@@ -59,34 +58,37 @@ __device__ __forceinline__ uint32_t spread_hi(uint32_t h16) {
     return t << 2;
 }
 
-// acc[t][i] += u(code 16k+4b+i) * x_t[16k+4b+i] over b, i for one quarter k.
+// acc[t][i] += v(code 16k+4b+i) * x_t[16k+4b+i] over b, i for one quarter k.
+// u = v + 4 is assembled one code per byte, a byte-permute table lookup turns
+// every u into the signed byte v, and each byte is converted to f32 exactly.
 template <int T>
 __device__ __forceinline__ void quarter_fma(uint32_t L, uint32_t sp4, const float* const* xq,
                                             int k, float (&acc)[T][4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t u4 = ((L >> (2 * i)) & 0x03030303u) | ((sp4 >> i) & 0x04040404u);
-        const float u0 = (float)(u4 & 0xFFu);
-        const float u1 = (float)((u4 >> 8) & 0xFFu);
-        const float u2 = (float)((u4 >> 16) & 0xFFu);
-        const float u3 = (float)(u4 >> 24);
+        // table: u = 0..3 -> fc fd fe ff, u = 4..7 -> 00 01 02 03
+        const uint32_t v4 = __builtin_amdgcn_perm(0x03020100u, 0xFFFEFDFCu, u4);
+        const float v0 = (float)(int8_t)(uint8_t)v4;
+        const float v1 = (float)(int8_t)(uint8_t)(v4 >> 8);
+        const float v2 = (float)(int8_t)(uint8_t)(v4 >> 16);
+        const float v3 = (float)(int8_t)(uint8_t)(v4 >> 24);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             const float* x = xq[t] + 16 * k + i;
-            acc[t][i] = __builtin_fmaf(u0, x[0], acc[t][i]);
-            acc[t][i] = __builtin_fmaf(u1, x[4], acc[t][i]);
-            acc[t][i] = __builtin_fmaf(u2, x[8], acc[t][i]);
-            acc[t][i] = __builtin_fmaf(u3, x[12], acc[t][i]);
+            acc[t][i] = __builtin_fmaf(v0, x[0], acc[t][i]);
+            acc[t][i] = __builtin_fmaf(v1, x[4], acc[t][i]);
+            acc[t][i] = __builtin_fmaf(v2, x[8], acc[t][i]);
+            acc[t][i] = __builtin_fmaf(v3, x[12], acc[t][i]);
         }
     }
 }
 
-// Dot of one packed group with T staged input groups: returns, per token,
-// scale * sum_j v_j x_j added into rowacc[t].
+// Dot of one packed group with T staged input groups: adds, per token,
+// scale * sum_j v_j x_j into rowacc[t].
 template <int T>
 __device__ __forceinline__ void group_dot(const GroupBits& gb, float scale,
-                                          const float* const* xg, const float* xsum,
-                                          float (&rowacc)[T]) {
+                                          const float* const* xg, float (&rowacc)[T]) {
     float acc[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -101,18 +103,17 @@ __device__ __forceinline__ void group_dot(const GroupBits& gb, float scale,
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        float d = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
-        d = __builtin_fmaf(-4.0f, xsum[t], d);
+        const float d = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
         rowacc[t] = __builtin_fmaf(scale, d, rowacc[t]);
     }
 }
 
-// Stage tokens [tok0, tok0+nt) x groups [g0, g0+gn) of the inputs into LDS.
-// xs: [T][GC][kSlot] floats, xsum: [T][GC].  Columns at or past I read as 0.
+// Stage tokens [tok0, tok0+nt) x groups [g0, g0+gn) of the inputs into LDS
+// as [T][GC][kSlot] floats.  Columns at or past I read as 0.
 template <int T, int GC, int NTHR>
 __device__ __forceinline__ void stage_inputs(const void* __restrict__ X, bool bf16,
                                              const int32_t* rows, int nt, int64_t I,
-                                             int64_t g0, int gn, float* xs, float* xsum) {
+                                             int64_t g0, int gn, float* xs) {
     const int tid = threadIdx.x;
     // 4 columns per thread step
     const int quads = gn * (kGroup / 4);
@@ -138,20 +139,6 @@ __device__ __forceinline__ void stage_inputs(const void* __restrict__ X, bool bf
         }
     }
     __syncthreads();
-    for (int e = tid; e < nt * gn; e += NTHR) {
-        const int t = e / gn, gl = e - t * gn;
-        const float* src = xs + (t * GC + gl) * kSlot;
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-        for (int j = 0; j < kGroup; j += 4) {
-            s0 += src[j];
-            s1 += src[j + 1];
-            s2 += src[j + 2];
-            s3 += src[j + 3];
-        }
-        xsum[t * GC + gl] = (s0 + s1) + (s2 + s3);
-    }
-    __syncthreads();
 }
 
 // Rows [r0, r0+RB) of one matrix against up to T staged tokens at a time.
@@ -167,7 +154,6 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
     constexpr int NG = (GC + LPR - 1) / LPR;  // groups per lane per chunk
     static_assert(GC >= LPR, "each lane needs at least one group per chunk");
     float* xs = lds;
-    float* xsum = lds + T * GC * kSlot;
 
     const int q = threadIdx.x % LPR;
     const int64_t r = r0 + threadIdx.x / LPR;
@@ -197,19 +183,15 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
                 }
             }
             __syncthreads();  // previous chunk's readers are done with LDS
-            stage_inputs<T, GC, NTHR>(X, bf16, tok_rows + tt, nt, I, g0, gn, xs, xsum);
+            stage_inputs<T, GC, NTHR>(X, bf16, tok_rows + tt, nt, I, g0, gn, xs);
 #pragma unroll
             for (int m = 0; m < NG; ++m) {
                 const int gl = q + m * LPR;
                 if (row_ok && gl < gn) {
                     const float* xg[T];
-                    float xsm[T];
 #pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        xg[t] = xs + (t * GC + gl) * kSlot;
-                        xsm[t] = xsum[t * GC + gl];
-                    }
-                    group_dot<T>(gb[m], sc[m], xg, xsm, rowacc);
+                    for (int t = 0; t < T; ++t) xg[t] = xs + (t * GC + gl) * kSlot;
+                    group_dot<T>(gb[m], sc[m], xg, rowacc);
                 }
             }
         }
@@ -230,7 +212,7 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
 
 template <int T>
 constexpr size_t lds_bytes() {
-    return (size_t)T * (128 / T) * (kSlot + 1) * sizeof(float);
+    return (size_t)T * (128 / T) * kSlot * sizeof(float);
 }
 
 // ---------------------------------------------------------------- kernels

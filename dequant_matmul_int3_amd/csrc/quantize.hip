@@ -143,8 +143,9 @@ __global__ __launch_bounds__(256) void pack_i3_kernel(const int8_t* __restrict__
     uint32_t hi[2] = {0, 0};
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-        // u = v + 4 in every byte (v in [-4,3] -> u in [0,7]), low 3 bits kept
-        const uint32_t u4 = (c[q] + 0x04040404u) & 0x07070707u;
+        // u = (v + 4) mod 8 in every byte: flipping bit 2 of the low three
+        // bits of v (no carry crosses a byte)
+        const uint32_t u4 = (c[q] & 0x07070707u) ^ 0x04040404u;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const uint32_t u = (u4 >> (8 * b)) & 7u;
