@@ -13,17 +13,17 @@
 //  * The inputs of the current chunk of groups are staged in LDS as f32, one
 //    68-float slot per group (4 floats of padding shift consecutive groups by 4
 //    banks).  All rows of a wave read the same addresses, which LDS broadcasts.
-//  * A lane fetches its groups' 24 packed bytes (three 8-byte loads) and
-//    scales before the chunk's inputs are staged, so the HBM latency overlaps
-//    the staging.
+//  * Every thread issues its input loads, then its weight loads (24 packed
+//    bytes and a scale per group), and only then waits to store the inputs to
+//    LDS, so the two latencies overlap.
 //  * Unpacking is byte-parallel: for low-plane word L (16 codes, code 4b+i in
 //    bits 8b+2i..8b+2i+1) and the 16 matching high bits spread one nibble per
 //    byte, ((L >> 2i) & 0x03030303) | (high bits at bit 2) gives four u = v+4
-//    values, one per byte; one v_perm_b32 table lookup maps them to the signed
-//    bytes v, which convert to f32 exactly.  Products v*x are formed with
-//    fused multiply-adds into four interleaved accumulators per token (hiding
-//    FMA latency); the LPR partial row sums are combined by a fixed xor
-//    butterfly, so results are deterministic.
+//    values, one per byte; v_perm_b32 table lookups turn them into f16 pairs
+//    of v (exact), and v_fma_mix_f32 multiplies each by its f32 input with one
+//    f32 rounding.  Four interleaved accumulators per token hide FMA latency;
+//    the LPR partial row sums are combined by a fixed xor butterfly, so
+//    results are deterministic.
 #include <algorithm>
 
 #include "qt_internal.h"
@@ -34,6 +34,7 @@ namespace {
 constexpr int kSlot = kGroup + 4;  // padded LDS floats per group
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 struct GroupBits {
     u32x2_t a, b, c;  // low plane words 0..3, then the high plane
@@ -58,35 +59,36 @@ __device__ __forceinline__ uint32_t spread_hi(uint32_t h16) {
     return t << 2;
 }
 
-// acc[t][i] += v(code 16k+4b+i) * x_t[16k+4b+i] over b, i for one quarter k.
-// u = v + 4 is assembled one code per byte, a byte-permute table lookup turns
-// every u into the signed byte v, and each byte is converted to f32 exactly.
-template <int T>
+// acc[t][i] += v(code 16k+4b+i) * x_t[16k+4b+i] over b, i for one quarter k,
+// for the first NT of T tokens.  u = v + 4 is assembled one code per byte; a
+// byte-permute table lookup maps every u to the high byte of the f16 encoding
+// of v (whose low byte is zero for v in [-4, 3]) and two more permutes place
+// the codes as f16 pairs.  v_fma_mix_f32 then multiplies each f16 code (exact)
+// by the f32 input with a single f32 rounding, as an f32 fused multiply-add.
+template <int T, int NT>
 __device__ __forceinline__ void quarter_fma(uint32_t L, uint32_t sp4, const float* const* xq,
                                             int k, float (&acc)[T][4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t u4 = ((L >> (2 * i)) & 0x03030303u) | ((sp4 >> i) & 0x04040404u);
-        // table: u = 0..3 -> fc fd fe ff, u = 4..7 -> 00 01 02 03
-        const uint32_t v4 = __builtin_amdgcn_perm(0x03020100u, 0xFFFEFDFCu, u4);
-        const float v0 = (float)(int8_t)(uint8_t)v4;
-        const float v1 = (float)(int8_t)(uint8_t)(v4 >> 8);
-        const float v2 = (float)(int8_t)(uint8_t)(v4 >> 16);
-        const float v3 = (float)(int8_t)(uint8_t)(v4 >> 24);
+        // f16(v) high bytes: u = 0..3 -> c4 c2 c0 bc, u = 4..7 -> 00 3c 40 42
+        const uint32_t hb = __builtin_amdgcn_perm(0x42403C00u, 0xBCC0C2C4u, u4);
+        const half2_t p01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hb, hb, 0x010C000Cu));
+        const half2_t p23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hb, hb, 0x030C020Cu));
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
+        for (int t = 0; t < NT; ++t) {
             const float* x = xq[t] + 16 * k + i;
-            acc[t][i] = __builtin_fmaf(v0, x[0], acc[t][i]);
-            acc[t][i] = __builtin_fmaf(v1, x[4], acc[t][i]);
-            acc[t][i] = __builtin_fmaf(v2, x[8], acc[t][i]);
-            acc[t][i] = __builtin_fmaf(v3, x[12], acc[t][i]);
+            acc[t][i] = __builtin_fmaf((float)p01.x, x[0], acc[t][i]);
+            acc[t][i] = __builtin_fmaf((float)p01.y, x[4], acc[t][i]);
+            acc[t][i] = __builtin_fmaf((float)p23.x, x[8], acc[t][i]);
+            acc[t][i] = __builtin_fmaf((float)p23.y, x[12], acc[t][i]);
         }
     }
 }
 
-// Dot of one packed group with T staged input groups: adds, per token,
-// scale * sum_j v_j x_j into rowacc[t].
-template <int T>
+// Dot of one packed group with the first NT staged input groups: adds, per
+// token, scale * sum_j v_j x_j into rowacc[t].
+template <int T, int NT>
 __device__ __forceinline__ void group_dot(const GroupBits& gb, float scale,
                                           const float* const* xg, float (&rowacc)[T]) {
     float acc[T][4];
@@ -99,58 +101,116 @@ __device__ __forceinline__ void group_dot(const GroupBits& gb, float scale,
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint32_t h16 = (H[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-        quarter_fma<T>(L[k], spread_hi(h16), xg, k, acc);
+        quarter_fma<T, NT>(L[k], spread_hi(h16), xg, k, acc);
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+    for (int t = 0; t < NT; ++t) {
         const float d = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
         rowacc[t] = __builtin_fmaf(scale, d, rowacc[t]);
     }
 }
 
-// Stage tokens [tok0, tok0+nt) x groups [g0, g0+gn) of the inputs into LDS
-// as [T][GC][kSlot] floats.  Columns at or past I read as 0.
-template <int T, int GC, int NTHR>
-__device__ __forceinline__ void stage_inputs(const void* __restrict__ X, bool bf16,
-                                             const int32_t* rows, int nt, int64_t I,
-                                             int64_t g0, int gn, float* xs) {
-    const int tid = threadIdx.x;
-    // 4 columns per thread step
-    const int quads = gn * (kGroup / 4);
-    for (int t = 0; t < nt; ++t) {
-        const int64_t row = rows[t];
-        for (int qd = tid; qd < quads; qd += NTHR) {
-            const int gl = qd >> 4;
-            const int j = (qd & 15) * 4;
-            const int64_t col = (g0 + gl) * kGroup + j;
-            float v[4];
-            if (bf16) {
-                const uint16_t* xr = reinterpret_cast<const uint16_t*>(X) + row * I;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = col + e < I ? __uint_as_float((uint32_t)xr[col + e] << 16) : 0.0f;
-            } else {
-                const float* xr = reinterpret_cast<const float*>(X) + row * I;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = col + e < I ? xr[col + e] : 0.0f;
-            }
-            float* dst = xs + (t * GC + gl) * kSlot + j;
-            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+// Dispatch on the number of live tokens of a tile (uniform over the block), so
+// that no multiply is spent on tokens that are not there.
+template <int T>
+__device__ __forceinline__ void group_dot_n(int nt, const GroupBits& gb, float scale,
+                                            const float* const* xg, float (&rowacc)[T]) {
+    if constexpr (T == 1) {
+        group_dot<T, 1>(gb, scale, xg, rowacc);
+    } else {
+        switch (nt) {
+            case 1: group_dot<T, 1>(gb, scale, xg, rowacc); break;
+            case 2: if constexpr (T >= 2) group_dot<T, 2>(gb, scale, xg, rowacc); break;
+            case 3: if constexpr (T >= 3) group_dot<T, 3>(gb, scale, xg, rowacc); break;
+            case 4: if constexpr (T >= 4) group_dot<T, 4>(gb, scale, xg, rowacc); break;
+            default: group_dot<T, T>(gb, scale, xg, rowacc); break;
         }
     }
-    __syncthreads();
 }
 
-// Rows [r0, r0+RB) of one matrix against up to T staged tokens at a time.
-// rows_of_tok: input row of each token; out_of_tok: output row (times O) of
-// each token.  Tokens are processed in tiles of T.
+// Inputs of tokens [0, nt) x groups [g0, g0+gn), staged in LDS as
+// [T][GC][kSlot] floats.  Columns at or past I read as 0.  load() issues all
+// of a thread's global loads (16-byte ones where the row allows); store()
+// writes them to LDS.  Callers issue the weight loads between the two.
+template <int T, int GC, int NTHR>
+struct InputStage {
+    static constexpr int QUADS = GC * (kGroup / 4);  // 4-column pieces per token
+    static constexpr int QPT = (QUADS + NTHR - 1) / NTHR;
+    float4 v[T][QPT];
+
+    __device__ __forceinline__ void load(const void* __restrict__ X, bool bf16, bool xvec,
+                                         const int32_t* rows, int nt, int64_t I, int64_t g0,
+                                         int gn) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int64_t row = t < nt ? rows[t] : 0;
+#pragma unroll
+            for (int j = 0; j < QPT; ++j) {
+                const int qd = tid + j * NTHR;
+                const int gl = qd >> 4;
+                const int64_t col = (g0 + gl) * kGroup + (qd & 15) * 4;
+                float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (t < nt && qd < QUADS && gl < gn) {
+                    if (bf16) {
+                        const uint16_t* xr = reinterpret_cast<const uint16_t*>(X) + row * I;
+                        if (xvec && col + 4 <= I) {
+                            const uint2 w = *reinterpret_cast<const uint2*>(xr + col);
+                            r = make_float4(__uint_as_float(w.x << 16),
+                                            __uint_as_float(w.x & 0xFFFF0000u),
+                                            __uint_as_float(w.y << 16),
+                                            __uint_as_float(w.y & 0xFFFF0000u));
+                        } else {
+                            float e[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                e[q] = col + q < I
+                                           ? __uint_as_float((uint32_t)xr[col + q] << 16)
+                                           : 0.0f;
+                            r = make_float4(e[0], e[1], e[2], e[3]);
+                        }
+                    } else {
+                        const float* xr = reinterpret_cast<const float*>(X) + row * I;
+                        if (xvec && col + 4 <= I) {
+                            r = *reinterpret_cast<const float4*>(xr + col);
+                        } else {
+                            float e[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) e[q] = col + q < I ? xr[col + q] : 0.0f;
+                            r = make_float4(e[0], e[1], e[2], e[3]);
+                        }
+                    }
+                }
+                v[t][j] = r;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(int nt, float* xs) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int j = 0; j < QPT; ++j) {
+                const int qd = tid + j * NTHR;
+                if (t < nt && qd < QUADS) {
+                    float* dst = xs + (t * GC + (qd >> 4)) * kSlot + (qd & 15) * 4;
+                    *reinterpret_cast<float4*>(dst) = v[t][j];
+                }
+            }
+    }
+};
+
+// Rows [r0, r0+RB) of one matrix against the tokens listed in tok_rows
+// (input row of each token) / tok_outs (output row of each token, -1 = do not
+// store), T tokens per pass over the weights.
 template <int LPR, int WAVES, int T>
 __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __restrict__ scales,
                           int64_t O, int64_t I, int64_t G, const void* __restrict__ X, bool bf16,
-                          const int32_t* tok_rows, const int32_t* tok_outs, int ntok,
+                          bool xvec, const int32_t* tok_rows, const int32_t* tok_outs, int ntok,
                           float* __restrict__ Y, int64_t r0, float* lds) {
     constexpr int NTHR = WAVES * 64;
-    constexpr int GC = 128 / T;          // groups per chunk
+    constexpr int GC = 128 / T;               // groups per chunk
     constexpr int NG = (GC + LPR - 1) / LPR;  // groups per lane per chunk
     static_assert(GC >= LPR, "each lane needs at least one group per chunk");
     float* xs = lds;
@@ -167,7 +227,9 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
 
         for (int64_t g0 = 0; g0 < G; g0 += GC) {
             const int gn = (int)min<int64_t>(GC, G - g0);
-            // issue this lane's weight loads before staging the inputs
+            __syncthreads();  // previous chunk's readers are done with LDS
+            InputStage<T, GC, NTHR> stage;
+            stage.load(X, bf16, xvec, tok_rows + tt, nt, I, g0, gn);
             GroupBits gb[NG];
             float sc[NG];
 #pragma unroll
@@ -182,8 +244,8 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
                     sc[m] = 0.0f;
                 }
             }
-            __syncthreads();  // previous chunk's readers are done with LDS
-            stage_inputs<T, GC, NTHR>(X, bf16, tok_rows + tt, nt, I, g0, gn, xs);
+            stage.store(nt, xs);
+            __syncthreads();
 #pragma unroll
             for (int m = 0; m < NG; ++m) {
                 const int gl = q + m * LPR;
@@ -191,7 +253,7 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
                     const float* xg[T];
 #pragma unroll
                     for (int t = 0; t < T; ++t) xg[t] = xs + (t * GC + gl) * kSlot;
-                    group_dot<T>(gb[m], sc[m], xg, rowacc);
+                    group_dot_n<T>(nt, gb[m], sc[m], xg, rowacc);
                 }
             }
         }
@@ -221,23 +283,24 @@ constexpr int kMaxTok = 16;  // token rows per launch chunk of the batch kernel
 template <int LPR, int WAVES, int T>
 __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
-    int64_t G, const void* __restrict__ X, int bf16, int64_t tok0, int ntok,
+    int64_t G, const void* __restrict__ X, int bf16, int xvec, int64_t tok0, int ntok,
     float* __restrict__ Y) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     __shared__ int32_t rows[kMaxTok];
     if (threadIdx.x < kMaxTok) rows[threadIdx.x] = (int32_t)(tok0 + threadIdx.x);
     __syncthreads();
     constexpr int RB = WAVES * 64 / LPR;
-    gemv_rows<LPR, WAVES, T>(packed, scales, O, I, G, X, bf16 != 0, rows, rows, ntok, Y,
-                             (int64_t)blockIdx.x * RB, lds);
+    gemv_rows<LPR, WAVES, T>(packed, scales, O, I, G, X, bf16 != 0, xvec != 0, rows, rows, ntok,
+                             Y, (int64_t)blockIdx.x * RB, lds);
 }
 
 // grid: (row blocks, experts).  Pairs of expert e: [off[e], off[e+1]).
 template <int LPR, int WAVES, int T>
 __global__ __launch_bounds__(WAVES * 64) void gemv_grouped_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
-    int64_t G, const float* __restrict__ X, int64_t n_x_rows, const int32_t* __restrict__ pair_row,
-    const int32_t* __restrict__ off, int32_t E, int32_t P, float* __restrict__ Y) {
+    int64_t G, const float* __restrict__ X, int xvec, int64_t n_x_rows,
+    const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t E, int32_t P,
+    float* __restrict__ Y) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     __shared__ int32_t rows[kMaxTok];
     __shared__ int32_t outs[kMaxTok];
@@ -253,14 +316,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_grouped_kernel(
         __syncthreads();
         if (threadIdx.x < n) {
             const int32_t p = pb + threadIdx.x;
-            int32_t xr = pair_row ? pair_row[p] : p;
+            const int32_t xr = pair_row ? pair_row[p] : p;
             // out-of-range rows read row 0 and are not written; the host
             // documents the valid range, this only keeps accesses in bounds
-            outs[threadIdx.x] = (xr >= 0 && xr < n_x_rows) ? p : -1;
-            rows[threadIdx.x] = (xr >= 0 && xr < n_x_rows) ? xr : 0;
+            const bool ok = xr >= 0 && xr < n_x_rows;
+            outs[threadIdx.x] = ok ? p : -1;
+            rows[threadIdx.x] = ok ? xr : 0;
         }
         __syncthreads();
-        gemv_rows<LPR, WAVES, T>(pk, sc, O, I, G, X, false, rows, outs, n, Y,
+        gemv_rows<LPR, WAVES, T>(pk, sc, O, I, G, X, false, xvec != 0, rows, outs, n, Y,
                                  (int64_t)blockIdx.x * RB, lds);
     }
 }
@@ -275,11 +339,14 @@ static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t 
     const int64_t G = (I + kGroup - 1) / kGroup;
     constexpr int RB = WAVES * 64 / LPR;
     const int64_t blocks = (O + RB - 1) / RB;
+    // 16-byte (f32) or 8-byte (bf16) input loads need aligned rows
+    const uintptr_t al = bf16 ? 8 : 16;
+    const int xvec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & (al - 1)) == 0);
     for (int64_t t0 = 0; t0 < ntok; t0 += kMaxTok) {
         const int n = (int)std::min<int64_t>(kMaxTok, ntok - t0);
         hipLaunchKernelGGL((gemv_batch_kernel<LPR, WAVES, T>), dim3((unsigned)blocks),
                            dim3(WAVES * 64), lds_bytes<T>(), s, packed, scales, O, I, G, X,
-                           (int)bf16, t0, n, Y);
+                           (int)bf16, xvec, t0, n, Y);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -289,7 +356,7 @@ static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t 
 hipError_t launch_gemv_batch(const uint8_t* packed, const float* scales, int64_t O,
                              int64_t I, const void* X, bool bf16, int64_t ntok, float* Y,
                              hipStream_t s) {
-    if (ntok == 1) return run_batch<32, 4, 1>(packed, scales, O, I, X, bf16, 1, Y, s);
+    if (ntok == 1) return run_batch<64, 8, 1>(packed, scales, O, I, X, bf16, 1, Y, s);
     if (ntok == 2) return run_batch<32, 4, 2>(packed, scales, O, I, X, bf16, 2, Y, s);
     if (ntok <= 4) return run_batch<16, 4, 4>(packed, scales, O, I, X, bf16, ntok, Y, s);
     return run_batch<16, 4, 8>(packed, scales, O, I, X, bf16, ntok, Y, s);
@@ -303,8 +370,9 @@ hipError_t launch_gemv_grouped(const uint8_t* packed, const float* scales, int32
     constexpr int RB = WAVES * 64 / LPR;
     const int64_t G = (I + kGroup - 1) / kGroup;
     const int64_t rb = (O + RB - 1) / RB;
+    const int xvec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     hipLaunchKernelGGL((gemv_grouped_kernel<LPR, WAVES, T>), dim3((unsigned)rb, (unsigned)E),
-                       dim3(WAVES * 64), lds_bytes<T>(), s, packed, scales, O, I, G, X,
+                       dim3(WAVES * 64), lds_bytes<T>(), s, packed, scales, O, I, G, X, xvec,
                        n_x_rows, pair_row, expert_offsets, E, P, Y);
     return hipGetLastError();
 }
