@@ -130,58 +130,62 @@ __device__ __forceinline__ void group_dot_n(int nt, const GroupBits& gb, float s
 
 // Inputs of tokens [0, nt) x groups [g0, g0+gn), staged in LDS as
 // [T][GC][kSlot] floats.  Columns at or past I read as 0.  load() issues all
-// of a thread's global loads (16-byte ones where the row allows); store()
-// writes them to LDS.  Callers issue the weight loads between the two.
-template <int T, int GC, int NTHR>
+// of a thread's global loads without any branch (out-of-range pieces load a
+// valid address and are replaced by zero), so they are all in flight at once;
+// store() writes them to LDS.  Callers issue the weight loads in between.
+// BF16: inputs are bf16 bit patterns, widened exactly.  VEC: rows allow 16-byte
+// (f32) or 8-byte (bf16) loads of 4 columns, I % 4 == 0.
+template <int T, int GC, int NTHR, bool BF16, bool VEC>
 struct InputStage {
     static constexpr int QUADS = GC * (kGroup / 4);  // 4-column pieces per token
     static constexpr int QPT = (QUADS + NTHR - 1) / NTHR;
     float4 v[T][QPT];
 
-    __device__ __forceinline__ void load(const void* __restrict__ X, bool bf16, bool xvec,
-                                         const int32_t* rows, int nt, int64_t I, int64_t g0,
-                                         int gn) {
+    __device__ __forceinline__ void load(const void* __restrict__ X, const int32_t* rows, int nt,
+                                         int64_t I, int64_t g0, int gn) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int64_t row = t < nt ? rows[t] : 0;
+            const int64_t row = rows[t < nt ? t : 0];
 #pragma unroll
             for (int j = 0; j < QPT; ++j) {
                 const int qd = tid + j * NTHR;
                 const int gl = qd >> 4;
                 const int64_t col = (g0 + gl) * kGroup + (qd & 15) * 4;
-                float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (t < nt && qd < QUADS && gl < gn) {
-                    if (bf16) {
-                        const uint16_t* xr = reinterpret_cast<const uint16_t*>(X) + row * I;
-                        if (xvec && col + 4 <= I) {
-                            const uint2 w = *reinterpret_cast<const uint2*>(xr + col);
-                            r = make_float4(__uint_as_float(w.x << 16),
-                                            __uint_as_float(w.x & 0xFFFF0000u),
-                                            __uint_as_float(w.y << 16),
-                                            __uint_as_float(w.y & 0xFFFF0000u));
-                        } else {
-                            float e[4];
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                e[q] = col + q < I
-                                           ? __uint_as_float((uint32_t)xr[col + q] << 16)
-                                           : 0.0f;
-                            r = make_float4(e[0], e[1], e[2], e[3]);
-                        }
+                const bool live = t < nt && qd < QUADS && gl < gn;
+                if constexpr (VEC) {
+                    const bool ok = live && col < I;
+                    const int64_t c = ok ? col : 0;
+                    float4 r;
+                    if constexpr (BF16) {
+                        const uint2 w = *reinterpret_cast<const uint2*>(
+                            reinterpret_cast<const uint16_t*>(X) + row * I + c);
+                        r = make_float4(__uint_as_float(w.x << 16),
+                                        __uint_as_float(w.x & 0xFFFF0000u),
+                                        __uint_as_float(w.y << 16),
+                                        __uint_as_float(w.y & 0xFFFF0000u));
                     } else {
-                        const float* xr = reinterpret_cast<const float*>(X) + row * I;
-                        if (xvec && col + 4 <= I) {
-                            r = *reinterpret_cast<const float4*>(xr + col);
-                        } else {
-                            float e[4];
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) e[q] = col + q < I ? xr[col + q] : 0.0f;
-                            r = make_float4(e[0], e[1], e[2], e[3]);
-                        }
+                        r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(X) +
+                                                             row * I + c);
                     }
+                    v[t][j] = ok ? r : make_float4(0.f, 0.f, 0.f, 0.f);
+                } else {
+                    float e[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bool ok = live && col + q < I;
+                        const int64_t c = ok ? col + q : 0;
+                        float f;
+                        if constexpr (BF16)
+                            f = __uint_as_float(
+                                (uint32_t)(reinterpret_cast<const uint16_t*>(X)[row * I + c])
+                                << 16);
+                        else
+                            f = reinterpret_cast<const float*>(X)[row * I + c];
+                        e[q] = ok ? f : 0.0f;
+                    }
+                    v[t][j] = make_float4(e[0], e[1], e[2], e[3]);
                 }
-                v[t][j] = r;
             }
         }
     }
@@ -204,10 +208,10 @@ struct InputStage {
 // Rows [r0, r0+RB) of one matrix against the tokens listed in tok_rows
 // (input row of each token) / tok_outs (output row of each token, -1 = do not
 // store), T tokens per pass over the weights.
-template <int LPR, int WAVES, int T>
+template <int LPR, int WAVES, int T, bool BF16, bool VEC>
 __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __restrict__ scales,
-                          int64_t O, int64_t I, int64_t G, const void* __restrict__ X, bool bf16,
-                          bool xvec, const int32_t* tok_rows, const int32_t* tok_outs, int ntok,
+                          int64_t O, int64_t I, int64_t G, const void* __restrict__ X,
+                          const int32_t* tok_rows, const int32_t* tok_outs, int ntok,
                           float* __restrict__ Y, int64_t r0, float* lds) {
     constexpr int NTHR = WAVES * 64;
     constexpr int GC = 128 / T;               // groups per chunk
@@ -227,22 +231,20 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
 
         for (int64_t g0 = 0; g0 < G; g0 += GC) {
             const int gn = (int)min<int64_t>(GC, G - g0);
-            __syncthreads();  // previous chunk's readers are done with LDS
-            InputStage<T, GC, NTHR> stage;
-            stage.load(X, bf16, xvec, tok_rows + tt, nt, I, g0, gn);
+            if (tt > 0 || g0 > 0) __syncthreads();  // earlier readers are done with LDS
+            InputStage<T, GC, NTHR, BF16, VEC> stage;
+            stage.load(X, tok_rows + tt, nt, I, g0, gn);
+            // weight loads, branch-free: idle lanes load group 0 of the block's
+            // first row (always valid) and are not used
             GroupBits gb[NG];
             float sc[NG];
 #pragma unroll
             for (int m = 0; m < NG; ++m) {
                 const int gl = q + m * LPR;
-                if (row_ok && gl < gn) {
-                    const int64_t gi = r * G + g0 + gl;
-                    gb[m] = load_group(packed + gi * kGroupBytes);
-                    sc[m] = scales[gi];
-                } else {
-                    gb[m] = GroupBits{};
-                    sc[m] = 0.0f;
-                }
+                const bool ok = row_ok && gl < gn;
+                const int64_t gi = ok ? r * G + g0 + gl : r0 * G;
+                gb[m] = load_group(packed + gi * kGroupBytes);
+                sc[m] = scales[gi];
             }
             stage.store(nt, xs);
             __syncthreads();
@@ -257,11 +259,34 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
                 }
             }
         }
-        // combine the LPR partial sums of each row (fixed butterfly)
+        // combine the LPR partial sums of each row: a fixed xor butterfly
+        // inside the wave, then (rows wider than a wave) the per-wave sums in
+        // wave order through LDS
+        constexpr int WL = LPR < 64 ? LPR : 64;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
 #pragma unroll
-            for (int m = LPR / 2; m >= 1; m >>= 1) rowacc[t] += __shfl_xor(rowacc[t], m, LPR);
+            for (int m = WL / 2; m >= 1; m >>= 1) rowacc[t] += __shfl_xor(rowacc[t], m, WL);
+        }
+        if constexpr (LPR > 64) {
+            constexpr int PARTS = LPR / 64;
+            __syncthreads();  // every wave is done reading the staged inputs
+            float* part = xs;  // [row in block][part][T]
+            const int rb = threadIdx.x / LPR, pw = q / 64;
+            if ((q & 63) == 0) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) part[(rb * PARTS + pw) * T + t] = rowacc[t];
+            }
+            __syncthreads();
+            if (q == 0) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    float a = part[(rb * PARTS) * T + t];
+#pragma unroll
+                    for (int w = 1; w < PARTS; ++w) a += part[(rb * PARTS + w) * T + t];
+                    rowacc[t] = a;
+                }
+            }
         }
         if (row_ok && q == 0) {
 #pragma unroll
@@ -280,25 +305,24 @@ constexpr size_t lds_bytes() {
 // ---------------------------------------------------------------- kernels
 constexpr int kMaxTok = 16;  // token rows per launch chunk of the batch kernel
 
-template <int LPR, int WAVES, int T>
+template <int LPR, int WAVES, int T, bool BF16, bool VEC>
 __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
-    int64_t G, const void* __restrict__ X, int bf16, int xvec, int64_t tok0, int ntok,
-    float* __restrict__ Y) {
+    int64_t G, const void* __restrict__ X, int64_t tok0, int ntok, float* __restrict__ Y) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     __shared__ int32_t rows[kMaxTok];
     if (threadIdx.x < kMaxTok) rows[threadIdx.x] = (int32_t)(tok0 + threadIdx.x);
     __syncthreads();
     constexpr int RB = WAVES * 64 / LPR;
-    gemv_rows<LPR, WAVES, T>(packed, scales, O, I, G, X, bf16 != 0, xvec != 0, rows, rows, ntok,
-                             Y, (int64_t)blockIdx.x * RB, lds);
+    gemv_rows<LPR, WAVES, T, BF16, VEC>(packed, scales, O, I, G, X, rows, rows, ntok, Y,
+                                        (int64_t)blockIdx.x * RB, lds);
 }
 
 // grid: (row blocks, experts).  Pairs of expert e: [off[e], off[e+1]).
-template <int LPR, int WAVES, int T>
+template <int LPR, int WAVES, int T, bool VEC>
 __global__ __launch_bounds__(WAVES * 64) void gemv_grouped_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
-    int64_t G, const float* __restrict__ X, int xvec, int64_t n_x_rows,
+    int64_t G, const float* __restrict__ X, int64_t n_x_rows,
     const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t E, int32_t P,
     float* __restrict__ Y) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -324,8 +348,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_grouped_kernel(
             rows[threadIdx.x] = ok ? xr : 0;
         }
         __syncthreads();
-        gemv_rows<LPR, WAVES, T>(pk, sc, O, I, G, X, false, xvec != 0, rows, outs, n, Y,
-                                 (int64_t)blockIdx.x * RB, lds);
+        gemv_rows<LPR, WAVES, T, false, VEC>(pk, sc, O, I, G, X, rows, outs, n, Y,
+                                             (int64_t)blockIdx.x * RB, lds);
     }
 }
 
@@ -333,33 +357,43 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_grouped_kernel(
 
 // Decode and small batches.  LPR/WAVES chosen so that O/RB blocks cover the
 // chip; tokens in tiles of T per pass over the weights.
-template <int LPR, int WAVES, int T>
+template <int LPR, int WAVES, int T, bool BF16, bool VEC>
 static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
-                            const void* X, bool bf16, int64_t ntok, float* Y, hipStream_t s) {
+                            const void* X, int64_t ntok, float* Y, hipStream_t s) {
     const int64_t G = (I + kGroup - 1) / kGroup;
     constexpr int RB = WAVES * 64 / LPR;
     const int64_t blocks = (O + RB - 1) / RB;
-    // 16-byte (f32) or 8-byte (bf16) input loads need aligned rows
-    const uintptr_t al = bf16 ? 8 : 16;
-    const int xvec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & (al - 1)) == 0);
     for (int64_t t0 = 0; t0 < ntok; t0 += kMaxTok) {
         const int n = (int)std::min<int64_t>(kMaxTok, ntok - t0);
-        hipLaunchKernelGGL((gemv_batch_kernel<LPR, WAVES, T>), dim3((unsigned)blocks),
-                           dim3(WAVES * 64), lds_bytes<T>(), s, packed, scales, O, I, G, X,
-                           (int)bf16, xvec, t0, n, Y);
+        hipLaunchKernelGGL((gemv_batch_kernel<LPR, WAVES, T, BF16, VEC>), dim3((unsigned)blocks),
+                           dim3(WAVES * 64), lds_bytes<T>(), s, packed, scales, O, I, G, X, t0, n,
+                           Y);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
+template <bool BF16, bool VEC>
+static hipError_t batch_dispatch(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                                 const void* X, int64_t ntok, float* Y, hipStream_t s) {
+    if (ntok == 1) return run_batch<64, 8, 1, BF16, VEC>(packed, scales, O, I, X, 1, Y, s);
+    if (ntok == 2) return run_batch<32, 4, 2, BF16, VEC>(packed, scales, O, I, X, 2, Y, s);
+    if (ntok <= 4) return run_batch<16, 4, 4, BF16, VEC>(packed, scales, O, I, X, ntok, Y, s);
+    return run_batch<16, 4, 8, BF16, VEC>(packed, scales, O, I, X, ntok, Y, s);
+}
+
 hipError_t launch_gemv_batch(const uint8_t* packed, const float* scales, int64_t O,
                              int64_t I, const void* X, bool bf16, int64_t ntok, float* Y,
                              hipStream_t s) {
-    if (ntok == 1) return run_batch<64, 8, 1>(packed, scales, O, I, X, bf16, 1, Y, s);
-    if (ntok == 2) return run_batch<32, 4, 2>(packed, scales, O, I, X, bf16, 2, Y, s);
-    if (ntok <= 4) return run_batch<16, 4, 4>(packed, scales, O, I, X, bf16, ntok, Y, s);
-    return run_batch<16, 4, 8>(packed, scales, O, I, X, bf16, ntok, Y, s);
+    // 16-byte (f32) or 8-byte (bf16) input loads need aligned rows
+    const uintptr_t al = bf16 ? 8 : 16;
+    const bool vec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & (al - 1)) == 0);
+    if (bf16)
+        return vec ? batch_dispatch<true, true>(packed, scales, O, I, X, ntok, Y, s)
+                   : batch_dispatch<true, false>(packed, scales, O, I, X, ntok, Y, s);
+    return vec ? batch_dispatch<false, true>(packed, scales, O, I, X, ntok, Y, s)
+               : batch_dispatch<false, false>(packed, scales, O, I, X, ntok, Y, s);
 }
 
 hipError_t launch_gemv_grouped(const uint8_t* packed, const float* scales, int32_t E,
@@ -370,10 +404,17 @@ hipError_t launch_gemv_grouped(const uint8_t* packed, const float* scales, int32
     constexpr int RB = WAVES * 64 / LPR;
     const int64_t G = (I + kGroup - 1) / kGroup;
     const int64_t rb = (O + RB - 1) / RB;
-    const int xvec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-    hipLaunchKernelGGL((gemv_grouped_kernel<LPR, WAVES, T>), dim3((unsigned)rb, (unsigned)E),
-                       dim3(WAVES * 64), lds_bytes<T>(), s, packed, scales, O, I, G, X, xvec,
-                       n_x_rows, pair_row, expert_offsets, E, P, Y);
+    const bool vec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    if (vec)
+        hipLaunchKernelGGL((gemv_grouped_kernel<LPR, WAVES, T, true>),
+                           dim3((unsigned)rb, (unsigned)E), dim3(WAVES * 64), lds_bytes<T>(), s,
+                           packed, scales, O, I, G, X, n_x_rows, pair_row, expert_offsets, E, P,
+                           Y);
+    else
+        hipLaunchKernelGGL((gemv_grouped_kernel<LPR, WAVES, T, false>),
+                           dim3((unsigned)rb, (unsigned)E), dim3(WAVES * 64), lds_bytes<T>(), s,
+                           packed, scales, O, I, G, X, n_x_rows, pair_row, expert_offsets, E, P,
+                           Y);
     return hipGetLastError();
 }
 
