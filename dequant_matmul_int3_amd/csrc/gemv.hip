@@ -139,7 +139,8 @@ template <int T, int GC, int NTHR, bool BF16, bool VEC>
 struct InputStage {
     static constexpr int QUADS = GC * (kGroup / 4);  // 4-column pieces per token
     static constexpr int QPT = (QUADS + NTHR - 1) / NTHR;
-    float4 v[T][QPT];
+    uint4 raw_[T][QPT];  // loaded bits (f32, or bf16 pairs in x, y)
+    bool ok_[T][QPT];
 
     __device__ __forceinline__ void load(const void* __restrict__ X, const int32_t* rows, int nt,
                                          int64_t I, int64_t g0, int gn) {
@@ -154,21 +155,20 @@ struct InputStage {
                 const int64_t col = (g0 + gl) * kGroup + (qd & 15) * 4;
                 const bool live = t < nt && qd < QUADS && gl < gn;
                 if constexpr (VEC) {
+                    // raw data stay untouched until store(): computing on them
+                    // here would make the wave wait for each load in turn
                     const bool ok = live && col < I;
                     const int64_t c = ok ? col : 0;
-                    float4 r;
+                    ok_[t][j] = ok;
                     if constexpr (BF16) {
                         const uint2 w = *reinterpret_cast<const uint2*>(
                             reinterpret_cast<const uint16_t*>(X) + row * I + c);
-                        r = make_float4(__uint_as_float(w.x << 16),
-                                        __uint_as_float(w.x & 0xFFFF0000u),
-                                        __uint_as_float(w.y << 16),
-                                        __uint_as_float(w.y & 0xFFFF0000u));
+                        raw_[t][j] = make_uint4(w.x, w.y, 0u, 0u);
                     } else {
-                        r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(X) +
-                                                             row * I + c);
+                        const uint4 w = *reinterpret_cast<const uint4*>(
+                            reinterpret_cast<const float*>(X) + row * I + c);
+                        raw_[t][j] = w;
                     }
-                    v[t][j] = ok ? r : make_float4(0.f, 0.f, 0.f, 0.f);
                 } else {
                     float e[4];
 #pragma unroll
@@ -184,7 +184,9 @@ struct InputStage {
                             f = reinterpret_cast<const float*>(X)[row * I + c];
                         e[q] = ok ? f : 0.0f;
                     }
-                    v[t][j] = make_float4(e[0], e[1], e[2], e[3]);
+                    ok_[t][j] = true;
+                    raw_[t][j] = make_uint4(__float_as_uint(e[0]), __float_as_uint(e[1]),
+                                            __float_as_uint(e[2]), __float_as_uint(e[3]));
                 }
             }
         }
@@ -199,7 +201,18 @@ struct InputStage {
                 const int qd = tid + j * NTHR;
                 if (t < nt && qd < QUADS) {
                     float* dst = xs + (t * GC + (qd >> 4)) * kSlot + (qd & 15) * 4;
-                    *reinterpret_cast<float4*>(dst) = v[t][j];
+                    const uint4 w = raw_[t][j];
+                    float4 f;
+                    if constexpr (VEC && BF16)
+                        f = make_float4(__uint_as_float(w.x << 16),
+                                        __uint_as_float(w.x & 0xFFFF0000u),
+                                        __uint_as_float(w.y << 16),
+                                        __uint_as_float(w.y & 0xFFFF0000u));
+                    else
+                        f = make_float4(__uint_as_float(w.x), __uint_as_float(w.y),
+                                        __uint_as_float(w.z), __uint_as_float(w.w));
+                    if (!ok_[t][j]) f = make_float4(0.f, 0.f, 0.f, 0.f);
+                    *reinterpret_cast<float4*>(dst) = f;
                 }
             }
     }
