@@ -282,34 +282,36 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     // the activations, which every block re-reads and mostly hit L2, are
     // fetched one group ahead.  After the MFMAs of group g, group g+1 is
     // dequantized and stored into the other LDS buffer.
+    // The loop body is straight-line (prefetches past the last group re-read
+    // group G-1 and land in a buffer nobody reads): with loads issued under
+    // conditions the compiler cannot tell which are still in flight and waits
+    // for all of them.
     XLoad xl[kXPer];
     WLoad wa[kWPer], wb[kWPer];
+    const int64_t glast = G - 1;
     load_x(0, xl);
     load_w(0, wa);
     store_x(0, xl);
     store_w(0, wa);
-    if (G > 1) load_w(1, wa);
+    load_w(min<int64_t>(1, glast), wa);
     __syncthreads();
-    for (int64_t g = 0; g < G; g += 2) {
-        // step g: registers A hold group g+1's weights
-        if (g + 1 < G) load_x(g + 1, xl);
-        if (g + 2 < G) load_w(g + 2, wb);
+    for (int64_t g = 0;; g += 2) {
+        // step g: registers A hold group g+1's weights, fetch g+2's
+        load_x(min(g + 1, glast), xl);
+        load_w(min(g + 2, glast), wb);
         compute(0);
-        if (g + 1 < G) {
-            store_x(1, xl);
-            store_w(1, wa);
-        }
+        store_x(1, xl);
+        store_w(1, wa);
         __syncthreads();
         if (g + 1 >= G) break;
-        // step g+1: registers B hold group g+2's weights
-        if (g + 2 < G) load_x(g + 2, xl);
-        if (g + 3 < G) load_w(g + 3, wa);
+        // step g+1: registers B hold group g+2's weights, fetch g+3's
+        load_x(min(g + 2, glast), xl);
+        load_w(min(g + 3, glast), wa);
         compute(1);
-        if (g + 2 < G) {
-            store_x(0, xl);
-            store_w(0, wb);
-        }
+        store_x(0, xl);
+        store_w(0, wb);
         __syncthreads();
+        if (g + 2 >= G) break;
     }
 
     // C layout of a 16x16 tile: register r of lane l holds token row
