@@ -16,17 +16,42 @@ namespace {
 constexpr int kLanesPerGroup = 16;  // a quarter wave owns one group
 constexpr int kQuantBlock = 256;    // 16 groups per block
 
-// q = clamp(rne(w / s), -4, 3), 0 when s == 0.  IEEE division (correctly
-// rounded), then round-half-even.
+// q = clamp(rne(fl(w / s)), -4, 3), 0 when s == 0, where fl(w / s) is the
+// correctly rounded f32 quotient.
 __device__ __forceinline__ float code_of(float w, float s) {
     if (s == 0.0f) return 0.0f;
     float q = __builtin_rintf(w / s);
     return fminf(fmaxf(q, -4.0f), 3.0f);
 }
 
+// The same code without a division on the common path.  With r = rcp(s)
+// (v_rcp_f32: within 1 ulp of 1/s) and y = fl(w * r), |y - w/s| and
+// |fl(w/s) - w/s| together stay below 2.4e-7 * |w/s|, i.e. below
+// |y| * 2^-21 for every finite y.  When y is farther than that from every
+// half-integer, fl(w/s) lies strictly on the same side of each half-integer
+// as y, so rint(y) == rint(fl(w/s)).  Otherwise (and for s outside
+// [2^-100, 2^100], or |y| >= 2^22) the correctly rounded division decides.
+__device__ __forceinline__ float code_fast(float w, float s, float r, bool s_ok) {
+    const float y = w * r;
+    const float q = __builtin_rintf(y);
+    const float d = fabsf(y - q);  // exact for |y| < 2^22: distance to the nearest integer
+    const float margin = 0.5f - fabsf(y) * 0x1p-21f;
+    float c = q;
+    if (!(s_ok && fabsf(y) < 0x1p22f && d < margin)) c = __builtin_rintf(w / s);
+    return fminf(fmaxf(c, -4.0f), 3.0f);
+}
+
+// One halving step of the slot errors: lane l (l < m) of a 16-lane row adds
+// the partial sum of lane l + m (row_shl:m moves lane l+m's value to lane l).
+template <int M>
+__device__ __forceinline__ float add_from_lane_plus(float a) {
+    const int v = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x100 + M, 0xF, 0xF, true);
+    return a + __builtin_bit_cast(float, v);
+}
+
 // Lane l of a quarter wave holds slots l, l+16, l+32, l+48 of its group, so
 // the first two halving steps (m = 32, 16) are lane-local and the remaining
-// four (m = 8, 4, 2, 1) read the partner lane l + m.
+// four (m = 8, 4, 2, 1) read the partner lane l + m through DPP.
 __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
     const float* __restrict__ W, int64_t n_groups, int32_t I, int32_t G,
     const float* __restrict__ d, int32_t ncand, GridTable tab,
@@ -35,8 +60,9 @@ __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
     const int l = threadIdx.x & (kLanesPerGroup - 1);
     const int64_t grp = (int64_t)blockIdx.x * (kQuantBlock / kLanesPerGroup) +
                         (threadIdx.x / kLanesPerGroup);
-    // grp is uniform over the 16 lanes of a group, so a whole quarter wave
-    // leaves together and the cross-lane reads below never see a missing lane.
+    // grp is uniform over the 16 lanes of a group (one DPP row), so a whole
+    // row leaves together and the cross-lane reads below see only live lanes
+    // of the same group.
     if (grp >= n_groups) return;
     const int64_t o = grp / G;
     const int32_t g = (int32_t)(grp - o * G);
@@ -60,28 +86,30 @@ __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
 
     float best_e = 0.0f;
     int best_k = 0;
+#pragma unroll 4
     for (int k = 0; k < ncand; ++k) {
         const float s = base * tab.f[k];
+        const float r = __builtin_amdgcn_rcpf(s);
+        const bool s_ok = s >= 0x1p-100f && s <= 0x1p100f;
         float e4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float q = code_of(wv[e], s);
+            const float q = s == 0.0f ? 0.0f : code_fast(wv[e], s, r, s_ok);
             const float t = s * q;
-            const float r = wv[e] - t;
-            const float r2 = r * r;
-            e4[e] = dv[e] * r2;  // padding slots: dv = 0 and r = 0 give +0
+            const float rr = wv[e] - t;
+            const float r2 = rr * rr;
+            e4[e] = dv[e] * r2;  // padding slots: dv = 0 and rr = 0 give +0
         }
         // m = 32: slots j and j+32 are e4[0] + e4[2] and e4[1] + e4[3];
         // m = 16: slot l gets slot l+16.
         const float a32_lo = e4[0] + e4[2];
         const float a32_hi = e4[1] + e4[3];
         float a = a32_lo + a32_hi;
-        // m = 8, 4, 2, 1: slot l (l < m) gets slot l + m, held by lane l + m.
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) {
-            const float partner = __shfl_down(a, m, kLanesPerGroup);
-            a = a + partner;
-        }
+        // m = 8, 4, 2, 1: slot l (l < m) gets slot l + m, held by lane l + m
+        a = add_from_lane_plus<8>(a);
+        a = add_from_lane_plus<4>(a);
+        a = add_from_lane_plus<2>(a);
+        a = add_from_lane_plus<1>(a);
         if (k == 0 || a < best_e) {  // strict: the lowest k wins ties
             best_e = a;
             best_k = k;

@@ -294,3 +294,31 @@ def test_hessian_constant_columns_closed_form():
     X = np.ones((T, I), np.float32)
     d = host(qt.qt_hessian_diag(dev(X)))
     assert np.array_equal(d, np.full(I, float(T), np.float32))
+
+
+def test_search_quotients_on_and_next_to_half_integers():
+    # weights whose quotient w/s falls exactly on a half-integer, or one ulp
+    # beside it, for the scale of a chosen candidate: rounding ties and
+    # near-ties must be decided exactly as the correctly rounded division does
+    rng = workloads.rng_for("generic", 4711)
+    fk = np.linspace(0.5, 1.0, 64).astype(np.float32)
+    rows = []
+    for r in range(48):
+        b = np.float32(rng.uniform(0.01, 0.05))
+        k = int(rng.integers(0, 64))
+        s = np.float32(b * fk[k])
+        w = np.empty(64, np.float32)
+        w[0] = np.float32(4.0) * b  # the group maximum: base = b exactly
+        for j in range(1, 64):
+            h = np.float32(int(rng.integers(-4, 4)) + 0.5)
+            v = np.float32(h * s)
+            step = int(rng.integers(-1, 2))
+            w[j] = np.nextafter(v, np.float32(np.inf) if step > 0 else np.float32(-np.inf)) \
+                if step else v
+        w = np.clip(w, -w[0], w[0])
+        rows.append(w)
+    W = np.stack(rows).astype(np.float32)
+    check_quantize(W, None, 64, 0.5, 1.0)
+    check_quantize(W, None, 0)
+    d = np.exp(workloads.generic_vector(64, seed=17)).astype(np.float32)
+    check_quantize(W, d, 64, 0.5, 1.0)
