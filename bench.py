@@ -30,8 +30,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
-# Vector ALU: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.3 T lane-instructions/s
-VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# Vector ALU: the published fp32 vector peak, 157.3 TFLOP/s, counts an FMA as
+# two operations: 78.65 T lane-operations/s.  (Single-issue non-packed f32
+# instructions measure 64 lanes/clock/CU = 39.3 T at 2.4 GHz; round-to-integer
+# issues beside them, so an op count can exceed that figure.)
+VALU_PEAK_TOPS = 157.3 / 2
 N_COPIES = 64
 
 
@@ -71,11 +74,14 @@ def traffic_for(name, bytes_alg):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_launches(fn, n, torch):
+def time_launches(fn, n, torch, warmup=2):
     """Average time per fn() call over n back-to-back calls, from a pair of
-    events on the current stream (the stream the kernels run on)."""
+    events on the current stream (the stream the kernels run on), after
+    `warmup` untimed calls."""
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(warmup):
+        fn(i)
     torch.cuda.synchronize()
     e0.record(st)
     for i in range(n):

@@ -1,6 +1,7 @@
 // C-ABI layer of libqt.so: host-side argument validation, then one launch
 // (or a short fixed sequence of launches) on the caller's stream.  See qt.h
 // for the contract of every entry point.
+#include <cmath>
 #include "qt.h"
 
 #include <hip/hip_runtime.h>
@@ -130,6 +131,25 @@ qt_status qt_quantize_g64(const float* W, int64_t O, int64_t I, const float* d, 
         for (int k = 0; k < n_grid; ++k) tab.f[k] = (float)((double)lo + (double)k * step);
         tab.f[n_grid - 1] = hi;
     }
+    // In a group with a normal base = absmax/4 and s = fl(base * f), every
+    // |w/s| stays below bound = 4/f * (1 + 2^-20).  The kernel accepts
+    // rint(w * rcp(s)) when that quotient lies closer than margin to its
+    // nearest integer, margin = 0.5 - 2^-21 * bound rounded toward zero: twice
+    // the combined error of the reciprocal quotient and of fl(w/s).  Huge
+    // quotient ranges get margin 0, which sends every lane to the division.
+    for (int k = 0; k < ncand; ++k) {
+        const double bound = 4.0 / (double)tab.f[k] * (1.0 + 0x1p-20);
+        if (!(bound < 0x1p20)) {
+            tab.margin[k] = 0.0f;
+            continue;
+        }
+        const double m = 0.5 - bound * 0x1p-21;
+        float mf = (float)m;
+        if ((double)mf > m) mf = std::nextafter(mf, 0.0f);
+        tab.margin[k] = mf;
+    }
+    tab.fmin = tab.f[0];
+    tab.fmax = tab.f[ncand - 1];
     return launched(qt::launch_quantize_g64(W, O, I, d, ncand, tab, scales, codes, grid_idx,
                                             as_stream(stream)));
 }

@@ -11,8 +11,12 @@ constexpr int kGroupBytes = 24;  // 16 B low plane + 8 B high plane
 constexpr int kMaxGrid = 256;    // largest candidate grid of the scale search
 
 // Candidate factors of the scale search, passed by value as a kernel argument.
+// Candidate scale factors and, per factor, the rounding margin the search
+// kernel uses to accept a reciprocal-based quotient without a division.
 struct GridTable {
     float f[kMaxGrid];
+    float margin[kMaxGrid];
+    float fmin, fmax;
 };
 
 hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,

@@ -24,23 +24,6 @@ __device__ __forceinline__ float code_of(float w, float s) {
     return fminf(fmaxf(q, -4.0f), 3.0f);
 }
 
-// The same code without a division on the common path.  With r = rcp(s)
-// (v_rcp_f32: within 1 ulp of 1/s) and y = fl(w * r), |y - w/s| and
-// |fl(w/s) - w/s| together stay below 2.4e-7 * |w/s|, i.e. below
-// |y| * 2^-21 for every finite y.  When y is farther than that from every
-// half-integer, fl(w/s) lies strictly on the same side of each half-integer
-// as y, so rint(y) == rint(fl(w/s)).  Otherwise (and for s outside
-// [2^-100, 2^100], or |y| >= 2^22) the correctly rounded division decides.
-__device__ __forceinline__ float code_fast(float w, float s, float r, bool s_ok) {
-    const float y = w * r;
-    const float q = __builtin_rintf(y);
-    const float d = fabsf(y - q);  // exact for |y| < 2^22: distance to the nearest integer
-    const float margin = 0.5f - fabsf(y) * 0x1p-21f;
-    float c = q;
-    if (!(s_ok && fabsf(y) < 0x1p22f && d < margin)) c = __builtin_rintf(w / s);
-    return fminf(fmaxf(c, -4.0f), 3.0f);
-}
-
 // One halving step of the slot errors: lane l (l < m) of a 16-lane row adds
 // the partial sum of lane l + m (row_shl:m moves lane l+m's value to lane l).
 template <int M>
@@ -49,9 +32,56 @@ __device__ __forceinline__ float add_from_lane_plus(float a) {
     return a + __builtin_bit_cast(float, v);
 }
 
+// Codes of a candidate without a division on the common path.  With r =
+// rcp(s) (v_rcp_f32: within 1 ulp of 1/s) and y = fl(w * r), y and the
+// correctly rounded fl(w/s) differ by at most 2^-22 * |w/s|.  The host's
+// per-candidate margin leaves twice that bound (for the largest |w/s| the
+// group can hold) between y and every half-integer, so wherever
+// |y - rint(y)| < margin, fl(w/s) rounds to the same integer as y.  Lanes
+// outside the margin, and groups whose scales leave [2^-100, 2^100], take the
+// correctly rounded division instead.
+template <bool WEIGHTED>
+__device__ __forceinline__ float candidate_error(const float (&wv)[4], const float (&dv)[4],
+                                                 float s, float margin, bool s_ok) {
+    const float r = __builtin_amdgcn_rcpf(s);
+    float q[4];
+    bool near = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float y = wv[e] * r;
+        q[e] = __builtin_rintf(y);
+        near |= !(fabsf(y - q[e]) < margin);
+    }
+    if (near || !s_ok) {  // rare: decide with the division
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = s == 0.0f ? 0.0f : __builtin_rintf(wv[e] / s);
+    }
+    float e4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float qc = __builtin_amdgcn_fmed3f(q[e], -4.0f, 3.0f);
+        const float t = s * qc;
+        const float rr = wv[e] - t;
+        const float r2 = rr * rr;
+        e4[e] = WEIGHTED ? dv[e] * r2 : r2;  // padding slots: rr = 0 (and dv = 0)
+    }
+    // m = 32: slots j and j+32 are e4[0] + e4[2] and e4[1] + e4[3];
+    // m = 16: slot l gets slot l+16.
+    const float a32_lo = e4[0] + e4[2];
+    const float a32_hi = e4[1] + e4[3];
+    float a = a32_lo + a32_hi;
+    // m = 8, 4, 2, 1: slot l (l < m) gets slot l + m, held by lane l + m
+    a = add_from_lane_plus<8>(a);
+    a = add_from_lane_plus<4>(a);
+    a = add_from_lane_plus<2>(a);
+    a = add_from_lane_plus<1>(a);
+    return a;
+}
+
 // Lane l of a quarter wave holds slots l, l+16, l+32, l+48 of its group, so
 // the first two halving steps (m = 32, 16) are lane-local and the remaining
 // four (m = 8, 4, 2, 1) read the partner lane l + m through DPP.
+template <bool WEIGHTED>
 __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
     const float* __restrict__ W, int64_t n_groups, int32_t I, int32_t G,
     const float* __restrict__ d, int32_t ncand, GridTable tab,
@@ -77,39 +107,24 @@ __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
         const int j = l + 16 * e;
         const bool ok = j < n;
         wv[e] = ok ? w[j] : 0.0f;
-        dv[e] = ok ? (d ? d[c0 + j] : 1.0f) : 0.0f;
+        dv[e] = ok && WEIGHTED ? d[c0 + j] : 0.0f;
         amax = fmaxf(amax, fabsf(wv[e]));
     }
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kLanesPerGroup));
     const float base = amax * 0.25f;
+    // base normal: then 4 * base == amax exactly and every |w| <= 4 * base
+    // s = fl(base * f) is monotone in f, so the range check of the
+    // smallest and largest factor covers every candidate
+    const bool group_ok = base >= 0x1p-125f && base * tab.fmin >= 0x1p-100f &&
+                          base * tab.fmax <= 0x1p100f;
 
     float best_e = 0.0f;
     int best_k = 0;
-#pragma unroll 4
+#pragma unroll 2
     for (int k = 0; k < ncand; ++k) {
         const float s = base * tab.f[k];
-        const float r = __builtin_amdgcn_rcpf(s);
-        const bool s_ok = s >= 0x1p-100f && s <= 0x1p100f;
-        float e4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float q = s == 0.0f ? 0.0f : code_fast(wv[e], s, r, s_ok);
-            const float t = s * q;
-            const float rr = wv[e] - t;
-            const float r2 = rr * rr;
-            e4[e] = dv[e] * r2;  // padding slots: dv = 0 and rr = 0 give +0
-        }
-        // m = 32: slots j and j+32 are e4[0] + e4[2] and e4[1] + e4[3];
-        // m = 16: slot l gets slot l+16.
-        const float a32_lo = e4[0] + e4[2];
-        const float a32_hi = e4[1] + e4[3];
-        float a = a32_lo + a32_hi;
-        // m = 8, 4, 2, 1: slot l (l < m) gets slot l + m, held by lane l + m
-        a = add_from_lane_plus<8>(a);
-        a = add_from_lane_plus<4>(a);
-        a = add_from_lane_plus<2>(a);
-        a = add_from_lane_plus<1>(a);
+        const float a = candidate_error<WEIGHTED>(wv, dv, s, tab.margin[k], group_ok);
         if (k == 0 || a < best_e) {  // strict: the lowest k wins ties
             best_e = a;
             best_k = k;
@@ -127,6 +142,149 @@ __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
         scales[grp] = s;
         if (grid_idx) grid_idx[grp] = (uint8_t)best_k;
     }
+}
+
+// ---------------------------------------------------------------- search
+// With more than one candidate the work is 64 candidates x 64 slots of
+// arithmetic per group, so one lane owns a whole group: the halving sum is
+// then lane-local (63 adds per candidate instead of a cross-lane reduction),
+// the per-candidate set-up (scale, reciprocal, comparison) is paid once per
+// 64 slots, and a wave's 64 lanes take 64 rows of the same group column, so
+// the importance weights d are the same for the whole wave (scalar registers).
+constexpr int kSearchRows = 64;  // one wave per block, one row per lane
+
+enum QuotientMode { kReciprocal, kDivision };
+
+// Halving sum of the 64 slot errors of one candidate with scale s.  In
+// kReciprocal mode the codes come from y = fl(w * r), r = rcp(s), and *dev
+// receives the largest |y - rint(y)| for the exactness check; kDivision uses
+// the correctly rounded quotient (0 when s == 0).
+template <bool WEIGHTED, int MODE>
+__device__ __forceinline__ float group_error(const float (&w)[kGroup], const float (&dj)[kGroup],
+                                             float s, float r, float* dev) {
+    float a[32];
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        float e2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int jj = j + 32 * h;
+            float q;
+            if (MODE == kReciprocal) {
+                const float y = w[jj] * r;
+                q = __builtin_rintf(y);
+                mx = fmaxf(mx, fabsf(y - q));
+            } else {
+                q = s == 0.0f ? 0.0f : __builtin_rintf(w[jj] / s);
+            }
+            const float qc = __builtin_amdgcn_fmed3f(q, -4.0f, 3.0f);
+            const float t = s * qc;
+            const float rr = w[jj] - t;
+            const float r2 = rr * rr;
+            e2[h] = WEIGHTED ? dj[jj] * r2 : r2;  // padding slots: w = 0, d = 0
+        }
+        a[j] = e2[0] + e2[1];  // m = 32
+    }
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1)
+#pragma unroll
+        for (int j = 0; j < m; ++j) a[j] = a[j] + a[j + m];
+    if (MODE == kReciprocal) *dev = mx;
+    return a[0];
+}
+
+template <bool WEIGHTED>
+__global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
+    const float* __restrict__ W, int64_t O, int32_t I, int32_t G,
+    const float* __restrict__ d, int32_t ncand, GridTable tab, int vec,
+    float* __restrict__ scales, int8_t* __restrict__ codes, uint8_t* __restrict__ grid_idx) {
+    // consecutive blocks walk the group columns of one 64-row slab
+    const int64_t rb = blockIdx.x / G;
+    const int32_t g = (int32_t)(blockIdx.x - rb * G);
+    const int64_t o = rb * kSearchRows + threadIdx.x;
+    if (o >= O) return;  // no cross-lane operations below
+    const int32_t c0 = g * kGroup;
+    const int32_t n = min(kGroup, I - c0);
+    const float* wp = W + o * (int64_t)I + c0;
+
+    float w[kGroup], dj[kGroup];
+    if (vec) {  // I % 4 == 0 and W 16-byte aligned: n is a multiple of 4
+#pragma unroll
+        for (int c = 0; c < kGroup / 4; ++c) {
+            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (4 * c < n) v = reinterpret_cast<const float4*>(wp)[c];
+            w[4 * c + 0] = v.x;
+            w[4 * c + 1] = v.y;
+            w[4 * c + 2] = v.z;
+            w[4 * c + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) w[j] = j < n ? wp[j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) dj[j] = (WEIGHTED && j < n) ? d[c0 + j] : 0.0f;
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) amax = fmaxf(amax, fabsf(w[j]));
+    const float base = amax * 0.25f;
+    // base normal: 4 * base == amax exactly, so every |w| <= 4 * base; and
+    // s = fl(base * f) is monotone in f, so checking the smallest and the
+    // largest factor covers every candidate
+    const bool group_ok = base >= 0x1p-125f && base * tab.fmin >= 0x1p-100f &&
+                          base * tab.fmax <= 0x1p100f;
+
+    float best_e = 0.0f, best_s = 0.0f, best_margin = 0.0f;
+    int best_k = 0;
+    for (int k = 0; k < ncand; ++k) {
+        const float s = base * tab.f[k];
+        const float margin = tab.margin[k];
+        const float r = __builtin_amdgcn_rcpf(s);
+        float dev;
+        float a = group_error<WEIGHTED, kReciprocal>(w, dj, s, r, &dev);
+        if (!(group_ok && dev < margin))  // rare: some quotient near a half-integer
+            a = group_error<WEIGHTED, kDivision>(w, dj, s, r, nullptr);
+        if (k == 0 || a < best_e) {  // strict: the lowest k wins ties
+            best_e = a;
+            best_k = k;
+            best_s = s;
+            best_margin = margin;
+        }
+    }
+
+    // codes of the chosen scale, by the same exactness rule per slot
+    const float s = best_s;
+    const float r = __builtin_amdgcn_rcpf(s);
+    uint32_t packed4[kGroup / 4];
+#pragma unroll
+    for (int c = 0; c < kGroup / 4; ++c) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int j = 4 * c + b;
+            const float y = w[j] * r;
+            float q = __builtin_rintf(y);
+            if (!(group_ok && fabsf(y - q) < best_margin))
+                q = s == 0.0f ? 0.0f : __builtin_rintf(w[j] / s);
+            const int v = (int)__builtin_amdgcn_fmed3f(q, -4.0f, 3.0f);
+            word |= ((uint32_t)v & 0xFFu) << (8 * b);
+        }
+        packed4[c] = word;
+    }
+    int8_t* cp = codes + o * (int64_t)I + c0;
+    if (vec == 2 && n == kGroup) {  // I % 16 == 0, W and codes 16-byte aligned
+#pragma unroll
+        for (int c = 0; c < kGroup / 16; ++c)
+            reinterpret_cast<uint4*>(cp)[c] = make_uint4(packed4[4 * c], packed4[4 * c + 1],
+                                                         packed4[4 * c + 2], packed4[4 * c + 3]);
+    } else {
+        for (int j = 0; j < n; ++j) cp[j] = (int8_t)(packed4[j >> 2] >> (8 * (j & 3)));
+    }
+    const int64_t grp = o * G + g;
+    scales[grp] = s;
+    if (grid_idx) grid_idx[grp] = (uint8_t)best_k;
 }
 
 // One thread per group: 64 codes in, 24 packed bytes out (three 8-byte
@@ -194,12 +352,34 @@ hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float
                                int ncand, const GridTable& tab, float* scales,
                                int8_t* codes, uint8_t* grid_idx, hipStream_t s) {
     const int64_t G = (I + kGroup - 1) / kGroup;
+    if (ncand > 1) {
+        // lane-per-group search: blocks = G * ceil(O / 64)
+        const bool w16 = (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+        const bool c16 = (reinterpret_cast<uintptr_t>(codes) & 15) == 0;
+        const int vec = (w16 && I % 4 == 0) ? ((c16 && I % 16 == 0) ? 2 : 1) : 0;
+        const int64_t blocks = G * ((O + kSearchRows - 1) / kSearchRows);
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        if (d)
+            hipLaunchKernelGGL(search_g64_kernel<true>, dim3((unsigned)blocks), dim3(kSearchRows),
+                               0, s, W, O, (int32_t)I, (int32_t)G, d, ncand, tab, vec, scales,
+                               codes, grid_idx);
+        else
+            hipLaunchKernelGGL(search_g64_kernel<false>, dim3((unsigned)blocks), dim3(kSearchRows),
+                               0, s, W, O, (int32_t)I, (int32_t)G, d, ncand, tab, vec, scales,
+                               codes, grid_idx);
+        return hipGetLastError();
+    }
     const int64_t n_groups = O * G;
     const int64_t per_block = kQuantBlock / kLanesPerGroup;
     const int64_t blocks = (n_groups + per_block - 1) / per_block;
-    hipLaunchKernelGGL(quantize_g64_kernel, dim3((unsigned)blocks), dim3(kQuantBlock), 0, s, W,
-                       n_groups, (int32_t)I, (int32_t)G, d, ncand, tab, scales, codes,
-                       grid_idx);
+    if (d)
+        hipLaunchKernelGGL(quantize_g64_kernel<true>, dim3((unsigned)blocks), dim3(kQuantBlock), 0,
+                           s, W, n_groups, (int32_t)I, (int32_t)G, d, ncand, tab, scales, codes,
+                           grid_idx);
+    else
+        hipLaunchKernelGGL(quantize_g64_kernel<false>, dim3((unsigned)blocks), dim3(kQuantBlock), 0,
+                           s, W, n_groups, (int32_t)I, (int32_t)G, d, ncand, tab, scales, codes,
+                           grid_idx);
     return hipGetLastError();
 }
 
