@@ -10,55 +10,45 @@
 // matmul_i3 kernel ("int3-g64 (fmt=5)" pull request page, "Design", Kernel
 // bullet), with bf16 inputs.
 //
-// Tiling.  A block of 8 waves computes a BM = 256 (tokens) x BN = 144 (output
-// rows) tile and walks the input dimension one 64-wide group at a time; wave w
-// owns tokens [32w, 32w+32) against all 144 rows (2 x 9 MFMA tiles of 16x16).
-// Per group, the block
-//   * dequantizes the group's 144 x 64 codes once into LDS as bf16 (one
-//     16-code quarter per thread: byte-parallel unpack, then v_perm_b32 table
-//     lookups to bf16), with the 144 scales;
-//   * stages the activations 256 x 64 in LDS;
-// double-buffered: the loads for group g+1 are issued before the MFMAs of
-// group g and written to the other buffer after them, one barrier per group.
+// Tiling.  A block of 8 waves (two per SIMD) computes a BM = 256 (tokens) x
+// BN = 144 (output rows) tile and walks the input dimension one 64-wide group
+// at a time; wave w owns tokens [32w, 32w+32) against all 144 rows (2 x 9 MFMA
+// tiles of 16x16, two 32-deep MFMAs per tile and group).
+//   * Weights: the group's 144 x 64 codes are dequantized once per block into
+//     LDS as bf16 in natural k order (one 16-code quarter per task:
+//     byte-parallel unpack, then v_perm_b32 table lookups), with the 144
+//     scales; every wave reads its B operands from there.
+//   * Activations never touch LDS: each lane loads its A-operand slices
+//     (8 consecutive bf16 of one token) straight from global memory into
+//     registers with buffer loads, one group ahead.  Tokens past the batch and
+//     inputs past the row use an offset outside the buffer, for which the
+//     hardware returns zeros.
+// Double-buffered LDS, one barrier per group; packed weights are fetched two
+// groups ahead.
 //
-// k order.  The unpack naturally yields, from a 16-code quarter, the pairs
-// (0,1) (4,5) (8,9) (12,13) and (2,3) (6,7) (10,11) (14,15).  Each 8-element
-// operand slice of an MFMA takes one such set, and the activations are written
-// to LDS in the same order (a 32-byte load of 16 inputs is stored as its even
-// and its odd 4-byte pairs), so every product pairs the right input and code
-// without any shuffle.
-//
-// For B x O shapes that are not multiples of the tile, out-of-range rows and
-// tokens read zeros (or valid addresses whose results are discarded) and are
-// never stored.
+// For B x O shapes that are not multiples of the tile, out-of-range rows read
+// a valid row (their results are discarded) and are never stored.
 #include "qt_internal.h"
 
 namespace qt {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int BM = 256;                 // tokens per block tile
 constexpr int BN = 144;                 // output rows per block tile (9 x 16)
 constexpr int NTN = BN / 16;            // MFMA tiles along the rows
+constexpr int NTM = 2;                  // MFMA tiles along the tokens, per wave
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int ROWB = 64 * 2 + 16;       // LDS bytes per 64-element row (+16 padding)
-constexpr int XS_BYTES = BM * ROWB;     // one activation buffer
+constexpr int ROWB = 64 * 2 + 16;       // LDS bytes per 64-element row (+16: conflict-free reads)
 constexpr int WS_BYTES = BN * ROWB;     // one dequantized-weight buffer
-constexpr int kXTasks = BM * 4;         // 16-input quarters of activations per group
-constexpr int kWTasks = BN * 4;         // 16-code quarters of weights per group
-constexpr int kXPer = kXTasks / kThreads;                   // 2
-constexpr int kWPer = (kWTasks + kThreads - 1) / kThreads;  // 2 (second for 64 threads)
-
-// LDS byte offset, inside a 64-element row, of the 8-element slice that holds
-// set `half` (0: pairs 0,1 4,5 8,9 12,13; 1: the other pairs) of quarter q.
-__device__ __forceinline__ int slice_off(int q, int half) {
-    const int s = q >> 1, h4 = 2 * (q & 1) + half;
-    return (32 * s + 8 * h4) * 2;
-}
+constexpr int kWTasks = BN * 4;         // 16-code quarters of weights per group (576)
+constexpr int kWPer = (kWTasks + kThreads - 1) / kThreads;  // 2 (the second: wave 0 only)
+constexpr uint32_t kOutside = 0x80000000u;  // buffer offset that reads as zero
 
 // bf16 bit patterns of v = u - 4 for four codes u (one per byte), as the pairs
 // [c0 | c1 << 16] and [c2 | c3 << 16].  bf16(v) for v = -4..3 is c080 c040 c000
@@ -71,37 +61,38 @@ __device__ __forceinline__ void to_bf16_pairs(uint32_t W4, uint32_t& d0, uint32_
 }
 
 // One 16-code quarter: low-plane word L (code 4b+i at bits 8b+2i) and its 16
-// high bits h16 (code j at bit j) -> set 0 and set 1 as bf16x8 (4 dwords each).
-__device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t h16, u32x4_t& set0,
-                                                u32x4_t& set1) {
+// high bits h16 (code j at bit j) -> codes 0..7 and 8..15 as bf16x8 (natural
+// order, 4 dwords each).
+__device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t h16, u32x4_t& lo8,
+                                                u32x4_t& hi8) {
     uint32_t sp = (h16 | (h16 << 8)) & 0x00FF00FFu;
     sp = ((sp | (sp << 4)) & 0x0F0F0F0Fu) << 2;  // code 4b+i's high bit at bit 2+i of byte b
     const uint32_t u0 = (L & 0x03030303u) | (sp & 0x04040404u);
     const uint32_t u1 = ((L >> 2) & 0x03030303u) | ((sp >> 1) & 0x04040404u);
     const uint32_t u2 = ((L >> 4) & 0x03030303u) | ((sp >> 2) & 0x04040404u);
     const uint32_t u3 = ((L >> 6) & 0x03030303u) | ((sp >> 3) & 0x04040404u);
-    // natural pairs: bytes [u_i.b, u_{i+1}.b] for b = 0, 1 and b = 2, 3
+    // byte b of u_i is code 4b+i; regroup into code quads in natural order
     const uint32_t a0 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // codes 0 1 4 5
     const uint32_t a1 = __builtin_amdgcn_perm(u1, u0, 0x07030602u);  // codes 8 9 12 13
     const uint32_t b0 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);  // codes 2 3 6 7
     const uint32_t b1 = __builtin_amdgcn_perm(u3, u2, 0x07030602u);  // codes 10 11 14 15
-    uint32_t d[8];
-    to_bf16_pairs(a0, d[0], d[1]);
-    to_bf16_pairs(a1, d[2], d[3]);
-    to_bf16_pairs(b0, d[4], d[5]);
-    to_bf16_pairs(b1, d[6], d[7]);
-    set0 = u32x4_t{d[0], d[1], d[2], d[3]};
-    set1 = u32x4_t{d[4], d[5], d[6], d[7]};
+    uint32_t p01, p45, p89, p1213, p23, p67, p1011, p1415;
+    to_bf16_pairs(a0, p01, p45);
+    to_bf16_pairs(a1, p89, p1213);
+    to_bf16_pairs(b0, p23, p67);
+    to_bf16_pairs(b1, p1011, p1415);
+    lo8 = u32x4_t{p01, p23, p45, p67};
+    hi8 = u32x4_t{p89, p1011, p1213, p1415};
 }
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
-    const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
-    int64_t G, const uint16_t* __restrict__ X, int64_t B, float* __restrict__ Y) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* xs = smem;                           // [2][BM][ROWB]
-    uint8_t* ws = smem + 2 * XS_BYTES;            // [2][BN][ROWB]
-    float* ss = reinterpret_cast<float*>(smem + 2 * XS_BYTES + 2 * WS_BYTES);  // [2][BN]
+    const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int32_t I,
+    int32_t G, const uint16_t* __restrict__ X, int32_t B, float* __restrict__ Y) {
+    __shared__ __attribute__((aligned(16))) uint8_t ws[2][WS_BYTES];
+    __shared__ float ss[2][BN];
+    __shared__ __attribute__((aligned(16))) uint8_t raw[2][kThreads * 8];  // rows 0..BN-1: 24 B each
+    __shared__ float rawsc[2][kThreads];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -109,207 +100,210 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     const int h4 = lane >> 4;  // which 8-element slice of an MFMA operand
     const int l16 = lane & 15;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int32_t m0 = blockIdx.y * BM;
 
-    // ---- loaders (branch-free: out-of-range pieces load a valid address and
-    // are replaced by zeros or discarded).  Per-thread base pointers are set
-    // up once; each group only advances them.
-    const uint16_t* xrow[kXPer];
-    bool xrow_ok[kXPer];
-    int xq16[kXPer];
+    // ---- activations: buffer over this launch's X, offsets per A slice
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(X), (short)0, (int)((int64_t)B * I * 2), 0x00020000);
+    uint32_t xoff[NTM][2];  // byte offset of slice (mt, ks) in group 0, or kOutside
 #pragma unroll
-    for (int i = 0; i < kXPer; ++i) {
-        const int task = tid + kThreads * i;
-        const int64_t t = m0 + (task >> 2);
-        xrow_ok[i] = t < B;
-        xq16[i] = 16 * (task & 3);
-        xrow[i] = X + (xrow_ok[i] ? t : 0) * I + xq16[i];
-    }
-    const uint8_t* wrow[kWPer];
-    const float* srow[kWPer];
-    bool w_ok[kWPer];
+    for (int mt = 0; mt < NTM; ++mt) {
+        const int32_t t = m0 + wave * (16 * NTM) + mt * 16 + l16;
 #pragma unroll
-    for (int i = 0; i < kWPer; ++i) {
-        const int task = tid + kThreads * i;
-        const int64_t n = n0 + (task >> 2);
-        w_ok[i] = task < kWTasks && n < O;
-        const int64_t gi = w_ok[i] ? n * G : 0;
-        wrow[i] = packed + gi * kGroupBytes + 4 * (task & 3);
-        srow[i] = scales + gi;
+        for (int ks = 0; ks < 2; ++ks)
+            xoff[mt][ks] = t < B ? (uint32_t)(((int64_t)t * I + 32 * ks + 8 * h4) * 2) : kOutside;
     }
+    const bool ragged = (I % kGroup) != 0;
 
-    // Raw loaded values stay untouched until the store after the MFMAs:
-    // anything computed from them right after the load would make the wave
-    // wait for the data there.
-    struct XLoad {
-        u32x4_t a, b;
-        bool ok0, ok1;
+    // A slices of group g: 8 registers quads, loaded as raw bf16 bits
+    struct ALoad {
+        u32x4_t v[NTM][2];
     };
-    auto load_x = [&](int64_t g, XLoad (&xl)[kXPer]) {
+    auto load_a = [&](int32_t g, ALoad& a) {
+        uint32_t off[NTM][2];
 #pragma unroll
-        for (int i = 0; i < kXPer; ++i) {
-            const int64_t k = g * kGroup + xq16[i];  // first input of the quarter
-            const uint16_t* src = xrow[i] + g * kGroup;
-            if constexpr (VEC) {
-                xl[i].ok0 = xrow_ok[i] && k < I;
-                xl[i].ok1 = xrow_ok[i] && k + 8 < I;
-                xl[i].a = *reinterpret_cast<const u32x4_t*>(xl[i].ok0 ? src : X);
-                xl[i].b = *reinterpret_cast<const u32x4_t*>(xl[i].ok1 ? src + 8 : X);
-            } else {
-                // unaligned rows: element loads, masked here (rare path)
-                uint32_t w[8];
+        for (int mt = 0; mt < NTM; ++mt)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const bool oa = xrow_ok[i] && k + 2 * e < I;
-                    const bool ob = xrow_ok[i] && k + 2 * e + 1 < I;
-                    const uint32_t va = *(oa ? src + 2 * e : X);
-                    const uint32_t vb = *(ob ? src + 2 * e + 1 : X);
-                    w[e] = (oa ? va : 0u) | ((ob ? vb : 0u) << 16);
-                }
-                xl[i].a = u32x4_t{w[0], w[1], w[2], w[3]};
-                xl[i].b = u32x4_t{w[4], w[5], w[6], w[7]};
-                xl[i].ok0 = xl[i].ok1 = true;
+            for (int ks = 0; ks < 2; ++ks) off[mt][ks] = xoff[mt][ks] + (uint32_t)g * 128u;
+        if (ragged && g == G - 1) {  // slices past the row read zeros
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bool inside = g * kGroup + 32 * ks + 8 * h4 < I;
+#pragma unroll
+                for (int mt = 0; mt < NTM; ++mt)
+                    if (!inside) off[mt][ks] = kOutside;
             }
         }
-    };
-    // store: the 16 inputs of a quarter as their even pairs (set 0) and odd
-    // pairs (set 1); pieces past the row or the batch become zeros
-    auto store_x = [&](int buf, const XLoad (&xl)[kXPer]) {
 #pragma unroll
-        for (int i = 0; i < kXPer; ++i) {
-            const int task = tid + kThreads * i;
-            const int row = task >> 2, q = task & 3;
-            uint8_t* r = xs + buf * XS_BYTES + row * ROWB;
-            const u32x4_t z = {0u, 0u, 0u, 0u};
-            const u32x4_t a = xl[i].ok0 ? xl[i].a : z;
-            const u32x4_t b = xl[i].ok1 ? xl[i].b : z;
-            const u32x4_t s0 = {a.x, a.z, b.x, b.z};
-            const u32x4_t s1 = {a.y, a.w, b.y, b.w};
-            *reinterpret_cast<u32x4_t*>(r + slice_off(q, 0)) = s0;
-            *reinterpret_cast<u32x4_t*>(r + slice_off(q, 1)) = s1;
-        }
+        for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if constexpr (VEC) {
+                    a.v[mt][ks] = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, off[mt][ks], 0, 0));
+                } else {
+                    // rows not 16-byte aligned: element loads, each bounded by the row
+                    uint32_t w[8];
+                    const int32_t k0 = g * kGroup + 32 * ks + 8 * h4;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t oe = (k0 + e < I && off[mt][ks] != kOutside)
+                                                ? off[mt][ks] + 2 * e
+                                                : kOutside;
+                        w[e] = __builtin_amdgcn_raw_buffer_load_b16(xr, oe, 0, 0);
+                    }
+                    a.v[mt][ks] = u32x4_t{w[0] | (w[1] << 16), w[2] | (w[3] << 16),
+                                          w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
+                }
+            }
     };
-    struct WLoad {
-        uint32_t lo, hw;
+
+    // ---- weights.  Each group's 144 packed rows (24 bytes each) arrive with
+    // coalesced 8-byte loads, three consecutive lanes per row, and one f32
+    // scale per row; they are parked in a raw LDS slot and dequantized from
+    // there by quarter tasks (row, q).  Threads past the tile load a valid
+    // row and write to the slot's unused tail, so nothing branches.
+    const int rn = min(tid / 3, BN - 1);
+    const int64_t wr_row = min<int64_t>(n0 + rn, O - 1);  // rows past O: discarded
+    const uint8_t* wptr = packed + wr_row * G * kGroupBytes + 8 * (tid % 3);
+    const int64_t sc_row = min<int64_t>(n0 + min(tid, BN - 1), O - 1);
+    const float* sptr = scales + sc_row * G;
+    struct RawLoad {
+        u32x2_t w;
         float s;
     };
-    auto load_w = [&](int64_t g, WLoad (&wl)[kWPer]) {
-#pragma unroll
-        for (int i = 0; i < kWPer; ++i) {
-            const int q = (tid + kThreads * i) & 3;
-            // rows past O read their block's group 0 (valid); their scale is
-            // replaced by 0 at the store
-            const uint8_t* p = wrow[i] + (w_ok[i] ? g * kGroupBytes : 0);
-            wl[i].lo = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-            wl[i].hw = __builtin_nontemporal_load(
-                reinterpret_cast<const uint32_t*>(p - 4 * q + 16 + 4 * (q >> 1)));
-            wl[i].s = srow[i][w_ok[i] ? g : 0];
-        }
+    auto load_raw = [&](int32_t g, RawLoad& rl) {
+        rl.w = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2_t*>(wptr + (int64_t)g * kGroupBytes));
+        rl.s = sptr[g];
     };
-    auto store_w = [&](int buf, const WLoad (&wl)[kWPer]) {
-#pragma unroll
-        for (int i = 0; i < kWPer; ++i) {
-            const int task = tid + kThreads * i;
-            if (task < kWTasks) {
-                const int n = task >> 2, q = task & 3;
-                u32x4_t s0, s1;
-                dequant_quarter(wl[i].lo, (wl[i].hw >> (16 * (q & 1))) & 0xFFFFu, s0, s1);
-                uint8_t* r = ws + buf * WS_BYTES + n * ROWB;
-                *reinterpret_cast<u32x4_t*>(r + slice_off(q, 0)) = s0;
-                *reinterpret_cast<u32x4_t*>(r + slice_off(q, 1)) = s1;
-                if (q == 0) ss[buf * BN + n] = w_ok[i] ? wl[i].s : 0.0f;
-            }
-        }
+    auto write_raw = [&](int slot, const RawLoad& rl) {
+        reinterpret_cast<u32x2_t*>(raw[slot])[tid] = rl.w;
+        rawsc[slot][tid] = rl.s;
     };
+    // dequantize task i (quarter q of tile row n) from raw slot into LDS
+    // buffer buf; the four lanes of a row all write its scale
+    auto store_task = [&](int buf, int slot, int i) {
+        const int task = tid + kThreads * i;
+        const int n = task >> 2, q = task & 3;
+        const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw[slot]) + 6 * n;
+        const uint32_t lo = rw[q], hw = rw[4 + (q >> 1)];
+        u32x4_t lo8, hi8;
+        dequant_quarter(lo, (hw >> (16 * (q & 1))) & 0xFFFFu, lo8, hi8);
+        uint8_t* r = &ws[buf][n * ROWB + 32 * q];
+        *reinterpret_cast<u32x4_t*>(r) = lo8;
+        *reinterpret_cast<u32x4_t*>(r + 16) = hi8;
+        ss[buf][n] = rawsc[slot][n];
+    };
+    static_assert(kWPer == 2 && kThreads <= kWTasks && kWTasks - kThreads <= 64,
+                  "task split: one task per thread plus a remainder for wave 0");
+    static_assert(3 * BN <= kThreads && BN <= kThreads, "one raw piece and scale per thread");
 
-    f32x4_t acc[2][NTN];
+    f32x4_t acc[NTM][NTN];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < NTM; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NTN; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // MFMAs and scale accumulation of one group from LDS buffer cb.  The B
-    // operands and scale of row tile nt+1 are read from LDS while tile nt is
-    // multiplied, so LDS latency overlaps the matrix cores.
-    auto compute = [&](int cb) {
-        const uint8_t* xb = xs + cb * XS_BYTES + (wave * 32 + l16) * ROWB + 16 * h4;
-        const uint8_t* wb = ws + cb * WS_BYTES + l16 * ROWB + 16 * h4;
-        const float* sb = ss + cb * BN + l16;
-        bf16x8_t aop[2][2];
+    // One group: MFMAs and scale accumulation from A registers and LDS
+    // buffer cb, then the dequantization of the next group's first task into
+    // buffer 1-cb.  Row tile nt's B operands are read from LDS two tiles
+    // ahead; the scale FMAs of tile nt-1 follow the MFMAs of tile nt, and the
+    // scheduling groups at the end ask for three other vector ops after
+    // every MFMA, so the FMAs and the dequantization fill the matrix core's
+    // shadow.
+    auto step = [&](int cb, const ALoad& a) {
+        const uint8_t* wb = &ws[cb][l16 * ROWB + 16 * h4];
+        const float* sb = &ss[cb][l16];
+        bf16x8_t aop[NTM][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < NTM; ++mt)
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                aop[mt][s] = __builtin_bit_cast(
-                    bf16x8_t,
-                    *reinterpret_cast<const u32x4_t*>(xb + mt * 16 * ROWB + 64 * s));
-        bf16x8_t bcur0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(wb));
-        bf16x8_t bcur1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(wb + 64));
-        float scur = sb[0];
+            for (int ks = 0; ks < 2; ++ks) aop[mt][ks] = __builtin_bit_cast(bf16x8_t, a.v[mt][ks]);
+        auto read_b = [&](int nt, bf16x8_t (&bb)[2]) {
+            const uint8_t* wr = wb + nt * 16 * ROWB;
+            bb[0] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(wr));
+            bb[1] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(wr + 64));
+        };
+        float sc[NTN];
+#pragma unroll
+        for (int nt = 0; nt < NTN; ++nt) sc[nt] = sb[nt * 16];
+        bf16x8_t bring[3][2];
+        read_b(0, bring[0]);
+        read_b(1, bring[1]);
+        f32x4_t part[2][NTM];
 #pragma unroll
         for (int nt = 0; nt < NTN; ++nt) {
-            bf16x8_t bnext0 = bcur0, bnext1 = bcur1;
-            float snext = scur;
-            if (nt + 1 < NTN) {
-                const uint8_t* wr = wb + (nt + 1) * 16 * ROWB;
-                bnext0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(wr));
-                bnext1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(wr + 64));
-                snext = sb[(nt + 1) * 16];
+            if (nt + 2 < NTN) read_b(nt + 2, bring[(nt + 2) % 3]);
+            const bf16x8_t(&bb)[2] = bring[nt % 3];
+#pragma unroll
+            for (int mt = 0; mt < NTM; ++mt)
+                part[nt & 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    aop[mt][0], bb[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < NTM; ++mt)
+                part[nt & 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    aop[mt][1], bb[1], part[nt & 1][mt], 0, 0, 0);
+            if (nt > 0) {
+#pragma unroll
+                for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[mt][nt - 1][r] = __builtin_fmaf(sc[nt - 1], part[(nt - 1) & 1][mt][r],
+                                                            acc[mt][nt - 1][r]);
             }
-            f32x4_t part[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    aop[mt][0], bcur0, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mt][1], bcur1, part[mt], 0,
-                                                                   0, 0);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[mt][nt][r] = __builtin_fmaf(scur, part[mt][r], acc[mt][nt][r]);
-            bcur0 = bnext0;
-            bcur1 = bnext1;
-            scur = snext;
         }
+#pragma unroll
+        for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[mt][NTN - 1][r] = __builtin_fmaf(sc[NTN - 1], part[(NTN - 1) & 1][mt][r],
+                                                     acc[mt][NTN - 1][r]);
+        store_task(1 - cb, 1 - cb, 0);
+        // 0x8: MFMA, 0x2: other vector ALU
+#pragma unroll
+        for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+            for (int m = 0; m < 2 * NTM; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x2, 3, 0);
+            }
     };
 
-    // Software pipeline.  The packed weights stream from HBM and are fetched
-    // two groups ahead (group g+1 waits in registers while g+2 is in flight);
-    // the activations, which every block re-reads and mostly hit L2, are
-    // fetched one group ahead.  After the MFMAs of group g, group g+1 is
-    // dequantized and stored into the other LDS buffer.
+    // Software pipeline.  Step k: the A slices of group k are in registers
+    // and its weights in LDS buffer k&1; the raw weights of group k+1 wait in
+    // raw slot (k+1)&1 and those of k+2 in registers.  It issues the loads of
+    // A(k+1) and of the raw weights of k+3, multiplies group k, dequantizes
+    // k+1 into the other buffer and parks the raw weights of k+2 in slot k&1.
     // The loop body is straight-line (prefetches past the last group re-read
-    // group G-1 and land in a buffer nobody reads): with loads issued under
-    // conditions the compiler cannot tell which are still in flight and waits
-    // for all of them.
-    XLoad xl[kXPer];
-    WLoad wa[kWPer], wb[kWPer];
-    const int64_t glast = G - 1;
-    load_x(0, xl);
-    load_w(0, wa);
-    store_x(0, xl);
-    store_w(0, wa);
-    load_w(min<int64_t>(1, glast), wa);
+    // group G-1 and land where nobody reads): loads issued under conditions
+    // keep the compiler from telling which are still in flight.
+    ALoad a0, a1;
+    RawLoad ra, rb;
+    const int32_t glast = G - 1;
+    load_a(0, a0);
+    load_raw(0, ra);
+    load_raw(min(1, glast), rb);
+    write_raw(0, ra);
+    write_raw(1, rb);
     __syncthreads();
-    for (int64_t g = 0;; g += 2) {
-        // step g: registers A hold group g+1's weights, fetch g+2's
-        load_x(min(g + 1, glast), xl);
-        load_w(min(g + 2, glast), wb);
-        compute(0);
-        store_x(1, xl);
-        store_w(1, wa);
+    store_task(0, 0, 0);
+    if (wave == 0) store_task(0, 0, 1);
+    load_raw(min(2, glast), ra);
+    __syncthreads();
+    for (int32_t g = 0;; g += 2) {
+        load_a(min(g + 1, glast), a1);
+        load_raw(min(g + 3, glast), rb);
+        step(0, a0);
+        if (wave == 0) store_task(1, 1, 1);
+        write_raw(0, ra);
         __syncthreads();
         if (g + 1 >= G) break;
-        // step g+1: registers B hold group g+2's weights, fetch g+3's
-        load_x(min(g + 2, glast), xl);
-        load_w(min(g + 3, glast), wa);
-        compute(1);
-        store_x(0, xl);
-        store_w(0, wb);
+        load_a(min(g + 2, glast), a0);
+        load_raw(min(g + 4, glast), ra);
+        step(1, a1);
+        if (wave == 0) store_task(0, 0, 1);
+        write_raw(1, rb);
         __syncthreads();
         if (g + 2 >= G) break;
     }
@@ -321,16 +315,14 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
         const int64_t o = n0 + nt * 16 + l16;
         if (o >= O) continue;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < NTM; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t t = m0 + wave * 32 + mt * 16 + 4 * h4 + r;
-                if (t < B) Y[t * O + o] = acc[mt][nt][r];
+                const int32_t t = m0 + wave * (16 * NTM) + mt * 16 + 4 * h4 + r;
+                if (t < B) Y[(int64_t)t * O + o] = acc[mt][nt][r];
             }
     }
 }
-
-constexpr size_t kSmem = 2 * XS_BYTES + 2 * WS_BYTES + 2 * BN * sizeof(float);
 
 }  // namespace
 
@@ -338,23 +330,26 @@ hipError_t launch_gemm_mfma(const uint8_t* packed, const float* scales, int64_t 
                             int64_t I, const uint16_t* X, int64_t B, float* Y,
                             hipStream_t s) {
     const int64_t G = (I + kGroup - 1) / kGroup;
-    const dim3 grid((unsigned)((O + BN - 1) / BN), (unsigned)((B + BM - 1) / BM));
+    // The activation buffer of one launch spans at most 2^31 - 1 bytes (its
+    // out-of-range offset is 2^31), so long batches go in token slabs.
+    const int64_t slab = ((0x7FFFFFFFLL / (I * 2)) / BM) * BM;
+    if (slab < BM || G > 0x7FFFFFFF) return hipErrorInvalidValue;
     const bool vec = (I % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-    hipError_t e;
-    if (vec) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_i3_mfma_kernel<true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);
+    for (int64_t t0 = 0; t0 < B; t0 += slab) {
+        const int64_t bt = min(slab, B - t0);
+        const dim3 grid((unsigned)((O + BN - 1) / BN), (unsigned)((bt + BM - 1) / BM));
+        if (vec)
+            hipLaunchKernelGGL((gemm_i3_mfma_kernel<true>), grid, dim3(kThreads), 0, s, packed,
+                               scales, O, (int32_t)I, (int32_t)G, X + t0 * I, (int32_t)bt,
+                               Y + t0 * O);
+        else
+            hipLaunchKernelGGL((gemm_i3_mfma_kernel<false>), grid, dim3(kThreads), 0, s, packed,
+                               scales, O, (int32_t)I, (int32_t)G, X + t0 * I, (int32_t)bt,
+                               Y + t0 * O);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((gemm_i3_mfma_kernel<true>), grid, dim3(kThreads), kSmem, s, packed,
-                           scales, O, I, G, X, B, Y);
-    } else {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_i3_mfma_kernel<false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((gemm_i3_mfma_kernel<false>), grid, dim3(kThreads), kSmem, s, packed,
-                           scales, O, I, G, X, B, Y);
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace qt
