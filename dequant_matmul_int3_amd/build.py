@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 SO = os.path.join(PKG, "libqt.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "gemm.hip", "hessian.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "grouped.hip", "gemm.hip", "hessian.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -331,49 +331,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
                                         (int64_t)blockIdx.x * RB, lds);
 }
 
-// grid: (row blocks, experts).  Pairs of expert e: [off[e], off[e+1]),
-// processed in tiles of up to 4 pairs; each tile runs the variant built for
-// exactly its number of pairs, so no load or multiply is spent on empty slots.
-template <int LPR, int WAVES, bool VEC>
-__global__ __launch_bounds__(WAVES * 64) void gemv_grouped_kernel(
-    const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
-    int64_t G, const float* __restrict__ X, int64_t n_x_rows,
-    const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t E, int32_t P,
-    float* __restrict__ Y) {
-    constexpr int TT = 4;  // pairs per tile
-    extern __shared__ __attribute__((aligned(16))) float lds[];
-    __shared__ int32_t rows[TT];
-    __shared__ int32_t outs[TT];
-    const int e = blockIdx.y;
-    const int32_t p0 = max(0, min(off[e], P));
-    const int32_t p1 = max(p0, min(off[e + 1], P));
-    if (p1 == p0) return;  // uniform over the block
-    constexpr int RB = WAVES * 64 / LPR;
-    const int64_t r0 = (int64_t)blockIdx.x * RB;
-    const uint8_t* pk = packed + (int64_t)e * O * G * kGroupBytes;
-    const float* sc = scales + (int64_t)e * O * G;
-    for (int32_t pb = p0; pb < p1; pb += TT) {
-        const int n = min(TT, p1 - pb);
-        __syncthreads();  // the previous tile is done with rows, outs and LDS
-        if (threadIdx.x < n) {
-            const int32_t p = pb + threadIdx.x;
-            const int32_t xr = pair_row ? pair_row[p] : p;
-            // out-of-range rows read row 0 and are not written; the host
-            // documents the valid range, this only keeps accesses in bounds
-            const bool ok = xr >= 0 && xr < n_x_rows;
-            outs[threadIdx.x] = ok ? p : -1;
-            rows[threadIdx.x] = ok ? xr : 0;
-        }
-        __syncthreads();
-        switch (n) {
-            case 1: gemv_rows<LPR, WAVES, 1, false, VEC>(pk, sc, O, I, G, X, rows, outs, 1, Y, r0, lds); break;
-            case 2: gemv_rows<LPR, WAVES, 2, false, VEC>(pk, sc, O, I, G, X, rows, outs, 2, Y, r0, lds); break;
-            case 3: gemv_rows<LPR, WAVES, 3, false, VEC>(pk, sc, O, I, G, X, rows, outs, 3, Y, r0, lds); break;
-            default: gemv_rows<LPR, WAVES, 4, false, VEC>(pk, sc, O, I, G, X, rows, outs, 4, Y, r0, lds); break;
-        }
-    }
-}
-
 }  // namespace
 
 // Decode and small batches.  LPR/WAVES chosen so that O/RB blocks cover the
@@ -415,26 +372,6 @@ hipError_t launch_gemv_batch(const uint8_t* packed, const float* scales, int64_t
                    : batch_dispatch<true, false>(packed, scales, O, I, X, ntok, Y, s);
     return vec ? batch_dispatch<false, true>(packed, scales, O, I, X, ntok, Y, s)
                : batch_dispatch<false, false>(packed, scales, O, I, X, ntok, Y, s);
-}
-
-hipError_t launch_gemv_grouped(const uint8_t* packed, const float* scales, int32_t E,
-                               int64_t O, int64_t I, const float* X, int64_t n_x_rows,
-                               const int32_t* pair_row, const int32_t* expert_offsets,
-                               int32_t P, float* Y, hipStream_t s) {
-    constexpr int LPR = 16, WAVES = 8;
-    constexpr int RB = WAVES * 64 / LPR;
-    const int64_t G = (I + kGroup - 1) / kGroup;
-    const int64_t rb = (O + RB - 1) / RB;
-    const bool vec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-    if (vec)
-        hipLaunchKernelGGL((gemv_grouped_kernel<LPR, WAVES, true>), dim3((unsigned)rb, (unsigned)E),
-                           dim3(WAVES * 64), lds_bytes<4>(), s, packed, scales, O, I, G, X,
-                           n_x_rows, pair_row, expert_offsets, E, P, Y);
-    else
-        hipLaunchKernelGGL((gemv_grouped_kernel<LPR, WAVES, false>), dim3((unsigned)rb, (unsigned)E),
-                           dim3(WAVES * 64), lds_bytes<4>(), s, packed, scales, O, I, G, X,
-                           n_x_rows, pair_row, expert_offsets, E, P, Y);
-    return hipGetLastError();
 }
 
 }  // namespace qt
