@@ -28,12 +28,16 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
+# The grouped matrix-core kernel scales every MFMA result on the vector ALUs:
+# ask the backend to keep MFMA results in VGPRs rather than AGPRs (saves one
+# copy per result).
+EXTRA = {"grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, src + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

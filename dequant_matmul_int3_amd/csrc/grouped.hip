@@ -188,7 +188,8 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
         for (int q = 0; q < 4; ++q) c.s[q] = ssrc[min(c0 + sg + q, G - 1)];
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            const int64_t xr = trow[t < nt ? t : 0];
+            if (t >= nt) break;  // uniform
+            const int64_t xr = trow[t];
             const int32_t k0 = c0 * kGroup + 4 * tid;  // this thread's 4 inputs
             const float* src = X + xr * I;
             if constexpr (XV) {
@@ -214,15 +215,17 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
         const int32_t k0 = c0 * kGroup + 4 * tid;
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            float x[4];
+            if (t < nt) {  // uniform; columns of absent tokens stay zero
+                float x[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) x[q] = (t < nt && k0 + q < I) ? c.x[t][q] : 0.0f;
-            uint32_t w[3][2];
-            split3(x, w);
+                for (int q = 0; q < 4; ++q) x[q] = k0 + q < I ? c.x[t][q] : 0.0f;
+                uint32_t w[3][2];
+                split3(x, w);
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
-                *reinterpret_cast<u32x2_t*>(pl + (3 * t + p) * kPRow + 8 * tid) =
-                    u32x2_t{w[p][0], w[p][1]};
+                for (int p = 0; p < 3; ++p)
+                    *reinterpret_cast<u32x2_t*>(pl + (3 * t + p) * kPRow + 8 * tid) =
+                        u32x2_t{w[p][0], w[p][1]};
+            }
         }
     };
 
@@ -240,6 +243,11 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
         }
         __syncthreads();
 
+        // columns of tokens past nt read zeros for the whole pass
+        for (int i = tid; i < (3 * (kTok - nt)) * (kCG * kGroup / 2); i += kThreads) {
+            const int col = 3 * nt + i / (kCG * kGroup / 2), w = i % (kCG * kGroup / 2);
+            reinterpret_cast<uint32_t*>(pl + col * kPRow)[w] = 0u;
+        }
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         Chunk cur;
         load_chunk(0, nt, cur);

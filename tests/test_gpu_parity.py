@@ -229,7 +229,8 @@ def _grouped_case(E, O, I, T, topk, seed):
 
 
 @pytest.mark.parametrize("E,O,I,T,topk", [(4, 40, 300, 6, 2), (16, 64, 1000, 32, 8),
-                                          (3, 100, 64, 40, 3), (8, 33, 7200, 5, 1)])
+                                          (3, 100, 64, 40, 3), (8, 33, 7200, 5, 1),
+                                          (5, 130, 450, 12, 3), (3, 70, 130, 9, 2)])
 def test_grouped_matvec(E, O, I, T, topk):
     tok, exp, offs, so, po, X = _grouped_case(E, O, I, T, topk, seed=E + T)
     P = tok.size
