@@ -1,6 +1,6 @@
 """Benchmark of the int3-g64 hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|gemv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|gemv|LEG[,LEG...]]
 
 Headline (one JSON line on stdout): the decode GEMV, W[2048x7168] int3-g64
 with f32 scales times x[7168] f32, batch 1.  A step is one dequantize-multiply
@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--legs", default="all", choices=["all", "gemv"])
+    ap.add_argument("--legs", default="all",
+                    help="all, gemv (headline only) or a comma list of: " + ",".join(LEG_NAMES))
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib", action="store_true",
                     help="also run a 256 MiB device copy (reference for HBM traffic counters)")
@@ -187,8 +188,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.legs == "all":
-        legs.update(run_legs(torch, qt, workloads, dev))
+    if args.legs != "gemv":
+        which = set(LEG_NAMES) if args.legs == "all" else set(args.legs.split(","))
+        unknown = which - set(LEG_NAMES)
+        if unknown:
+            raise SystemExit(f"unknown legs {sorted(unknown)}; choose from {LEG_NAMES}")
+        legs.update(run_legs(torch, qt, workloads, dev, which))
 
     cpu = cpu_baseline(W, x, args.cpu_seconds, bytes_step)
 
@@ -219,8 +224,26 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def run_legs(torch, qt, workloads, dev):
+LEG_NAMES = ["quant", "search", "moe", "prefill"]
+
+
+def run_legs(torch, qt, workloads, dev, which):
+    """Time the selected legs: quant (RTN quantize + pack at the decode shape),
+    search (Hessian diagonal + weighted scale search), moe (grouped GEMV),
+    prefill (bf16 MFMA GEMM)."""
     legs = {}
+    if "quant" in which:
+        quant_leg(torch, qt, workloads, dev, legs)
+    if "search" in which:
+        search_leg(torch, qt, workloads, dev, legs)
+    if "moe" in which:
+        moe_leg(torch, qt, workloads, dev, legs)
+    if "prefill" in which:
+        prefill_leg(torch, qt, workloads, dev, legs)
+    return legs
+
+
+def quant_leg(torch, qt, workloads, dev, legs):
     # -------------------------------------------------------- quantize + pack (decode, RTN)
     W, _ = workloads.decode()
     O, I = W.shape
@@ -242,6 +265,8 @@ def run_legs(torch, qt, workloads, dev):
     log(f"leg quantize/pack decode: {legs['quantize_rtn_decode']} {legs['pack_decode']}")
     del Wd, s, c, p
 
+
+def search_leg(torch, qt, workloads, dev, legs):
     # -------------------------------------------------------- Hessian diagonal + search
     log("leg search: generating X[8192x17408], W[5120x17408]")
     X = workloads.search_x()
@@ -279,6 +304,8 @@ def run_legs(torch, qt, workloads, dev):
     log(f"leg search: {legs['quantize_search']}")
     del Wd, s, c, k, d
 
+
+def moe_leg(torch, qt, workloads, dev, legs):
     # -------------------------------------------------------- grouped MoE GEMV
     E = workloads.MOE_EXPERTS
     log("leg moe: generating and quantizing 128 experts x (up, down)")
@@ -322,6 +349,8 @@ def run_legs(torch, qt, workloads, dev):
     log(f"leg moe: {legs['moe_grouped']}")
     del pu, su, pdn, sdn, h, yo
 
+
+def prefill_leg(torch, qt, workloads, dev, legs):
     # -------------------------------------------------------- prefill GEMM (bf16 MFMA)
     log("leg prefill: generating and quantizing W[18432x7168]")
     O, I = workloads.PREFILL_SHAPE
@@ -345,7 +374,6 @@ def run_legs(torch, qt, workloads, dev):
     legs["prefill_gemm"] = {"ms": round(ms, 4), "TFLOP_s": round(tf, 1), "bound": "mfma",
                             "peak_TFLOP_s": BF16_PEAK_TFLOPS, "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
     log(f"leg prefill: {legs['prefill_gemm']}")
-    return legs
 
 
 def cpu_baseline(W, x, seconds, bytes_step):

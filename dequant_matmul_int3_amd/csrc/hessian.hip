@@ -6,8 +6,8 @@
 // Streaming column reduction, bound by HBM reads of X.  Stage 1: the grid is
 // (column tiles) x (token slabs); a thread owns VEC adjacent columns (one
 // 16-byte load per token row) and sums the squares of its slab's rows in f32.
-// Stage 2 adds the slab partials in slab order.  No atomics: the result is
-// independent of scheduling.
+// Stage 2 adds the slab partials along a fixed tree.  No atomics: the result
+// is independent of scheduling.
 #include <algorithm>
 
 #include "qt_internal.h"
@@ -92,14 +92,30 @@ __global__ __launch_bounds__(kHesThreads) void hessian_partial_kernel(
     }
 }
 
+// Stage 2: a block owns kCombCols columns; thread (column c, part q) adds
+// the slab partials q, q + kCombParts, ... in slab order, then part 0 adds the
+// kCombParts sums in part order.  The summation tree is fixed, so the result
+// does not depend on scheduling.
+constexpr int kCombCols = 32;
+constexpr int kCombParts = kHesThreads / kCombCols;  // 8
+
 __global__ __launch_bounds__(kHesThreads) void hessian_combine_kernel(
     const float* __restrict__ part, int64_t I, int slabs, float* __restrict__ d,
     int accumulate) {
-    const int64_t j = (int64_t)blockIdx.x * kHesThreads + threadIdx.x;
-    if (j >= I) return;
+    __shared__ float sums[kCombParts][kCombCols];
+    const int c = threadIdx.x % kCombCols, q = threadIdx.x / kCombCols;
+    const int64_t j = (int64_t)blockIdx.x * kCombCols + c;
+    const int64_t jc = j < I ? j : I - 1;  // columns past I: read a valid one, unused
     float total = 0.0f;
-    for (int s = 0; s < slabs; ++s) total += part[(int64_t)s * I + j];
-    d[j] = accumulate ? d[j] + total : total;
+    for (int s = q; s < slabs; s += kCombParts) total += part[(int64_t)s * I + jc];
+    sums[q][c] = total;
+    __syncthreads();
+    if (q == 0 && j < I) {
+        float t = sums[0][c];
+#pragma unroll
+        for (int k = 1; k < kCombParts; ++k) t += sums[k][c];
+        d[j] = accumulate ? d[j] + t : t;
+    }
 }
 
 template <int VEC, bool BF16>
@@ -113,7 +129,7 @@ hipError_t run(const void* X, int64_t T, int64_t I, float* d, int accumulate, fl
                        T, I, rows, direct ? d : ws, direct, accumulate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
-    hipLaunchKernelGGL(hessian_combine_kernel, dim3((unsigned)((I + kHesThreads - 1) / kHesThreads)),
+    hipLaunchKernelGGL(hessian_combine_kernel, dim3((unsigned)((I + kCombCols - 1) / kCombCols)),
                        dim3(kHesThreads), 0, st, ws, I, slabs, d, accumulate);
     return hipGetLastError();
 }
