@@ -159,7 +159,11 @@ qt_status qt_matmul_i3(const uint8_t* packed, const float* scales, int64_t O,
  *   expert_offsets[E] = P.
  *   X       input rows; row of pair p is X[pair_row[p]] when pair_row is
  *           not NULL (int32 [P], values in [0, n_x_rows)), else X[p].
- *   Y       [P x O] f32 out: Y[p] = W_{e(p)} X[row(p)], f32 as qt_matvec_i3.
+ *   Y       [P x O] f32 out: Y[p] = W_{e(p)} X[row(p)], tolerance 1e-5 as
+ *           qt_matvec_i3.  The products are formed on the matrix cores from
+ *           the exact codes and an exact split of each f32 input into three
+ *           bf16 pieces, and every group is summed in f32 and scaled by its
+ *           f32 scale.
  * Everything runs in one launch; experts with no pair cost no weight reads.
  */
 qt_status qt_matvec_i3_grouped(const uint8_t* packed, const float* scales,
