@@ -302,6 +302,17 @@ def search_leg(torch, qt, workloads, dev, legs):
                                "frac": round(ops / (ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
                                "op_count": "9 per slot per candidate (division as one)"}
     log(f"leg search: {legs['quantize_search']}")
+    # two-stage signed search: 2 x 64 signed candidates, then 32 refinement points
+    qt.qt_quantize_g64_signed(Wd, d, 64, 32, 0.5, 1.0, scales=s, codes=c)
+    ms = time_launches(lambda i: qt.qt_quantize_g64_signed(Wd, d, 64, 32, 0.5, 1.0, scales=s,
+                                                          codes=c), 3, torch)
+    ops = ngroups * (2 * 64 + 32) * 64 * 9
+    legs["quantize_search_signed"] = {"ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)),
+                                      "bound": "alu", "achieved_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
+                                      "peak_Tops": round(VALU_PEAK_TOPS, 2),
+                                      "frac": round(ops / (ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
+                                      "candidates": "2 x 64 + 32 per group"}
+    log(f"leg search signed: {legs['quantize_search_signed']}")
     del Wd, s, c, k, d
 
 

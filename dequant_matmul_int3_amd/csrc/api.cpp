@@ -100,28 +100,12 @@ qt_status qt_hessian_diag(const void* X, qt_dtype xt, int64_t T, int64_t I, floa
                                             static_cast<float*>(workspace), as_stream(stream)));
 }
 
-qt_status qt_quantize_g64(const float* W, int64_t O, int64_t I, const float* d, int32_t n_grid,
-                          float lo, float hi, float* scales, int8_t* codes, uint8_t* grid_idx,
-                          void* stream) {
-    if (!W || !scales || !codes) return QT_ERR_NULL;
-    qt_status st = shape_ok(O, I);
-    if (st != QT_OK) return st;
-    if (n_grid != 0 && (n_grid < 2 || n_grid > qt::kMaxGrid)) return QT_ERR_ARG;
-    if (n_grid != 0 && !(lo > 0.0f && lo <= hi && hi < __builtin_inff())) return QT_ERR_ARG;
-    if (!aligned(W, 4) || !aligned(scales, 4) || (d && !aligned(d, 4))) return QT_ERR_ALIGN;
-    const int64_t G = qt_groups(I);
-    const int64_t wb = O * I * 4, sb = O * G * 4, cb = O * I, gb = O * G;
-    if (overlap(scales, sb, W, wb) || overlap(codes, cb, W, wb) ||
-        overlap(scales, sb, codes, cb) || (d && (overlap(scales, sb, d, I * 4) ||
-                                                 overlap(codes, cb, d, I * 4))) ||
-        (grid_idx && (overlap(grid_idx, gb, W, wb) || overlap(grid_idx, gb, scales, sb) ||
-                      overlap(grid_idx, gb, codes, cb) || (d && overlap(grid_idx, gb, d, I * 4)))))
-        return QT_ERR_ALIAS;
+namespace {
 
-    // Candidate factors: n_grid equally spaced points of [lo, hi], formed in
-    // double and rounded once; the last one is hi itself.  n_grid == 0 is the
-    // single plain absmax/4 scale (factor 1).
-    qt::GridTable tab{};
+// Candidate factors: n_grid equally spaced points of [lo, hi], formed in
+// double and rounded once; the last one is hi itself.  n_grid == 0 is the
+// single plain absmax/4 scale (factor 1).
+int make_grid(int32_t n_grid, float lo, float hi, qt::GridTable& tab) {
     int ncand = 1;
     if (n_grid == 0) {
         tab.f[0] = 1.0f;
@@ -150,8 +134,55 @@ qt_status qt_quantize_g64(const float* W, int64_t O, int64_t I, const float* d, 
     }
     tab.fmin = tab.f[0];
     tab.fmax = tab.f[ncand - 1];
-    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, tab, scales, codes, grid_idx,
-                                            as_stream(stream)));
+    return ncand;
+}
+
+qt_status quantize_args_ok(const float* W, int64_t O, int64_t I, const float* d,
+                           const float* scales, const int8_t* codes, const uint8_t* grid_idx) {
+    if (!W || !scales || !codes) return QT_ERR_NULL;
+    qt_status st = shape_ok(O, I);
+    if (st != QT_OK) return st;
+    if (!aligned(W, 4) || !aligned(scales, 4) || (d && !aligned(d, 4))) return QT_ERR_ALIGN;
+    const int64_t G = qt_groups(I);
+    const int64_t wb = O * I * 4, sb = O * G * 4, cb = O * I, gb = O * G;
+    if (overlap(scales, sb, W, wb) || overlap(codes, cb, W, wb) ||
+        overlap(scales, sb, codes, cb) || (d && (overlap(scales, sb, d, I * 4) ||
+                                                 overlap(codes, cb, d, I * 4))) ||
+        (grid_idx && (overlap(grid_idx, gb, W, wb) || overlap(grid_idx, gb, scales, sb) ||
+                      overlap(grid_idx, gb, codes, cb) || (d && overlap(grid_idx, gb, d, I * 4)))))
+        return QT_ERR_ALIAS;
+    return QT_OK;
+}
+
+bool grid_ok(float lo, float hi) { return lo > 0.0f && lo <= hi && hi < __builtin_inff(); }
+
+}  // namespace
+
+qt_status qt_quantize_g64(const float* W, int64_t O, int64_t I, const float* d, int32_t n_grid,
+                          float lo, float hi, float* scales, int8_t* codes, uint8_t* grid_idx,
+                          void* stream) {
+    qt_status st = quantize_args_ok(W, O, I, d, scales, codes, grid_idx);
+    if (st != QT_OK) return st;
+    if (n_grid != 0 && (n_grid < 2 || n_grid > qt::kMaxGrid)) return QT_ERR_ARG;
+    if (n_grid != 0 && !grid_ok(lo, hi)) return QT_ERR_ARG;
+    qt::GridTable tab{};
+    const int ncand = make_grid(n_grid, lo, hi, tab);
+    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, 0, false, tab, scales, codes,
+                                            grid_idx, as_stream(stream)));
+}
+
+qt_status qt_quantize_g64_signed(const float* W, int64_t O, int64_t I, const float* d,
+                                 int32_t n1, int32_t n2, float lo, float hi, float* scales,
+                                 int8_t* codes, void* stream) {
+    qt_status st = quantize_args_ok(W, O, I, d, scales, codes, nullptr);
+    if (st != QT_OK) return st;
+    if (n1 < 2 || n1 > qt::kMaxGrid) return QT_ERR_ARG;
+    if (n2 != 0 && (n2 < 2 || n2 > qt::kMaxGrid)) return QT_ERR_ARG;
+    if (!grid_ok(lo, hi)) return QT_ERR_ARG;
+    qt::GridTable tab{};
+    const int ncand = make_grid(n1, lo, hi, tab);
+    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, n2, true, tab, scales, codes,
+                                            nullptr, as_stream(stream)));
 }
 
 qt_status qt_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed, void* stream) {

@@ -19,9 +19,12 @@ struct GridTable {
     float fmin, fmax;
 };
 
+// ncand candidates of tab; signed_search: the two-stage signed search with n2
+// second-stage points (0: stage 1 only).
 hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
-                               int ncand, const GridTable& tab, float* scales,
-                               int8_t* codes, uint8_t* grid_idx, hipStream_t s);
+                               int ncand, int n2, bool signed_search, const GridTable& tab,
+                               float* scales, int8_t* codes, uint8_t* grid_idx,
+                               hipStream_t s);
 
 hipError_t launch_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed,
                           hipStream_t s);

@@ -194,10 +194,24 @@ __device__ __forceinline__ float group_error(const float (&w)[kGroup], const flo
     return a[0];
 }
 
-template <bool WEIGHTED>
+// Exactness margin for a factor f computed on the device (the second stage of
+// the signed search): the host's bound 4/f (1 + 2^-20) with extra slack that
+// covers the f32 rounding of this formula; a smaller margin only sends more
+// candidates to the division.
+__device__ __forceinline__ float device_margin(float f) {
+    const float bound = 4.0f / f * 1.001f;
+    return bound < 0x1p20f ? 0.5f - bound * 0x1p-21f : 0.0f;
+}
+
+// SIGNED: the two-stage signed search of the NeUQI page.  Stage 1 takes every
+// factor of the grid with both signs (k ascending, + before -); stage 2 takes
+// n2 points of [f_{k-1}, f_{k+1}] around the stage-1 winner k with its sign,
+// formed in double exactly as the grid itself; the final choice is the strict
+// minimum over [stage-1 winner, stage-2 points], so ties keep the earlier one.
+template <bool WEIGHTED, bool SIGNED>
 __global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
     const float* __restrict__ W, int64_t O, int32_t I, int32_t G,
-    const float* __restrict__ d, int32_t ncand, GridTable tab, int vec,
+    const float* __restrict__ d, int32_t ncand, int32_t n2, GridTable tab, int vec,
     float* __restrict__ scales, int8_t* __restrict__ codes, uint8_t* __restrict__ grid_idx) {
     // consecutive blocks walk the group columns of one 64-row slab
     const int64_t rb = blockIdx.x / G;
@@ -236,21 +250,58 @@ __global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
     const bool group_ok = base >= 0x1p-125f && base * tab.fmin >= 0x1p-100f &&
                           base * tab.fmax <= 0x1p100f;
 
-    float best_e = 0.0f, best_s = 0.0f, best_margin = 0.0f;
-    int best_k = 0;
-    for (int k = 0; k < ncand; ++k) {
-        const float s = base * tab.f[k];
-        const float margin = tab.margin[k];
+    // objective of one candidate scale (reciprocal quotients, division where
+    // the exactness margin does not hold)
+    auto error_of = [&](float s, float margin) {
         const float r = __builtin_amdgcn_rcpf(s);
         float dev;
         float a = group_error<WEIGHTED, kReciprocal>(w, dj, s, r, &dev);
         if (!(group_ok && dev < margin))  // rare: some quotient near a half-integer
             a = group_error<WEIGHTED, kDivision>(w, dj, s, r, nullptr);
+        return a;
+    };
+    float best_e = 0.0f, best_s = 0.0f, best_margin = 0.0f;
+    int best_k = 0;
+    for (int k = 0; k < ncand; ++k) {
+        const float s = base * tab.f[k];
+        const float margin = tab.margin[k];
+        const float a = error_of(s, margin);
         if (k == 0 || a < best_e) {  // strict: the lowest k wins ties
             best_e = a;
             best_k = k;
             best_s = s;
             best_margin = margin;
+        }
+        if constexpr (SIGNED) {
+            const float an = error_of(-s, margin);
+            if (an < best_e) {
+                best_e = an;
+                best_k = k;
+                best_s = -s;
+                best_margin = margin;
+            }
+        }
+    }
+    if constexpr (SIGNED) {
+        if (n2 > 0) {
+            // the winner's neighbours on the grid (per lane: a global read of
+            // the kernel-argument table)
+            const float fa = tab.f[best_k > 0 ? best_k - 1 : 0];
+            const float fb = tab.f[best_k < ncand - 1 ? best_k + 1 : ncand - 1];
+            const double step = ((double)fb - (double)fa) / (double)(n2 - 1);
+            const bool neg = __builtin_signbit(best_s);
+            for (int j = 0; j < n2; ++j) {
+                const float f = j == n2 - 1 ? fb : (float)((double)fa + (double)j * step);
+                const float mag = base * f;
+                const float s = neg ? -mag : mag;
+                const float margin = device_margin(f);
+                const float a = error_of(s, margin);
+                if (a < best_e) {
+                    best_e = a;
+                    best_s = s;
+                    best_margin = margin;
+                }
+            }
         }
     }
 
@@ -284,7 +335,7 @@ __global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
     }
     const int64_t grp = o * G + g;
     scales[grp] = s;
-    if (grid_idx) grid_idx[grp] = (uint8_t)best_k;
+    if (!SIGNED && grid_idx) grid_idx[grp] = (uint8_t)best_k;
 }
 
 // One thread per group: 64 codes in, 24 packed bytes out (three 8-byte
@@ -349,24 +400,33 @@ __global__ __launch_bounds__(256) void pack_i3_kernel(const int8_t* __restrict__
 }  // namespace
 
 hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
-                               int ncand, const GridTable& tab, float* scales,
-                               int8_t* codes, uint8_t* grid_idx, hipStream_t s) {
+                               int ncand, int n2, bool signed_search, const GridTable& tab,
+                               float* scales, int8_t* codes, uint8_t* grid_idx,
+                               hipStream_t s) {
     const int64_t G = (I + kGroup - 1) / kGroup;
-    if (ncand > 1) {
+    if (ncand > 1 || signed_search) {
         // lane-per-group search: blocks = G * ceil(O / 64)
         const bool w16 = (reinterpret_cast<uintptr_t>(W) & 15) == 0;
         const bool c16 = (reinterpret_cast<uintptr_t>(codes) & 15) == 0;
         const int vec = (w16 && I % 4 == 0) ? ((c16 && I % 16 == 0) ? 2 : 1) : 0;
         const int64_t blocks = G * ((O + kSearchRows - 1) / kSearchRows);
         if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        if (d)
-            hipLaunchKernelGGL(search_g64_kernel<true>, dim3((unsigned)blocks), dim3(kSearchRows),
-                               0, s, W, O, (int32_t)I, (int32_t)G, d, ncand, tab, vec, scales,
-                               codes, grid_idx);
-        else
-            hipLaunchKernelGGL(search_g64_kernel<false>, dim3((unsigned)blocks), dim3(kSearchRows),
-                               0, s, W, O, (int32_t)I, (int32_t)G, d, ncand, tab, vec, scales,
-                               codes, grid_idx);
+#define QT_SEARCH(WT, SG)                                                                    \
+    hipLaunchKernelGGL((search_g64_kernel<WT, SG>), dim3((unsigned)blocks), dim3(kSearchRows), \
+                       0, s, W, O, (int32_t)I, (int32_t)G, d, ncand, n2, tab, vec, scales,   \
+                       codes, grid_idx)
+        if (signed_search) {
+            if (d)
+                QT_SEARCH(true, true);
+            else
+                QT_SEARCH(false, true);
+        } else {
+            if (d)
+                QT_SEARCH(true, false);
+            else
+                QT_SEARCH(false, false);
+        }
+#undef QT_SEARCH
         return hipGetLastError();
     }
     const int64_t n_groups = O * G;

@@ -29,6 +29,9 @@ _SIGS = {
     "qt_quantize_g64": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
                                   C.c_float, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p]),
+    "qt_quantize_g64_signed": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
+                                         C.c_int32, C.c_int32, C.c_float, C.c_float,
+                                         C.c_void_p, C.c_void_p, C.c_void_p]),
     "qt_pack_i3": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]),
     "qt_matvec_i3": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
                                C.c_void_p, C.c_void_p]),
@@ -143,6 +146,24 @@ def qt_quantize_g64(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0
                                  _ptr(codes), _ptr(grid_idx), _stream(stream, dev)),
            "qt_quantize_g64")
     return scales, codes, grid_idx
+
+
+def qt_quantize_g64_signed(W, d=None, n1: int = 64, n2: int = 32, lo: float = 0.5,
+                           hi: float = 1.0, scales=None, codes=None, stream=None):
+    """Two-stage signed search: W [O, I] f32 -> (scales [O, G] f32, codes [O, I] int8)."""
+    O, I = W.shape
+    G = qt_groups(I)
+    if scales is None:
+        scales = torch.empty((O, G), dtype=torch.float32, device=W.device)
+    if codes is None:
+        codes = torch.empty((O, I), dtype=torch.int8, device=W.device)
+    dev = _dev(W, d, scales, codes)
+    if W.dtype != torch.float32 or (d is not None and d.dtype != torch.float32):
+        raise ValueError("W and d must be float32")
+    _check(lib().qt_quantize_g64_signed(_ptr(W), O, I, _ptr(d), n1, n2, lo, hi, _ptr(scales),
+                                        _ptr(codes), _stream(stream, dev)),
+           "qt_quantize_g64_signed")
+    return scales, codes
 
 
 def qt_pack_i3(codes, packed=None, stream=None):

@@ -116,6 +116,27 @@ qt_status qt_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
                           int8_t* codes, uint8_t* grid_idx, void* stream);
 
 /*
+ * Two-stage signed scale search (NeUQI accuracy page, first paragraph:
+ * symmetric layers use a two-stage signed scale search; results notes: 64/32
+ * points by default).  Objective, rounding, codes and tie rule as
+ * qt_quantize_g64; the candidates are
+ *   stage 1: s = +base*f_k and -base*f_k for k = 0..n1-1 (order: k
+ *            ascending, + before -), f_k the n1-point grid of [lo, hi];
+ *   stage 2: n2 points t_j of [f_{k1-1}, f_{k1+1}] around the stage-1
+ *            winner k1 (clipped to the grid ends), t_j formed like the grid,
+ *            with the winner's sign;
+ * and the result is the strict minimum over [stage-1 winner, t_0 .. t_{n2-1}]
+ * (ties keep the earlier candidate).  A negative scale lets the largest |w|
+ * take the -4 level.  Scales may be negative; codes and scales are bit-exact
+ * functions of the inputs.
+ *   n1  2..256; n2 0 (stage 1 only) or 2..256; lo, hi with 0 < lo <= hi
+ *   other arguments as qt_quantize_g64 (no grid index output)
+ */
+qt_status qt_quantize_g64_signed(const float* W, int64_t O, int64_t I, const float* d,
+                                 int32_t n1, int32_t n2, float lo, float hi, float* scales,
+                                 int8_t* codes, void* stream);
+
+/*
  * Bit-plane packer (pull request page, "Design", Layout bullet): codes
  * [O x I] int8 in [-4, 3] -> packed [O*G*24] bytes in the layout described at
  * the top of this header, short groups padded with v = 0.  Codes outside

@@ -31,6 +31,7 @@ def lib():
         L.qto_grid_factor.restype = F32
         L.qto_grid_factor.argtypes = [I32, I32, F32, F32]
         L.qto_quantize_g64.argtypes = [P, I64, I64, P, I32, F32, F32, P, P, P, P]
+        L.qto_quantize_g64_signed.argtypes = [P, I64, I64, P, I32, I32, F32, F32, P, P]
         L.qto_pack_i3.argtypes = [P, I64, I64, P]
         L.qto_unpack_i3.argtypes = [P, I64, I64, P]
         L.qto_matvec_f64.argtypes = [P, P, I64, I64, P, P, P]
@@ -39,7 +40,7 @@ def lib():
         L.qto_hessian_diag.argtypes = [P, I64, I64, P, P]
         L.qto_rowint_recon.argtypes = [P, I64, I64, I32, P]
         L.qto_dequant_f64.argtypes = [P, P, I64, I64, P]
-        for f in ("qto_quantize_g64", "qto_pack_i3", "qto_unpack_i3", "qto_matvec_f64",
+        for f in ("qto_quantize_g64", "qto_quantize_g64_signed", "qto_pack_i3", "qto_unpack_i3", "qto_matvec_f64",
                   "qto_matmul_f64_sampled", "qto_matvec_f32", "qto_hessian_diag",
                   "qto_rowint_recon", "qto_dequant_f64"):
             getattr(L, f).restype = None
@@ -85,6 +86,20 @@ def quantize_g64(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0,
     if return_errs:
         return scales, codes, gidx, errs
     return scales, codes, gidx
+
+
+def quantize_g64_signed(W, d=None, n1: int = 64, n2: int = 32, lo: float = 0.5,
+                        hi: float = 1.0):
+    """Two-stage signed scale search -> (scales[O,G] f32, codes[O,I] int8)."""
+    W = _c(W, np.float32)
+    O, I = W.shape
+    G = groups(I)
+    d = None if d is None else _c(d, np.float32)
+    scales = np.empty((O, G), np.float32)
+    codes = np.empty((O, I), np.int8)
+    lib().qto_quantize_g64_signed(_p(W), O, I, _p(d), n1, n2, lo, hi, _p(scales),
+                                  _p(codes))
+    return scales, codes
 
 
 def pack_i3(codes):

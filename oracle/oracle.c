@@ -38,6 +38,39 @@ static int code_for(float w, float s) {
     return (int)r;
 }
 
+/* Weighted squared reconstruction error of one group at scale s, the search
+ * objective: every slot's error d*(w - s*q)^2 with each operation a rounded
+ * f32 operation (padding slots of a short tail group contribute zero), then
+ * the pairwise halving sum a[j] += a[j+m], m = 32, 16, ..., 1. */
+static float group_error(const float* w, int n, const float* dg, float s) {
+    float a[GROUP];
+    for (int j = 0; j < GROUP; ++j) {
+        if (j < n) {
+            const int q = code_for(w[j], s);
+            const float t = s * (float)q;
+            const float r = w[j] - t;
+            const float r2 = r * r;
+            a[j] = dg ? dg[j] * r2 : r2;
+        } else {
+            a[j] = 0.0f;
+        }
+    }
+    for (int m = GROUP / 2; m >= 1; m /= 2)
+        for (int j = 0; j < m; ++j) a[j] = a[j] + a[j + m];
+    return a[0];
+}
+
+/* base scale: absmax over the group's real values, times 1/4 (a 3-bit
+ * symmetric quantizer: 2^(3-1) = 4 levels per side) */
+static float group_base(const float* w, int n) {
+    float amax = 0.0f;
+    for (int j = 0; j < n; ++j) {
+        float a = fabsf(w[j]);
+        if (a > amax) amax = a;
+    }
+    return amax * 0.25f;
+}
+
 void qto_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
                       int n_grid, float lo, float hi, float* scales,
                       int8_t* codes, uint8_t* grid_idx, float* errs) {
@@ -48,39 +81,14 @@ void qto_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
             const int64_t c0 = g * GROUP;
             const int n = (int)((I - c0) < GROUP ? (I - c0) : GROUP);
             const float* w = W + o * I + c0;
-
-            /* base scale: absmax over the group's real values, times 1/4
-             * (a 3-bit symmetric quantizer: 2^(3-1) = 4 levels per side) */
-            float amax = 0.0f;
-            for (int j = 0; j < n; ++j) {
-                float a = fabsf(w[j]);
-                if (a > amax) amax = a;
-            }
-            const float base = amax * 0.25f;
+            const float base = group_base(w, n);
 
             int best_k = 0;
             float best_e = 0.0f;
             for (int k = 0; k < ncand; ++k) {
                 const float f = n_grid == 0 ? 1.0f : qto_grid_factor(k, n_grid, lo, hi);
                 const float s = base * f;
-                /* weighted squared reconstruction error of every slot;
-                 * padding slots of a short tail group contribute zero */
-                float a[GROUP];
-                for (int j = 0; j < GROUP; ++j) {
-                    if (j < n) {
-                        const int q = code_for(w[j], s);
-                        const float t = s * (float)q;
-                        const float r = w[j] - t;
-                        const float r2 = r * r;
-                        a[j] = d ? d[c0 + j] * r2 : r2;
-                    } else {
-                        a[j] = 0.0f;
-                    }
-                }
-                /* pairwise halving sum: a[j] += a[j+m], m = 32, 16, ..., 1 */
-                for (int m = GROUP / 2; m >= 1; m /= 2)
-                    for (int j = 0; j < m; ++j) a[j] = a[j] + a[j + m];
-                const float e = a[0];
+                const float e = group_error(w, n, d ? d + c0 : NULL, s);
                 if (errs) errs[(o * G + g) * ncand + k] = e;
                 if (k == 0 || e < best_e) { /* lowest k wins ties */
                     best_e = e;
@@ -92,6 +100,65 @@ void qto_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
             scales[o * G + g] = s;
             if (grid_idx) grid_idx[o * G + g] = (uint8_t)best_k;
             for (int j = 0; j < n; ++j) codes[o * I + c0 + j] = (int8_t)code_for(w[j], s);
+        }
+    }
+}
+
+/* NeUQI page, first paragraph and results notes: symmetric layers use a
+ * two-stage signed scale search, 64 then 32 points by default ("64/32").
+ * Reading of the stages (the pages give no formula):
+ *   stage 1: the n1-point grid f_k of [lo, hi] times base, each factor with
+ *            both signs, candidate order k ascending, + before - (a negative
+ *            scale lets the largest |w| take the -4 level);
+ *   stage 2: n2 points of [f_{k-1}, f_{k+1}] around the stage-1 winner k
+ *            (clipped to the grid ends), same linspace rule, with the
+ *            winner's sign;
+ *   the final choice is the strict minimum over [stage-1 winner, stage-2
+ *   points in order], so ties keep the earlier candidate and the result is
+ *   never worse than stage 1.  n2 == 0: stage 1 only. */
+void qto_quantize_g64_signed(const float* W, int64_t O, int64_t I, const float* d, int n1,
+                             int n2, float lo, float hi, float* scales, int8_t* codes) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o) {
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t c0 = g * GROUP;
+            const int n = (int)((I - c0) < GROUP ? (I - c0) : GROUP);
+            const float* w = W + o * I + c0;
+            const float* dg = d ? d + c0 : NULL;
+            const float base = group_base(w, n);
+
+            int best_k = 0, best_neg = 0, first = 1;
+            float best_e = 0.0f;
+            for (int k = 0; k < n1; ++k) {
+                for (int neg = 0; neg < 2; ++neg) {
+                    const float mag = base * qto_grid_factor(k, n1, lo, hi);
+                    const float s = neg ? -mag : mag;
+                    const float e = group_error(w, n, dg, s);
+                    if (first || e < best_e) {
+                        best_e = e;
+                        best_k = k;
+                        best_neg = neg;
+                        first = 0;
+                    }
+                }
+            }
+            const float mag1 = base * qto_grid_factor(best_k, n1, lo, hi);
+            float best_s = best_neg ? -mag1 : mag1;
+            if (n2 > 0) {
+                const float a = qto_grid_factor(best_k > 0 ? best_k - 1 : 0, n1, lo, hi);
+                const float b = qto_grid_factor(best_k < n1 - 1 ? best_k + 1 : n1 - 1, n1, lo, hi);
+                for (int j = 0; j < n2; ++j) {
+                    const float mag = base * qto_grid_factor(j, n2, a, b);
+                    const float s = best_neg ? -mag : mag;
+                    const float e = group_error(w, n, dg, s);
+                    if (e < best_e) {
+                        best_e = e;
+                        best_s = s;
+                    }
+                }
+            }
+            scales[o * G + g] = best_s;
+            for (int j = 0; j < n; ++j) codes[o * I + c0 + j] = (int8_t)code_for(w[j], best_s);
         }
     }
 }

@@ -58,6 +58,13 @@ void qto_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
                       int n_grid, float lo, float hi, float* scales,
                       int8_t* codes, uint8_t* grid_idx, float* errs);
 
+/* Two-stage signed scale search (NeUQI page): stage 1 over the n1-point grid
+ * of [lo, hi] with both signs, stage 2 over n2 points between the stage-1
+ * winner's neighbours with its sign (n2 == 0: stage 1 only).  Same objective,
+ * rounding and tie rule as qto_quantize_g64; scales may be negative. */
+void qto_quantize_g64_signed(const float* W, int64_t O, int64_t I, const float* d, int n1,
+                             int n2, float lo, float hi, float* scales, int8_t* codes);
+
 /* Bit-plane packer / unpacker (codes in [-4,3]; packed O*G*24 bytes). */
 void qto_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed);
 void qto_unpack_i3(const uint8_t* packed, int64_t O, int64_t I, int8_t* codes);

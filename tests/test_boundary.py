@@ -63,6 +63,21 @@ def setup_module(_):
     L = qt.lib()
 
 
+def test_quantize_signed_rejects():
+    f = L.qt_quantize_g64_signed
+    assert f(None, 4, 64, None, 64, 32, 0.5, 1.0, B, Cc, None) == QT_ERR_NULL
+    assert f(A, 0, 64, None, 64, 32, 0.5, 1.0, B, Cc, None) == QT_ERR_SHAPE
+    assert f(A, 4, 64, None, 1, 32, 0.5, 1.0, B, Cc, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 0, 32, 0.5, 1.0, B, Cc, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 257, 32, 0.5, 1.0, B, Cc, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 64, 1, 0.5, 1.0, B, Cc, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 64, 257, 0.5, 1.0, B, Cc, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 64, 32, 0.0, 1.0, B, Cc, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 64, 32, 1.0, 0.5, B, Cc, None) == QT_ERR_ARG
+    assert f(A + 2, 4, 64, None, 64, 32, 0.5, 1.0, B, Cc, None) == QT_ERR_ALIGN
+    assert f(A, 4, 64, None, 64, 32, 0.5, 1.0, A + 16, Cc, None) == QT_ERR_ALIAS
+
+
 def test_quantize_rejects():
     f = L.qt_quantize_g64
     assert f(None, 4, 64, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_NULL

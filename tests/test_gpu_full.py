@@ -130,3 +130,11 @@ def test_search_and_hessian_full_size_sampled():
     assert np.array_equal(k[rows], ko), "grid indices differ"
     say(f"  {rows.size} sampled rows bit-exact; grid index histogram head "
         f"{np.bincount(k.reshape(-1), minlength=64)[:4]}")
+    say(f"search: W[{O}x{I}] two-stage signed 64/32 weighted search on the GPU")
+    s2, c2 = qt.qt_quantize_g64_signed(dev(W), dev(d), 64, 32, 0.5, 1.0)
+    s2, c2 = host(s2), host(c2)
+    rows = np.sort(rng.choice(O, size=6, replace=False))
+    so2, co2 = oracle.quantize_g64_signed(W[rows], d, 64, 32, 0.5, 1.0)
+    assert np.array_equal(bits(s2[rows]), bits(so2)), "signed scales differ"
+    assert np.array_equal(c2[rows], co2), "signed codes differ"
+    say(f"  {rows.size} sampled rows bit-exact; negative scales {np.mean(s2 < 0):.3f}")

@@ -103,6 +103,55 @@ def test_search_bit_exact(n_grid, lo, hi, weighted):
     check_quantize(W, d, n_grid, lo, hi)
 
 
+def check_signed(W, d, n1, n2, lo=0.5, hi=1.0):
+    O, I = W.shape
+    say(f"signed search O={O} I={I} n1={n1} n2={n2} weighted={d is not None}")
+    s, c = qt.qt_quantize_g64_signed(dev(W), None if d is None else dev(d), n1, n2, lo, hi)
+    s, c = host(s), host(c)
+    so, co = oracle.quantize_g64_signed(W, d, n1, n2, lo, hi)
+    assert np.array_equal(bits(s), bits(so)), "scales differ"
+    assert np.array_equal(c, co), "codes differ"
+    # the packed planes of negative-scale groups multiply like any other
+    p = host(qt.qt_pack_i3(dev(c)))
+    assert np.array_equal(p, oracle.pack_i3(co))
+    return so, co
+
+
+@pytest.mark.parametrize("n1,n2,lo,hi", [(64, 32, 0.5, 1.0), (64, 0, 0.5, 1.0),
+                                         (16, 8, 0.3, 1.2), (2, 2, 0.75, 0.75)])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_signed_search_bit_exact(n1, n2, lo, hi, weighted):
+    O, I = 70, 1000
+    W = workloads.generic_weights(O, I, seed=100 + n1 + n2)
+    W[5, 64:128] = 0.0  # an all-zero group
+    d = None
+    if weighted:
+        d = np.exp(workloads.generic_vector(I, seed=6)).astype(np.float32)
+        d[9] = 0.0
+    so, co = check_signed(W, d, n1, n2, lo, hi)
+    # some groups really choose a negative scale
+    assert np.any(so < 0) and np.any(so > 0)
+
+
+def test_signed_search_special_groups_and_matvec():
+    O, I = 6, 192
+    W = np.zeros((O, I), np.float32)
+    W[0, 0] = 4.0                     # best scale -1: 4 on code -4 exactly
+    W[1, :] = -0.5                    # equal magnitudes of one sign
+    W[2] = np.tile(np.array([1.0, -1.0, 0.5, -0.5], np.float32), I // 4)
+    W[3, 7] = 3.0e-39                 # subnormal group maximum
+    W[4] = workloads.generic_weights(1, I, seed=8)[0] * np.float32(1e30)
+    W[5] = workloads.generic_weights(1, I, seed=9)[0]
+    so, co = check_signed(W, None, 64, 32)
+    assert so[0, 0] == np.float32(-1.0) and co[0, 0] == -4
+    # a matvec over signed scales against the f64 reference
+    po = oracle.pack_i3(co)
+    x = workloads.generic_vector(I, seed=10)
+    y = host(qt.qt_matvec_i3(dev(po), dev(so), O, I, dev(x)))
+    yr, ar = oracle.matvec_f64(po, so, O, I, x)
+    assert componentwise_err(y, yr, ar) <= TOL_F32
+
+
 def test_search_ties_and_special_groups():
     # groups built so that many candidates tie exactly (equal magnitudes on a
     # power-of-two grid); the lowest k must win on both sides
@@ -323,3 +372,6 @@ def test_search_quotients_on_and_next_to_half_integers():
     check_quantize(W, None, 0)
     d = np.exp(workloads.generic_vector(64, seed=17)).astype(np.float32)
     check_quantize(W, d, 64, 0.5, 1.0)
+    # the signed search meets the same quotients with both signs
+    check_signed(W, None, 64, 32)
+    check_signed(W, d, 64, 0)

@@ -232,6 +232,98 @@ def test_search_worked_example_s():
                                      * np.linspace(0.5, 1.0, 64).astype(np.float32)[k[0, 0]])
 
 
+# ---------------------------------------------------------------- signed two-stage search
+def _err_f64(w, d, s):
+    """The objective for one scale in f64 (codes as the method decides them:
+    the f32 quotient rounded to nearest even, clamped)."""
+    s = np.float32(s)
+    if s == 0:
+        q = np.zeros_like(w, np.float64)
+    else:
+        q = np.clip(np.rint((w / s).astype(np.float32)).astype(np.float64), -4, 3)
+    r = w.astype(np.float64) - float(s) * q
+    return float(np.sum(d.astype(np.float64) * r * r))
+
+
+def test_signed_search_worked_example():
+    # w = (4, 0, ..., 0): base = 1.  Positive scales put 4 on code 3 at best
+    # (f = 1: error (4 - 3)^2 = 1); the scale -1 puts it on -4 exactly
+    # (error 0), which a signed search must find; the refinement keeps it.
+    w = np.zeros((1, 64), np.float32)
+    w[0, 0] = 4.0
+    for n2 in (0, 32):
+        s, c = oracle.quantize_g64_signed(w, None, 64, n2)
+        assert s[0, 0] == np.float32(-1.0) and c[0, 0] == -4 and np.all(c[0, 1:] == 0)
+    su, cu, _ = oracle.quantize_g64(w, None, 64)
+    assert su[0, 0] == np.float32(1.0) and cu[0, 0] == 3
+    # an all-zero group: scale +0, codes 0
+    z = np.zeros((1, 70), np.float32)
+    s, c = oracle.quantize_g64_signed(z, None, 64, 32)
+    assert np.all(s == 0) and not np.any(np.signbit(s)) and np.all(c == 0)
+
+
+def test_signed_stage1_against_f64_bruteforce():
+    # stage 1 alone (n2 = 0) is the best of 2 x 64 signed candidates
+    rng = workloads.rng_for("generic", 92)
+    O, I = 30, 64 * 4
+    W = workloads.generic_weights(O, I, seed=21)
+    d = np.exp(rng.normal(size=I)).astype(np.float32)
+    s, c = oracle.quantize_g64_signed(W, d, 64, 0)
+    fk = np.linspace(0.5, 1.0, 64).astype(np.float32)
+    clear = 0
+    for o in range(O):
+        for g in range(I // 64):
+            w, dg = W[o, 64 * g:64 * g + 64], d[64 * g:64 * g + 64]
+            base = np.float32(np.float32(np.max(np.abs(w))) * np.float32(0.25))
+            cands = [np.float32(sg * np.float32(base * f)) for f in fk for sg in (1, -1)]
+            E = np.array([_err_f64(w, dg, x) for x in cands])
+            e = _err_f64(w, dg, s[o, g])
+            assert e <= E.min() * (1 + 1e-5) + 1e-30
+            srt = np.sort(E)
+            if srt[1] > srt[0] * (1 + 1e-4):
+                clear += 1
+                assert s[o, g] == cands[int(np.argmin(E))]
+    assert clear > O
+
+
+def test_signed_search_invariants():
+    W = workloads.generic_weights(48, 64 * 5 + 20, seed=23)
+    I = W.shape[1]
+    d = (np.abs(workloads.generic_vector(I, seed=24)) + 0.05).astype(np.float32)
+    s1, c1 = oracle.quantize_g64_signed(W, d, 64, 0)
+    s2, c2 = oracle.quantize_g64_signed(W, d, 64, 32)
+    su, cu, _ = oracle.quantize_g64(W, d=d, n_grid=64)
+    G = s2.shape[1]
+    fk = np.linspace(0.5, 1.0, 64).astype(np.float32)
+    for o in range(W.shape[0]):
+        for g in range(G):
+            lo_, hi_ = 64 * g, min(64 * g + 64, I)
+            w, dg = W[o, lo_:hi_], d[lo_:hi_]
+            e_u = _err_f64(w, dg, su[o, g])
+            e_1 = _err_f64(w, dg, s1[o, g])
+            e_2 = _err_f64(w, dg, s2[o, g])
+            # each stage can only improve (up to f32 rounding of the objective)
+            assert e_1 <= e_u * (1 + 1e-5) + 1e-30
+            assert e_2 <= e_1 * (1 + 1e-5) + 1e-30
+            # a refined scale keeps the stage-1 sign and lies between the
+            # stage-1 winner's neighbours on the grid
+            assert np.signbit(s2[o, g]) == np.signbit(s1[o, g])
+            base = np.float32(np.float32(np.max(np.abs(w))) * np.float32(0.25))
+            k = int(np.argmin(np.abs(np.abs(s1[o, g]) - base * fk)))
+            a, b = fk[max(k - 1, 0)], fk[min(k + 1, 63)]
+            assert base * a * (1 - 1e-6) <= abs(s2[o, g]) <= base * b * (1 + 1e-6)
+            # codes are the rounding rule applied to the chosen scale
+            q = np.clip(np.rint((w / s2[o, g]).astype(np.float32)), -4, 3)
+            assert np.array_equal(c2[o, lo_:hi_], q.astype(np.int8))
+    # negating W negates every scale and keeps the codes (the candidate set
+    # holds both signs) wherever stage 1 has a unique winner
+    s3, c3 = oracle.quantize_g64_signed(-W, d, 64, 0)
+    same = s3 == -s1
+    assert same.mean() > 0.95
+    for o, g in zip(*np.nonzero(same)):
+        assert np.array_equal(c3[o, 64 * g:64 * g + 64], c1[o, 64 * g:64 * g + 64])
+
+
 # ---------------------------------------------------------------- matvec / matmul
 def _quantized(O, I, seed):
     W = workloads.generic_weights(O, I, seed=seed)
