@@ -32,6 +32,12 @@ def lib():
         L.qto_grid_factor.argtypes = [I32, I32, F32, F32]
         L.qto_quantize_g64.argtypes = [P, I64, I64, P, I32, F32, F32, P, P, P, P]
         L.qto_quantize_g64_signed.argtypes = [P, I64, I64, P, I32, I32, F32, F32, P, P]
+        L.qto_packed_bytes_i4.restype = I64
+        L.qto_packed_bytes_i4.argtypes = [I64, I64]
+        L.qto_quantize_g64_i4.argtypes = [P, I64, I64, P, I32, F32, F32, P, P, P]
+        L.qto_pack_i4.argtypes = [P, I64, I64, P]
+        L.qto_unpack_i4.argtypes = [P, I64, I64, P]
+        L.qto_matvec_i4_f64.argtypes = [P, P, I64, I64, P, P, P]
         L.qto_pack_i3.argtypes = [P, I64, I64, P]
         L.qto_unpack_i3.argtypes = [P, I64, I64, P]
         L.qto_matvec_f64.argtypes = [P, P, I64, I64, P, P, P]
@@ -40,7 +46,8 @@ def lib():
         L.qto_hessian_diag.argtypes = [P, I64, I64, P, P]
         L.qto_rowint_recon.argtypes = [P, I64, I64, I32, P]
         L.qto_dequant_f64.argtypes = [P, P, I64, I64, P]
-        for f in ("qto_quantize_g64", "qto_quantize_g64_signed", "qto_pack_i3", "qto_unpack_i3", "qto_matvec_f64",
+        for f in ("qto_quantize_g64_i4", "qto_pack_i4", "qto_unpack_i4", "qto_matvec_i4_f64",
+                  "qto_quantize_g64", "qto_quantize_g64_signed", "qto_pack_i3", "qto_unpack_i3", "qto_matvec_f64",
                   "qto_matmul_f64_sampled", "qto_matvec_f32", "qto_hessian_diag",
                   "qto_rowint_recon", "qto_dequant_f64"):
             getattr(L, f).restype = None
@@ -100,6 +107,51 @@ def quantize_g64_signed(W, d=None, n1: int = 64, n2: int = 32, lo: float = 0.5,
     lib().qto_quantize_g64_signed(_p(W), O, I, _p(d), n1, n2, lo, hi, _p(scales),
                                   _p(codes))
     return scales, codes
+
+
+def packed_bytes_i4(O: int, I: int) -> int:
+    return int(lib().qto_packed_bytes_i4(O, I))
+
+
+def quantize_g64_i4(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0):
+    """Grouped int4 -> (scales[O,G] f32, codes[O,I] int8 in [-8,7], grid_idx[O,G] uint8)."""
+    W = _c(W, np.float32)
+    O, I = W.shape
+    G = groups(I)
+    d = None if d is None else _c(d, np.float32)
+    scales = np.empty((O, G), np.float32)
+    codes = np.empty((O, I), np.int8)
+    gidx = np.empty((O, G), np.uint8)
+    lib().qto_quantize_g64_i4(_p(W), O, I, _p(d), n_grid, lo, hi, _p(scales), _p(codes),
+                              _p(gidx))
+    return scales, codes, gidx
+
+
+def pack_i4(codes):
+    codes = _c(codes, np.int8)
+    O, I = codes.shape
+    out = np.empty(packed_bytes_i4(O, I), np.uint8)
+    lib().qto_pack_i4(_p(codes), O, I, _p(out))
+    return out
+
+
+def unpack_i4(packed, O: int, I: int):
+    packed = _c(packed, np.uint8)
+    assert packed.size == packed_bytes_i4(O, I)
+    out = np.empty((O, I), np.int8)
+    lib().qto_unpack_i4(_p(packed), O, I, _p(out))
+    return out
+
+
+def matvec_i4_f64(packed, scales, O: int, I: int, x):
+    """-> (y[O] f64, sum_i |w_oi x_i| [O] f64) for grouped int4 weights."""
+    packed = _c(packed, np.uint8)
+    scales = _c(scales, np.float32)
+    x = _c(x, np.float32)
+    y = np.empty(O, np.float64)
+    a = np.empty(O, np.float64)
+    lib().qto_matvec_i4_f64(_p(packed), _p(scales), O, I, _p(x), _p(y), _p(a))
+    return y, a
 
 
 def pack_i3(codes):

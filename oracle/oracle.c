@@ -28,25 +28,29 @@ float qto_grid_factor(int k, int n, float lo, float hi) {
 }
 
 /* Round-to-nearest-even of the correctly rounded f32 quotient w/s, clamped
- * to the code range [-4, 3] of the pull request page ("Design", Layout). */
-static int code_for(float w, float s) {
+ * to the code range [cmin, cmax]: [-4, 3] for int3-g64 (pull request page,
+ * "Design", Layout), [-8, 7] for grouped int4. */
+static int code_in(float w, float s, float cmin, float cmax) {
     if (s == 0.0f) return 0;
     float q = w / s;
     float r = rintf(q); /* default rounding mode: to nearest, ties to even */
-    if (r < -4.0f) r = -4.0f;
-    if (r > 3.0f) r = 3.0f;
+    if (r < cmin) r = cmin;
+    if (r > cmax) r = cmax;
     return (int)r;
 }
+
+static int code_for(float w, float s) { return code_in(w, s, -4.0f, 3.0f); }
 
 /* Weighted squared reconstruction error of one group at scale s, the search
  * objective: every slot's error d*(w - s*q)^2 with each operation a rounded
  * f32 operation (padding slots of a short tail group contribute zero), then
  * the pairwise halving sum a[j] += a[j+m], m = 32, 16, ..., 1. */
-static float group_error(const float* w, int n, const float* dg, float s) {
+static float group_error_in(const float* w, int n, const float* dg, float s, float cmin,
+                            float cmax) {
     float a[GROUP];
     for (int j = 0; j < GROUP; ++j) {
         if (j < n) {
-            const int q = code_for(w[j], s);
+            const int q = code_in(w[j], s, cmin, cmax);
             const float t = s * (float)q;
             const float r = w[j] - t;
             const float r2 = r * r;
@@ -58,6 +62,10 @@ static float group_error(const float* w, int n, const float* dg, float s) {
     for (int m = GROUP / 2; m >= 1; m /= 2)
         for (int j = 0; j < m; ++j) a[j] = a[j] + a[j + m];
     return a[0];
+}
+
+static float group_error(const float* w, int n, const float* dg, float s) {
+    return group_error_in(w, n, dg, s, -4.0f, 3.0f);
 }
 
 /* base scale: absmax over the group's real values, times 1/4 (a 3-bit
@@ -312,5 +320,100 @@ void qto_rowint_recon(const float* W, int64_t O, int64_t I, int bits,
             }
             recon[o * I + i] = (double)s * (double)q;
         }
+    }
+}
+
+
+/* ------------------------------------------------------------------ grouped int4
+ * The pull request page names group-scaled int4 (the format number it took,
+ * and grouped int4 at gs = 64 carrying the same O*ceil(I/64) scale count); it
+ * prints no layout.  Readings: a 4-bit symmetric absmax quantizer per
+ * 64-input group (base = absmax * 2^-(4-1) = absmax/8, codes in [-8, 7]), the
+ * same objective, grid and tie rule as int3-g64; storage per group 32 bytes of
+ * u = v + 8, code j in the low nibble of byte j/2 for even j and in the high
+ * nibble for odd j; one f32 scale per group in its own tensor; short tail
+ * groups padded with v = 0 (u = 8). */
+int64_t qto_packed_bytes_i4(int64_t O, int64_t I) { return O * qto_groups(I) * 32; }
+
+void qto_quantize_g64_i4(const float* W, int64_t O, int64_t I, const float* d, int n_grid,
+                         float lo, float hi, float* scales, int8_t* codes, uint8_t* grid_idx) {
+    const int64_t G = qto_groups(I);
+    const int ncand = n_grid == 0 ? 1 : n_grid;
+    for (int64_t o = 0; o < O; ++o) {
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t c0 = g * GROUP;
+            const int n = (int)((I - c0) < GROUP ? (I - c0) : GROUP);
+            const float* w = W + o * I + c0;
+            float amax = 0.0f;
+            for (int j = 0; j < n; ++j) {
+                float a = fabsf(w[j]);
+                if (a > amax) amax = a;
+            }
+            const float base = amax * 0.125f;
+            int best_k = 0;
+            float best_e = 0.0f;
+            for (int k = 0; k < ncand; ++k) {
+                const float f = n_grid == 0 ? 1.0f : qto_grid_factor(k, n_grid, lo, hi);
+                const float s = base * f;
+                const float e = group_error_in(w, n, d ? d + c0 : NULL, s, -8.0f, 7.0f);
+                if (k == 0 || e < best_e) {
+                    best_e = e;
+                    best_k = k;
+                }
+            }
+            const float f = n_grid == 0 ? 1.0f : qto_grid_factor(best_k, n_grid, lo, hi);
+            const float s = base * f;
+            scales[o * G + g] = s;
+            if (grid_idx) grid_idx[o * G + g] = (uint8_t)best_k;
+            for (int j = 0; j < n; ++j)
+                codes[o * I + c0 + j] = (int8_t)code_in(w[j], s, -8.0f, 7.0f);
+        }
+    }
+}
+
+void qto_pack_i4(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o) {
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t c0 = g * GROUP;
+            const int n = (int)((I - c0) < GROUP ? (I - c0) : GROUP);
+            uint8_t* p = packed + (o * G + g) * 32;
+            for (int b = 0; b < 32; ++b) p[b] = 0;
+            for (int j = 0; j < GROUP; ++j) {
+                const int v = j < n ? codes[o * I + c0 + j] : 0;
+                const int u = v + 8;
+                p[j / 2] |= (uint8_t)((u & 15) << (4 * (j % 2)));
+            }
+        }
+    }
+}
+
+static int code_at_i4(const uint8_t* p, int j) {
+    return (int)((p[j / 2] >> (4 * (j % 2))) & 15) - 8;
+}
+
+void qto_unpack_i4(const uint8_t* packed, int64_t O, int64_t I, int8_t* codes) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o)
+        for (int64_t i = 0; i < I; ++i)
+            codes[o * I + i] =
+                (int8_t)code_at_i4(packed + (o * G + i / GROUP) * 32, (int)(i % GROUP));
+}
+
+void qto_matvec_i4_f64(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                       const float* x, double* y, double* absy) {
+    const int64_t G = qto_groups(I);
+    for (int64_t o = 0; o < O; ++o) {
+        double acc = 0.0, aacc = 0.0;
+        for (int64_t i = 0; i < I; ++i) {
+            const int64_t g = i / GROUP;
+            const int v = code_at_i4(packed + (o * G + g) * 32, (int)(i % GROUP));
+            const double w = (double)scales[o * G + g] * (double)v;
+            const double p = w * (double)x[i];
+            acc += p;
+            aacc += fabs(p);
+        }
+        y[o] = acc;
+        if (absy) absy[o] = aacc;
     }
 }

@@ -99,6 +99,17 @@ void qto_rowint_recon(const float* W, int64_t O, int64_t I, int bits,
 void qto_dequant_f64(const uint8_t* packed, const float* scales, int64_t O,
                      int64_t I, double* What);
 
+/* Grouped int4 (the pull request page's group-scaled int4; layout read as
+ * 32 bytes of u = v + 8 per 64-input group, low nibble first, v in [-8, 7],
+ * base = absmax/8, search and objective as int3-g64). */
+int64_t qto_packed_bytes_i4(int64_t O, int64_t I);
+void qto_quantize_g64_i4(const float* W, int64_t O, int64_t I, const float* d, int n_grid,
+                         float lo, float hi, float* scales, int8_t* codes, uint8_t* grid_idx);
+void qto_pack_i4(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed);
+void qto_unpack_i4(const uint8_t* packed, int64_t O, int64_t I, int8_t* codes);
+void qto_matvec_i4_f64(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                       const float* x, double* y, double* absy);
+
 #ifdef __cplusplus
 }
 #endif

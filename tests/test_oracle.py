@@ -447,3 +447,116 @@ def test_rowint_matches_numpy():
     s = (amax / np.float32(8)).astype(np.float32)
     q = np.clip(np.rint(W / s[:, None]), -8, 7)
     assert np.array_equal(oracle.rowint_recon(W, 4), s[:, None].astype(np.float64) * q)
+
+
+# ---------------------------------------------------------------- grouped int4
+def _np_decode_nibbles(packed, O, I):
+    """Independent decoder of the grouped int4 layout: 32 bytes per group,
+    code j in the low nibble of byte j/2 (even j) or the high nibble (odd j),
+    stored as v + 8."""
+    G = -(-I // 64)
+    b = np.asarray(packed, np.uint8).reshape(O, G, 32)
+    nib = np.stack([b & 15, b >> 4], axis=-1).reshape(O, G * 64)
+    return nib[:, :I].astype(np.int16) - 8
+
+
+def test_i4_format_and_worked_bytes():
+    assert oracle.packed_bytes_i4(3, 64) == 96 and oracle.packed_bytes_i4(2, 70) == 128
+    # v_j = (j mod 16) - 8: u_j = j mod 16, byte b = u_{2b} | u_{2b+1} << 4
+    c = ((np.arange(64) % 16) - 8).astype(np.int8)[None, :]
+    p = oracle.pack_i4(c)
+    assert list(p[:8]) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    assert np.array_equal(p[8:16], p[:8]) and np.array_equal(p[:16], p[16:32])
+    # a short tail group: 6 real codes (v = 7), the rest padded with v = 0
+    t = np.zeros((1, 70), np.int8)
+    t[0, 64:] = 7
+    q = oracle.pack_i4(t)
+    assert list(q[32:35]) == [0xFF, 0xFF, 0xFF] and np.all(q[35:64] == 0x88)
+    assert np.all(q[:32] == 0x88)
+
+
+def test_i4_every_position_and_code_roundtrip():
+    for v in range(-8, 8):
+        for j in range(64):
+            c = np.zeros((1, 64), np.int8)
+            c[0, j] = v
+            p = oracle.pack_i4(c)
+            assert np.array_equal(oracle.unpack_i4(p, 1, 64), c)
+            assert np.array_equal(_np_decode_nibbles(p, 1, 64), c.astype(np.int16))
+
+
+def test_i4_rtn_rounding_and_clamps():
+    # base = absmax/8 = 1 for absmax 8: quotients equal the weights
+    w = np.array([[8.0, 7.5, 6.5, -7.5, -8.0, 0.5, -0.5, 2.5] + [0.0] * 56], np.float32)
+    s, c, k = oracle.quantize_g64_i4(w)
+    assert s[0, 0] == np.float32(1.0)
+    # 8 -> 7 (clip), 7.5 -> 8 -> 7, 6.5 -> 6 (ties to even), -7.5 -> -8,
+    # -8 -> -8, 0.5 -> 0, -0.5 -> -0, 2.5 -> 2
+    assert list(c[0, :8]) == [7, 7, 6, -8, -8, 0, 0, 2]
+    W = workloads.generic_weights(20, 200, seed=31)
+    s, c, _ = oracle.quantize_g64_i4(W)
+    G = -(-200 // 64)
+    for g in range(G):
+        blk = W[:, 64 * g:64 * g + 64]
+        base = (np.max(np.abs(blk), axis=1) * np.float32(0.125)).astype(np.float32)
+        assert np.array_equal(s[:, g], base)
+        q = np.clip(np.rint((blk / base[:, None]).astype(np.float32)), -8, 7)
+        assert np.array_equal(c[:, 64 * g:64 * g + blk.shape[1]], q.astype(np.int8))
+
+
+def test_i4_search_against_f64_bruteforce():
+    rng = workloads.rng_for("generic", 93)
+    O, I = 24, 64 * 3
+    W = workloads.generic_weights(O, I, seed=33)
+    d = np.exp(rng.normal(size=I)).astype(np.float32)
+    s, c, k = oracle.quantize_g64_i4(W, d, 64, 0.5, 1.0)
+    fk = np.linspace(0.5, 1.0, 64).astype(np.float32)
+    clear = 0
+    for o in range(O):
+        for g in range(I // 64):
+            w, dg = W[o, 64 * g:64 * g + 64], d[64 * g:64 * g + 64]
+            base = np.float32(np.float32(np.max(np.abs(w))) * np.float32(0.125))
+            E = []
+            for f in fk:
+                sc = np.float32(base * f)
+                q = np.clip(np.rint((w / sc).astype(np.float32)).astype(np.float64), -8, 7)
+                r = w.astype(np.float64) - float(sc) * q
+                E.append(float(np.sum(dg.astype(np.float64) * r * r)))
+            E = np.array(E)
+            kk = int(k[o, g])
+            assert E[kk] <= E.min() * (1 + 1e-5) + 1e-30
+            srt = np.sort(E)
+            if srt[1] > srt[0] * (1 + 1e-4):
+                clear += 1
+                assert kk == int(np.argmin(E))
+    assert clear > O
+
+
+def test_i4_reconstruction_beats_int3_and_rowwise_int4():
+    # one more bit per weight: lower error than int3-g64 on the same groups;
+    # group scales: lower error than per-row int4 on the outlier rows
+    W, _, rows = workloads.tiny()
+    O, I = W.shape
+    s4, c4, _ = oracle.quantize_g64_i4(W)
+    r4 = c4.astype(np.float64) * np.repeat(s4.astype(np.float64), 64, axis=1)[:, :I] - W
+    s3, c3, _ = oracle.quantize_g64(W)
+    r3 = c3.astype(np.float64) * np.repeat(s3.astype(np.float64), 64, axis=1)[:, :I] - W
+    rr = oracle.rowint_recon(W, 4) - W
+    rms = lambda a: float(np.sqrt(np.mean(a ** 2)))
+    assert rms(r4) < rms(r3)
+    assert rms(r4[rows]) < rms(rr[rows])
+
+
+@pytest.mark.parametrize("O,I", [(8, 64), (17, 100), (5, 7200)])
+def test_i4_matvec_f64_against_numpy(O, I):
+    W = workloads.generic_weights(O, I, seed=O * I)
+    s, c, _ = oracle.quantize_g64_i4(W)
+    p = oracle.pack_i4(c)
+    x = workloads.generic_vector(I, seed=I + 1)
+    y, a = oracle.matvec_i4_f64(p, s, O, I, x)
+    what = _np_decode_nibbles(p, O, I).astype(np.float64) * np.repeat(
+        s.astype(np.float64), 64, axis=1)[:, :I]
+    yr = what @ x.astype(np.float64)
+    ar = np.abs(what * x.astype(np.float64)[None, :]).sum(axis=1)
+    assert componentwise_err(y, yr, ar) < 1e-13
+    assert np.allclose(a, ar, rtol=1e-13, atol=0)
