@@ -14,6 +14,7 @@ namespace {
 
 using qt::kGroup;
 using qt::kGroupBytes;
+using qt::kGroupBytesI4;
 
 // Overflow-checked product a*b*c of non-negative sizes; -1 on overflow.
 int64_t mul3(int64_t a, int64_t b, int64_t c) {
@@ -31,9 +32,10 @@ bool overlap(const void* p, int64_t n, const void* q, int64_t m) {
     return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
 }
 
-qt_status shape_ok(int64_t O, int64_t I) {
+// gbytes: packed bytes per group (24 for int3, 32 for int4)
+qt_status shape_ok(int64_t O, int64_t I, int64_t gbytes = kGroupBytes) {
     if (O < 1 || I < 1 || I > QT_MAX_I) return QT_ERR_SHAPE;
-    if (mul3(O, (I + kGroup - 1) / kGroup, kGroupBytes) < 0 || mul3(O, I, 4) < 0)
+    if (mul3(O, (I + kGroup - 1) / kGroup, gbytes) < 0 || mul3(O, I, 4) < 0)
         return QT_ERR_SHAPE;
     return QT_OK;
 }
@@ -51,6 +53,12 @@ int64_t qt_groups(int64_t I) { return I < 1 ? 0 : (I + kGroup - 1) / kGroup; }
 int64_t qt_packed_bytes(int64_t O, int64_t I) {
     if (O < 1 || I < 1) return 0;
     const int64_t b = mul3(O, qt_groups(I), kGroupBytes);
+    return b < 0 ? 0 : b;
+}
+
+int64_t qt_packed_bytes_i4(int64_t O, int64_t I) {
+    if (O < 1 || I < 1) return 0;
+    const int64_t b = mul3(O, qt_groups(I), kGroupBytesI4);
     return b < 0 ? 0 : b;
 }
 
@@ -104,8 +112,9 @@ namespace {
 
 // Candidate factors: n_grid equally spaced points of [lo, hi], formed in
 // double and rounded once; the last one is hi itself.  n_grid == 0 is the
-// single plain absmax/4 scale (factor 1).
-int make_grid(int32_t n_grid, float lo, float hi, qt::GridTable& tab) {
+// single plain absmax/2^(b-1) scale (factor 1).  half = 2^(b-1): 4 for int3,
+// 8 for int4.
+int make_grid(int32_t n_grid, float lo, float hi, qt::GridTable& tab, double half = 4.0) {
     int ncand = 1;
     if (n_grid == 0) {
         tab.f[0] = 1.0f;
@@ -115,14 +124,14 @@ int make_grid(int32_t n_grid, float lo, float hi, qt::GridTable& tab) {
         for (int k = 0; k < n_grid; ++k) tab.f[k] = (float)((double)lo + (double)k * step);
         tab.f[n_grid - 1] = hi;
     }
-    // In a group with a normal base = absmax/4 and s = fl(base * f), every
-    // |w/s| stays below bound = 4/f * (1 + 2^-20).  The kernel accepts
+    // In a group with a normal base = absmax/half and s = fl(base * f), every
+    // |w/s| stays below bound = half/f * (1 + 2^-20).  The kernel accepts
     // rint(w * rcp(s)) when that quotient lies closer than margin to its
     // nearest integer, margin = 0.5 - 2^-21 * bound rounded toward zero: twice
     // the combined error of the reciprocal quotient and of fl(w/s).  Huge
     // quotient ranges get margin 0, which sends every lane to the division.
     for (int k = 0; k < ncand; ++k) {
-        const double bound = 4.0 / (double)tab.f[k] * (1.0 + 0x1p-20);
+        const double bound = half / (double)tab.f[k] * (1.0 + 0x1p-20);
         if (!(bound < 0x1p20)) {
             tab.margin[k] = 0.0f;
             continue;
@@ -140,7 +149,7 @@ int make_grid(int32_t n_grid, float lo, float hi, qt::GridTable& tab) {
 qt_status quantize_args_ok(const float* W, int64_t O, int64_t I, const float* d,
                            const float* scales, const int8_t* codes, const uint8_t* grid_idx) {
     if (!W || !scales || !codes) return QT_ERR_NULL;
-    qt_status st = shape_ok(O, I);
+    qt_status st = shape_ok(O, I, kGroupBytesI4);
     if (st != QT_OK) return st;
     if (!aligned(W, 4) || !aligned(scales, 4) || (d && !aligned(d, 4))) return QT_ERR_ALIGN;
     const int64_t G = qt_groups(I);
@@ -167,7 +176,20 @@ qt_status qt_quantize_g64(const float* W, int64_t O, int64_t I, const float* d, 
     if (n_grid != 0 && !grid_ok(lo, hi)) return QT_ERR_ARG;
     qt::GridTable tab{};
     const int ncand = make_grid(n_grid, lo, hi, tab);
-    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, 0, false, tab, scales, codes,
+    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, 0, false, 3, tab, scales, codes,
+                                            grid_idx, as_stream(stream)));
+}
+
+qt_status qt_quantize_g64_i4(const float* W, int64_t O, int64_t I, const float* d,
+                             int32_t n_grid, float lo, float hi, float* scales, int8_t* codes,
+                             uint8_t* grid_idx, void* stream) {
+    qt_status st = quantize_args_ok(W, O, I, d, scales, codes, grid_idx);
+    if (st != QT_OK) return st;
+    if (n_grid != 0 && (n_grid < 2 || n_grid > qt::kMaxGrid)) return QT_ERR_ARG;
+    if (n_grid != 0 && !grid_ok(lo, hi)) return QT_ERR_ARG;
+    qt::GridTable tab{};
+    const int ncand = make_grid(n_grid, lo, hi, tab, 8.0);
+    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, 0, false, 4, tab, scales, codes,
                                             grid_idx, as_stream(stream)));
 }
 
@@ -181,7 +203,7 @@ qt_status qt_quantize_g64_signed(const float* W, int64_t O, int64_t I, const flo
     if (!grid_ok(lo, hi)) return QT_ERR_ARG;
     qt::GridTable tab{};
     const int ncand = make_grid(n1, lo, hi, tab);
-    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, n2, true, tab, scales, codes,
+    return launched(qt::launch_quantize_g64(W, O, I, d, ncand, n2, true, 3, tab, scales, codes,
                                             nullptr, as_stream(stream)));
 }
 
@@ -194,19 +216,63 @@ qt_status qt_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed,
     return launched(qt::launch_pack_i3(codes, O, I, packed, as_stream(stream)));
 }
 
-qt_status qt_matvec_i3(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
-                       const float* x, float* y, void* stream) {
+qt_status qt_pack_i4(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed, void* stream) {
+    if (!codes || !packed) return QT_ERR_NULL;
+    qt_status st = shape_ok(O, I, kGroupBytesI4);
+    if (st != QT_OK) return st;
+    if (!aligned(packed, 16)) return QT_ERR_ALIGN;
+    if (overlap(packed, qt_packed_bytes_i4(O, I), codes, O * I)) return QT_ERR_ALIAS;
+    return launched(qt::launch_pack_i4(codes, O, I, packed, as_stream(stream)));
+}
+
+namespace {
+
+qt_status matvec_bits(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                      const float* x, float* y, void* stream, int bits) {
     if (!packed || !scales || !x || !y) return QT_ERR_NULL;
-    qt_status st = shape_ok(O, I);
+    const int64_t gbytes = bits == 3 ? kGroupBytes : kGroupBytesI4;
+    qt_status st = shape_ok(O, I, gbytes);
     if (st != QT_OK) return st;
     if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(x, 4) || !aligned(y, 4))
         return QT_ERR_ALIGN;
     const int64_t G = qt_groups(I);
-    if (overlap(y, O * 4, packed, O * G * kGroupBytes) || overlap(y, O * 4, scales, O * G * 4) ||
+    if (overlap(y, O * 4, packed, O * G * gbytes) || overlap(y, O * 4, scales, O * G * 4) ||
         overlap(y, O * 4, x, I * 4))
         return QT_ERR_ALIAS;
     return launched(qt::launch_gemv_batch(packed, scales, O, I, x, false, 1, y,
-                                          as_stream(stream)));
+                                          as_stream(stream), bits));
+}
+
+}  // namespace
+
+qt_status qt_matvec_i3(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                       const float* x, float* y, void* stream) {
+    return matvec_bits(packed, scales, O, I, x, y, stream, 3);
+}
+
+qt_status qt_matvec_i4(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                       const float* x, float* y, void* stream) {
+    return matvec_bits(packed, scales, O, I, x, y, stream, 4);
+}
+
+qt_status qt_matmul_i4(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                       const void* X, qt_dtype xt, int64_t B, float* Y, void* stream) {
+    if (!packed || !scales || !X || !Y) return QT_ERR_NULL;
+    if (xt != QT_F32 && xt != QT_BF16) return QT_ERR_DTYPE;
+    qt_status st = shape_ok(O, I, kGroupBytesI4);
+    if (st != QT_OK) return st;
+    if (B < 1) return QT_ERR_SHAPE;
+    const int64_t esz = xt == QT_F32 ? 4 : 2;
+    const int64_t xb = mul3(B, I, esz), yb = mul3(B, O, 4);
+    if (xb < 0 || yb < 0) return QT_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(Y, 4)) return QT_ERR_ALIGN;
+    if (!aligned(X, xt == QT_BF16 ? 16 : 4)) return QT_ERR_ALIGN;
+    const int64_t G = qt_groups(I);
+    if (overlap(Y, yb, packed, O * G * kGroupBytesI4) || overlap(Y, yb, scales, O * G * 4) ||
+        overlap(Y, yb, X, xb))
+        return QT_ERR_ALIAS;
+    return launched(qt::launch_gemv_batch(packed, scales, O, I, X, xt == QT_BF16, B, Y,
+                                          as_stream(stream), 4));
 }
 
 qt_status qt_matmul_i3(const uint8_t* packed, const float* scales, int64_t O, int64_t I,

@@ -1,11 +1,11 @@
-// int3-g64 dequantize-and-multiply on the vector ALUs: one or a few input rows
-// against a packed weight matrix, f32 throughout.
+// int3-g64 (and grouped int4) dequantize-and-multiply on the vector ALUs: one
+// or a few input rows against a packed weight matrix, f32 throughout.
 //
 // Semantics: the "int3-g64 (fmt=5)" pull request page, "Design", Kernel bullet
 // (matmul_i3: an exact-f32 path with per-group scale accumulation): for every
 // output row, each 64-input group's dot product of codes and inputs is formed
 // in f32, multiplied once by the group's f32 scale, and the groups are summed
-// in f32.
+// in f32.  Grouped int4 follows the same rule with 32-byte nibble groups.
 //
 // Layout on the GPU (gfx950, wave64):
 //  * A block owns RB = WAVES*64/LPR consecutive output rows; LPR lanes share a
@@ -21,7 +21,10 @@
 //    byte, ((L >> 2i) & 0x03030303) | (high bits at bit 2) gives four u = v+4
 //    values, one per byte; v_perm_b32 table lookups turn them into f16 pairs
 //    of v (exact), and v_fma_mix_f32 multiplies each by its f32 input with one
-//    f32 rounding.  Four interleaved accumulators per token hide FMA latency;
+//    f32 rounding.  int4 nibbles become f16 pairs by the 1024-bias trick: the
+//    f16 word 0x6400 | u is 1024 + u exactly, and one packed f16 subtraction
+//    of 1032 leaves v = u - 8.  Four interleaved accumulators per token hide
+//    FMA latency;
 //    the LPR partial row sums are combined by a fixed xor butterfly, so
 //    results are deterministic.
 #include <algorithm>
@@ -34,20 +37,37 @@ namespace {
 constexpr int kSlot = kGroup + 4;  // padded LDS floats per group
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-struct GroupBits {
+template <int BITS>
+struct GroupBits;
+template <>
+struct GroupBits<3> {
+    static constexpr int kBytes = kGroupBytes;
     u32x2_t a, b, c;  // low plane words 0..3, then the high plane
+};
+template <>
+struct GroupBits<4> {
+    static constexpr int kBytes = kGroupBytesI4;
+    u32x4_t a, b;  // nibble words 0..7: word w holds codes 8w..8w+7
 };
 
 // The weights are streamed once per call: non-temporal loads keep them from
 // displacing the staged inputs and scales in the caches.
-__device__ __forceinline__ GroupBits load_group(const uint8_t* __restrict__ p) {
-    const u32x2_t* q = reinterpret_cast<const u32x2_t*>(p);
-    GroupBits r;
-    r.a = __builtin_nontemporal_load(q + 0);
-    r.b = __builtin_nontemporal_load(q + 1);
-    r.c = __builtin_nontemporal_load(q + 2);
+template <int BITS>
+__device__ __forceinline__ GroupBits<BITS> load_group(const uint8_t* __restrict__ p) {
+    GroupBits<BITS> r;
+    if constexpr (BITS == 3) {
+        const u32x2_t* q = reinterpret_cast<const u32x2_t*>(p);
+        r.a = __builtin_nontemporal_load(q + 0);
+        r.b = __builtin_nontemporal_load(q + 1);
+        r.c = __builtin_nontemporal_load(q + 2);
+    } else {
+        const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+        r.a = __builtin_nontemporal_load(q + 0);
+        r.b = __builtin_nontemporal_load(q + 1);
+    }
     return r;
 }
 
@@ -86,22 +106,66 @@ __device__ __forceinline__ void quarter_fma(uint32_t L, uint32_t sp4, const floa
     }
 }
 
+// v_and_or_b32: (a & m) | c in one instruction.  gfx950's three-operand
+// encoding takes no literal constants, so the compiler splits a constant mask
+// and bias into two literal-operand instructions; here they come in registers.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
+}
+
+// acc[t][i] += v(code 8w+i) * x_t[8w+i] + v(code 8w+4+i) * x_t[8w+4+i] for
+// one int4 word w (nibble n = code 8w+n, so the two 16-bit halves hold codes
+// 8w..8w+3 and 8w+4..8w+7).  A nibble at bits 0..3 of a half or-ed into the
+// f16 word 0x6400 (1024, ulp 1) gives 1024 + u; a nibble at bits 4..7 or-ed
+// into 0x5400 (64, ulp 1/16) gives 64 + u.  Both are exact, and so is the
+// packed f16 subtraction of 1032 or 72 that leaves v = u - 8.
+template <int T, int NT>
+__device__ __forceinline__ void word_fma_i4(uint32_t W, const float* const* xq, int w,
+                                            float (&acc)[T][4]) {
+    const uint32_t lo_bias = 0x64006400u, hi_bias = 0x54005400u;
+    const half2_t lo_off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2_t hi_off = {(_Float16)72.0f, (_Float16)72.0f};
+    const uint32_t W8 = W >> 8;
+    half2_t p[4];
+    p[0] = __builtin_bit_cast(half2_t, and_or(W, 0x000F000Fu, lo_bias)) - lo_off;
+    p[1] = __builtin_bit_cast(half2_t, and_or(W, 0x00F000F0u, hi_bias)) - hi_off;
+    p[2] = __builtin_bit_cast(half2_t, and_or(W8, 0x000F000Fu, lo_bias)) - lo_off;
+    p[3] = __builtin_bit_cast(half2_t, and_or(W8, 0x00F000F0u, hi_bias)) - hi_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float* x = xq[t] + 8 * w + i;
+            acc[t][i] = __builtin_fmaf((float)p[i].x, x[0], acc[t][i]);
+            acc[t][i] = __builtin_fmaf((float)p[i].y, x[4], acc[t][i]);
+        }
+    }
+}
+
 // Dot of one packed group with the first NT staged input groups: adds, per
 // token, scale * sum_j v_j x_j into rowacc[t].
-template <int T, int NT>
-__device__ __forceinline__ void group_dot(const GroupBits& gb, float scale,
+template <int T, int NT, int BITS>
+__device__ __forceinline__ void group_dot(const GroupBits<BITS>& gb, float scale,
                                           const float* const* xg, float (&rowacc)[T]) {
     float acc[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-    const uint32_t L[4] = {gb.a.x, gb.a.y, gb.b.x, gb.b.y};
-    const uint32_t H[2] = {gb.c.x, gb.c.y};
+    if constexpr (BITS == 3) {
+        const uint32_t L[4] = {gb.a.x, gb.a.y, gb.b.x, gb.b.y};
+        const uint32_t H[2] = {gb.c.x, gb.c.y};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t h16 = (H[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-        quarter_fma<T, NT>(L[k], spread_hi(h16), xg, k, acc);
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t h16 = (H[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+            quarter_fma<T, NT>(L[k], spread_hi(h16), xg, k, acc);
+        }
+    } else {
+        const uint32_t Wd[8] = {gb.a.x, gb.a.y, gb.a.z, gb.a.w, gb.b.x, gb.b.y, gb.b.z, gb.b.w};
+#pragma unroll
+        for (int w = 0; w < 8; ++w) word_fma_i4<T, NT>(Wd[w], xg, w, acc);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -112,18 +176,18 @@ __device__ __forceinline__ void group_dot(const GroupBits& gb, float scale,
 
 // Dispatch on the number of live tokens of a tile (uniform over the block), so
 // that no multiply is spent on tokens that are not there.
-template <int T>
-__device__ __forceinline__ void group_dot_n(int nt, const GroupBits& gb, float scale,
+template <int T, int BITS>
+__device__ __forceinline__ void group_dot_n(int nt, const GroupBits<BITS>& gb, float scale,
                                             const float* const* xg, float (&rowacc)[T]) {
     if constexpr (T == 1) {
-        group_dot<T, 1>(gb, scale, xg, rowacc);
+        group_dot<T, 1, BITS>(gb, scale, xg, rowacc);
     } else {
         switch (nt) {
-            case 1: group_dot<T, 1>(gb, scale, xg, rowacc); break;
-            case 2: if constexpr (T >= 2) group_dot<T, 2>(gb, scale, xg, rowacc); break;
-            case 3: if constexpr (T >= 3) group_dot<T, 3>(gb, scale, xg, rowacc); break;
-            case 4: if constexpr (T >= 4) group_dot<T, 4>(gb, scale, xg, rowacc); break;
-            default: group_dot<T, T>(gb, scale, xg, rowacc); break;
+            case 1: group_dot<T, 1, BITS>(gb, scale, xg, rowacc); break;
+            case 2: if constexpr (T >= 2) group_dot<T, 2, BITS>(gb, scale, xg, rowacc); break;
+            case 3: if constexpr (T >= 3) group_dot<T, 3, BITS>(gb, scale, xg, rowacc); break;
+            case 4: if constexpr (T >= 4) group_dot<T, 4, BITS>(gb, scale, xg, rowacc); break;
+            default: group_dot<T, T, BITS>(gb, scale, xg, rowacc); break;
         }
     }
 }
@@ -221,7 +285,7 @@ struct InputStage {
 // Rows [r0, r0+RB) of one matrix against the tokens listed in tok_rows
 // (input row of each token) / tok_outs (output row of each token, -1 = do not
 // store), T tokens per pass over the weights.
-template <int LPR, int WAVES, int T, bool BF16, bool VEC>
+template <int LPR, int WAVES, int T, bool BF16, bool VEC, int BITS>
 __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __restrict__ scales,
                           int64_t O, int64_t I, int64_t G, const void* __restrict__ X,
                           const int32_t* tok_rows, const int32_t* tok_outs, int ntok,
@@ -249,14 +313,14 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
             stage.load(X, tok_rows + tt, nt, I, g0, gn);
             // weight loads, branch-free: idle lanes load group 0 of the block's
             // first row (always valid) and are not used
-            GroupBits gb[NG];
+            GroupBits<BITS> gb[NG];
             float sc[NG];
 #pragma unroll
             for (int m = 0; m < NG; ++m) {
                 const int gl = q + m * LPR;
                 const bool ok = row_ok && gl < gn;
                 const int64_t gi = ok ? r * G + g0 + gl : r0 * G;
-                gb[m] = load_group(packed + gi * kGroupBytes);
+                gb[m] = load_group<BITS>(packed + gi * GroupBits<BITS>::kBytes);
                 sc[m] = scales[gi];
             }
             stage.store(nt, xs);
@@ -268,7 +332,7 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
                     const float* xg[T];
 #pragma unroll
                     for (int t = 0; t < T; ++t) xg[t] = xs + (t * GC + gl) * kSlot;
-                    group_dot_n<T>(nt, gb[m], sc[m], xg, rowacc);
+                    group_dot_n<T, BITS>(nt, gb[m], sc[m], xg, rowacc);
                 }
             }
         }
@@ -318,7 +382,7 @@ constexpr size_t lds_bytes() {
 // ---------------------------------------------------------------- kernels
 constexpr int kMaxTok = 16;  // token rows per launch chunk of the batch kernel
 
-template <int LPR, int WAVES, int T, bool BF16, bool VEC>
+template <int LPR, int WAVES, int T, bool BF16, bool VEC, int BITS>
 __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
     int64_t G, const void* __restrict__ X, int64_t tok0, int ntok, float* __restrict__ Y) {
@@ -327,15 +391,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
     if (threadIdx.x < kMaxTok) rows[threadIdx.x] = (int32_t)(tok0 + threadIdx.x);
     __syncthreads();
     constexpr int RB = WAVES * 64 / LPR;
-    gemv_rows<LPR, WAVES, T, BF16, VEC>(packed, scales, O, I, G, X, rows, rows, ntok, Y,
-                                        (int64_t)blockIdx.x * RB, lds);
+    gemv_rows<LPR, WAVES, T, BF16, VEC, BITS>(packed, scales, O, I, G, X, rows, rows, ntok, Y,
+                                              (int64_t)blockIdx.x * RB, lds);
 }
 
 }  // namespace
 
 // Decode and small batches.  LPR/WAVES chosen so that O/RB blocks cover the
 // chip; tokens in tiles of T per pass over the weights.
-template <int LPR, int WAVES, int T, bool BF16, bool VEC>
+template <int LPR, int WAVES, int T, bool BF16, bool VEC, int BITS>
 static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
                             const void* X, int64_t ntok, float* Y, hipStream_t s) {
     const int64_t G = (I + kGroup - 1) / kGroup;
@@ -343,35 +407,44 @@ static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t 
     const int64_t blocks = (O + RB - 1) / RB;
     for (int64_t t0 = 0; t0 < ntok; t0 += kMaxTok) {
         const int n = (int)std::min<int64_t>(kMaxTok, ntok - t0);
-        hipLaunchKernelGGL((gemv_batch_kernel<LPR, WAVES, T, BF16, VEC>), dim3((unsigned)blocks),
-                           dim3(WAVES * 64), lds_bytes<T>(), s, packed, scales, O, I, G, X, t0, n,
-                           Y);
+        hipLaunchKernelGGL((gemv_batch_kernel<LPR, WAVES, T, BF16, VEC, BITS>),
+                           dim3((unsigned)blocks), dim3(WAVES * 64), lds_bytes<T>(), s, packed,
+                           scales, O, I, G, X, t0, n, Y);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int BITS>
 static hipError_t batch_dispatch(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
                                  const void* X, int64_t ntok, float* Y, hipStream_t s) {
-    if (ntok == 1) return run_batch<64, 8, 1, BF16, VEC>(packed, scales, O, I, X, 1, Y, s);
-    if (ntok == 2) return run_batch<32, 4, 2, BF16, VEC>(packed, scales, O, I, X, 2, Y, s);
-    if (ntok <= 4) return run_batch<16, 4, 4, BF16, VEC>(packed, scales, O, I, X, ntok, Y, s);
-    return run_batch<16, 4, 8, BF16, VEC>(packed, scales, O, I, X, ntok, Y, s);
+    if (ntok == 1) return run_batch<64, 8, 1, BF16, VEC, BITS>(packed, scales, O, I, X, 1, Y, s);
+    if (ntok == 2) return run_batch<32, 4, 2, BF16, VEC, BITS>(packed, scales, O, I, X, 2, Y, s);
+    if (ntok <= 4)
+        return run_batch<16, 4, 4, BF16, VEC, BITS>(packed, scales, O, I, X, ntok, Y, s);
+    return run_batch<16, 4, 8, BF16, VEC, BITS>(packed, scales, O, I, X, ntok, Y, s);
 }
 
-hipError_t launch_gemv_batch(const uint8_t* packed, const float* scales, int64_t O,
-                             int64_t I, const void* X, bool bf16, int64_t ntok, float* Y,
-                             hipStream_t s) {
+template <int BITS>
+static hipError_t gemv_bits(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                            const void* X, bool bf16, int64_t ntok, float* Y, hipStream_t s) {
     // 16-byte (f32) or 8-byte (bf16) input loads need aligned rows
     const uintptr_t al = bf16 ? 8 : 16;
     const bool vec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & (al - 1)) == 0);
     if (bf16)
-        return vec ? batch_dispatch<true, true>(packed, scales, O, I, X, ntok, Y, s)
-                   : batch_dispatch<true, false>(packed, scales, O, I, X, ntok, Y, s);
-    return vec ? batch_dispatch<false, true>(packed, scales, O, I, X, ntok, Y, s)
-               : batch_dispatch<false, false>(packed, scales, O, I, X, ntok, Y, s);
+        return vec ? batch_dispatch<true, true, BITS>(packed, scales, O, I, X, ntok, Y, s)
+                   : batch_dispatch<true, false, BITS>(packed, scales, O, I, X, ntok, Y, s);
+    return vec ? batch_dispatch<false, true, BITS>(packed, scales, O, I, X, ntok, Y, s)
+               : batch_dispatch<false, false, BITS>(packed, scales, O, I, X, ntok, Y, s);
+}
+
+hipError_t launch_gemv_batch(const uint8_t* packed, const float* scales, int64_t O,
+                             int64_t I, const void* X, bool bf16, int64_t ntok, float* Y,
+                             hipStream_t s, int bits) {
+    if (bits == 3) return gemv_bits<3>(packed, scales, O, I, X, bf16, ntok, Y, s);
+    if (bits == 4) return gemv_bits<4>(packed, scales, O, I, X, bf16, ntok, Y, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace qt

@@ -7,7 +7,8 @@
 namespace qt {
 
 constexpr int kGroup = 64;       // inputs per group
-constexpr int kGroupBytes = 24;  // 16 B low plane + 8 B high plane
+constexpr int kGroupBytes = 24;  // int3: 16 B low plane + 8 B high plane
+constexpr int kGroupBytesI4 = 32;  // int4: 64 nibbles
 constexpr int kMaxGrid = 256;    // largest candidate grid of the scale search
 
 // Candidate factors of the scale search, passed by value as a kernel argument.
@@ -20,20 +21,23 @@ struct GridTable {
 };
 
 // ncand candidates of tab; signed_search: the two-stage signed search with n2
-// second-stage points (0: stage 1 only).
+// second-stage points (0: stage 1 only; int3 only).  bits: 3 or 4.
 hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
-                               int ncand, int n2, bool signed_search, const GridTable& tab,
-                               float* scales, int8_t* codes, uint8_t* grid_idx,
-                               hipStream_t s);
+                               int ncand, int n2, bool signed_search, int bits,
+                               const GridTable& tab, float* scales, int8_t* codes,
+                               uint8_t* grid_idx, hipStream_t s);
 
 hipError_t launch_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed,
+                          hipStream_t s);
+hipError_t launch_pack_i4(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed,
                           hipStream_t s);
 
 // Dequantize-multiply of `ntok` input rows against one O x I matrix, exact-f32
 // path.  X rows are f32 (bf16 == false) or bf16 bit patterns (bf16 == true).
+// bits: 3 (24-byte int3 groups) or 4 (32-byte int4 groups).
 hipError_t launch_gemv_batch(const uint8_t* packed, const float* scales, int64_t O,
                              int64_t I, const void* X, bool bf16, int64_t ntok,
-                             float* Y, hipStream_t s);
+                             float* Y, hipStream_t s, int bits = 3);
 
 hipError_t launch_gemv_grouped(const uint8_t* packed, const float* scales, int32_t E,
                                int64_t O, int64_t I, const float* X, int64_t n_x_rows,

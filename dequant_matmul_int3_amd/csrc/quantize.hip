@@ -1,10 +1,13 @@
-// Per-group scale search, code emission and bit-plane packing for int3-g64.
+// Per-group scale search, code emission and packing for int3-g64 and grouped
+// int4.
 //
 // Method: the "int3-g64 (fmt=5)" pull request page ("Why this format" item 1:
 // a 3-bit group-64 absmax quantizer; "Design", Layout bullet: 24 bytes per
 // group, codes in [-4,3] stored as v+4) and the NeUQI accuracy page (first
 // paragraph: candidate scales searched on a grid, weighted by activation
-// importance).  Every f32 operation of the objective is a separately rounded
+// importance).  Grouped int4 (the grouped-int4 format of the int3-g64 page,
+// "Design" and the OLMoE per-projection table) is the same quantizer with
+// b = 4: base absmax/8, codes in [-8,7], stored as nibbles of v+8.  Every f32 operation of the objective is a separately rounded
 // operation (this file is compiled without floating-point contraction), and
 // the 64 slot errors are summed by halving, so the chosen candidate is a
 // bit-exact function of the inputs.
@@ -16,12 +19,24 @@ namespace {
 constexpr int kLanesPerGroup = 16;  // a quarter wave owns one group
 constexpr int kQuantBlock = 256;    // 16 groups per block
 
-// q = clamp(rne(fl(w / s)), -4, 3), 0 when s == 0, where fl(w / s) is the
+// The b-bit symmetric group quantizer: base = absmax * 2^-(b-1), codes v in
+// [-2^(b-1), 2^(b-1) - 1].  With base normal, 2^(b-1) * base == absmax exactly.
+template <int BITS>
+struct Range {
+    static_assert(BITS == 3 || BITS == 4, "int3 or int4 codes");
+    static constexpr float kHalf = (float)(1 << (BITS - 1));  // 4 or 8
+    static constexpr float kLo = -kHalf;
+    static constexpr float kHi = kHalf - 1.0f;
+    static constexpr float kBase = 1.0f / kHalf;  // exact power of two
+};
+
+// q = clamp(rne(fl(w / s)), lo, hi), 0 when s == 0, where fl(w / s) is the
 // correctly rounded f32 quotient.
+template <int BITS>
 __device__ __forceinline__ float code_of(float w, float s) {
     if (s == 0.0f) return 0.0f;
     float q = __builtin_rintf(w / s);
-    return fminf(fmaxf(q, -4.0f), 3.0f);
+    return fminf(fmaxf(q, Range<BITS>::kLo), Range<BITS>::kHi);
 }
 
 // One halving step of the slot errors: lane l (l < m) of a 16-lane row adds
@@ -40,7 +55,7 @@ __device__ __forceinline__ float add_from_lane_plus(float a) {
 // |y - rint(y)| < margin, fl(w/s) rounds to the same integer as y.  Lanes
 // outside the margin, and groups whose scales leave [2^-100, 2^100], take the
 // correctly rounded division instead.
-template <bool WEIGHTED>
+template <bool WEIGHTED, int BITS>
 __device__ __forceinline__ float candidate_error(const float (&wv)[4], const float (&dv)[4],
                                                  float s, float margin, bool s_ok) {
     const float r = __builtin_amdgcn_rcpf(s);
@@ -59,7 +74,7 @@ __device__ __forceinline__ float candidate_error(const float (&wv)[4], const flo
     float e4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float qc = __builtin_amdgcn_fmed3f(q[e], -4.0f, 3.0f);
+        const float qc = __builtin_amdgcn_fmed3f(q[e], Range<BITS>::kLo, Range<BITS>::kHi);
         const float t = s * qc;
         const float rr = wv[e] - t;
         const float r2 = rr * rr;
@@ -81,7 +96,7 @@ __device__ __forceinline__ float candidate_error(const float (&wv)[4], const flo
 // Lane l of a quarter wave holds slots l, l+16, l+32, l+48 of its group, so
 // the first two halving steps (m = 32, 16) are lane-local and the remaining
 // four (m = 8, 4, 2, 1) read the partner lane l + m through DPP.
-template <bool WEIGHTED>
+template <bool WEIGHTED, int BITS>
 __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
     const float* __restrict__ W, int64_t n_groups, int32_t I, int32_t G,
     const float* __restrict__ d, int32_t ncand, GridTable tab,
@@ -112,10 +127,10 @@ __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
     }
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kLanesPerGroup));
-    const float base = amax * 0.25f;
-    // base normal: then 4 * base == amax exactly and every |w| <= 4 * base
-    // s = fl(base * f) is monotone in f, so the range check of the
-    // smallest and largest factor covers every candidate
+    const float base = amax * Range<BITS>::kBase;
+    // base normal: then 2^(b-1) * base == amax exactly and every |w| <=
+    // 2^(b-1) * base; s = fl(base * f) is monotone in f, so the range check
+    // of the smallest and largest factor covers every candidate
     const bool group_ok = base >= 0x1p-125f && base * tab.fmin >= 0x1p-100f &&
                           base * tab.fmax <= 0x1p100f;
 
@@ -124,7 +139,7 @@ __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
 #pragma unroll 2
     for (int k = 0; k < ncand; ++k) {
         const float s = base * tab.f[k];
-        const float a = candidate_error<WEIGHTED>(wv, dv, s, tab.margin[k], group_ok);
+        const float a = candidate_error<WEIGHTED, BITS>(wv, dv, s, tab.margin[k], group_ok);
         if (k == 0 || a < best_e) {  // strict: the lowest k wins ties
             best_e = a;
             best_k = k;
@@ -136,7 +151,7 @@ __global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int j = l + 16 * e;
-        if (j < n) codes[o * (int64_t)I + c0 + j] = (int8_t)(int)code_of(wv[e], s);
+        if (j < n) codes[o * (int64_t)I + c0 + j] = (int8_t)(int)code_of<BITS>(wv[e], s);
     }
     if (l == 0) {
         scales[grp] = s;
@@ -159,7 +174,7 @@ enum QuotientMode { kReciprocal, kDivision };
 // kReciprocal mode the codes come from y = fl(w * r), r = rcp(s), and *dev
 // receives the largest |y - rint(y)| for the exactness check; kDivision uses
 // the correctly rounded quotient (0 when s == 0).
-template <bool WEIGHTED, int MODE>
+template <bool WEIGHTED, int MODE, int BITS>
 __device__ __forceinline__ float group_error(const float (&w)[kGroup], const float (&dj)[kGroup],
                                              float s, float r, float* dev) {
     float a[32];
@@ -178,7 +193,7 @@ __device__ __forceinline__ float group_error(const float (&w)[kGroup], const flo
             } else {
                 q = s == 0.0f ? 0.0f : __builtin_rintf(w[jj] / s);
             }
-            const float qc = __builtin_amdgcn_fmed3f(q, -4.0f, 3.0f);
+            const float qc = __builtin_amdgcn_fmed3f(q, Range<BITS>::kLo, Range<BITS>::kHi);
             const float t = s * qc;
             const float rr = w[jj] - t;
             const float r2 = rr * rr;
@@ -195,11 +210,12 @@ __device__ __forceinline__ float group_error(const float (&w)[kGroup], const flo
 }
 
 // Exactness margin for a factor f computed on the device (the second stage of
-// the signed search): the host's bound 4/f (1 + 2^-20) with extra slack that
-// covers the f32 rounding of this formula; a smaller margin only sends more
-// candidates to the division.
+// the signed search): the host's bound 2^(b-1)/f (1 + 2^-20) with extra slack
+// that covers the f32 rounding of this formula; a smaller margin only sends
+// more candidates to the division.
+template <int BITS>
 __device__ __forceinline__ float device_margin(float f) {
-    const float bound = 4.0f / f * 1.001f;
+    const float bound = Range<BITS>::kHalf / f * 1.001f;
     return bound < 0x1p20f ? 0.5f - bound * 0x1p-21f : 0.0f;
 }
 
@@ -208,7 +224,7 @@ __device__ __forceinline__ float device_margin(float f) {
 // n2 points of [f_{k-1}, f_{k+1}] around the stage-1 winner k with its sign,
 // formed in double exactly as the grid itself; the final choice is the strict
 // minimum over [stage-1 winner, stage-2 points], so ties keep the earlier one.
-template <bool WEIGHTED, bool SIGNED>
+template <bool WEIGHTED, bool SIGNED, int BITS>
 __global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
     const float* __restrict__ W, int64_t O, int32_t I, int32_t G,
     const float* __restrict__ d, int32_t ncand, int32_t n2, GridTable tab, int vec,
@@ -243,8 +259,9 @@ __global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) amax = fmaxf(amax, fabsf(w[j]));
-    const float base = amax * 0.25f;
-    // base normal: 4 * base == amax exactly, so every |w| <= 4 * base; and
+    const float base = amax * Range<BITS>::kBase;
+    // base normal: 2^(b-1) * base == amax exactly, so every |w| <= 2^(b-1) *
+    // base; and
     // s = fl(base * f) is monotone in f, so checking the smallest and the
     // largest factor covers every candidate
     const bool group_ok = base >= 0x1p-125f && base * tab.fmin >= 0x1p-100f &&
@@ -255,9 +272,9 @@ __global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
     auto error_of = [&](float s, float margin) {
         const float r = __builtin_amdgcn_rcpf(s);
         float dev;
-        float a = group_error<WEIGHTED, kReciprocal>(w, dj, s, r, &dev);
+        float a = group_error<WEIGHTED, kReciprocal, BITS>(w, dj, s, r, &dev);
         if (!(group_ok && dev < margin))  // rare: some quotient near a half-integer
-            a = group_error<WEIGHTED, kDivision>(w, dj, s, r, nullptr);
+            a = group_error<WEIGHTED, kDivision, BITS>(w, dj, s, r, nullptr);
         return a;
     };
     float best_e = 0.0f, best_s = 0.0f, best_margin = 0.0f;
@@ -294,7 +311,7 @@ __global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
                 const float f = j == n2 - 1 ? fb : (float)((double)fa + (double)j * step);
                 const float mag = base * f;
                 const float s = neg ? -mag : mag;
-                const float margin = device_margin(f);
+                const float margin = device_margin<BITS>(f);
                 const float a = error_of(s, margin);
                 if (a < best_e) {
                     best_e = a;
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(kSearchRows) void search_g64_kernel(
             float q = __builtin_rintf(y);
             if (!(group_ok && fabsf(y - q) < best_margin))
                 q = s == 0.0f ? 0.0f : __builtin_rintf(w[j] / s);
-            const int v = (int)__builtin_amdgcn_fmed3f(q, -4.0f, 3.0f);
+            const int v = (int)__builtin_amdgcn_fmed3f(q, Range<BITS>::kLo, Range<BITS>::kHi);
             word |= ((uint32_t)v & 0xFFu) << (8 * b);
         }
         packed4[c] = word;
@@ -397,12 +414,69 @@ __global__ __launch_bounds__(256) void pack_i3_kernel(const int8_t* __restrict__
     dst[2] = make_uint2(hi[0], hi[1]);
 }
 
-}  // namespace
+// One thread per group: 64 codes in, 32 packed bytes out (two 16-byte
+// stores; groups start on 32-byte boundaries).  Slot j goes to the low nibble
+// of byte j/2 when j is even, to the high nibble when j is odd, as u = v + 8;
+// padding holds u = 8.
+__global__ __launch_bounds__(256) void pack_i4_kernel(const int8_t* __restrict__ codes,
+                                                       int64_t n_groups, int32_t I, int32_t G,
+                                                       int vec16, uint8_t* __restrict__ packed) {
+    const int64_t grp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (grp >= n_groups) return;
+    const int64_t o = grp / G;
+    const int32_t g = (int32_t)(grp - o * G);
+    const int32_t c0 = g * kGroup;
+    const int32_t n = min(kGroup, I - c0);
+    const int8_t* src = codes + o * (int64_t)I + c0;
 
-hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
-                               int ncand, int n2, bool signed_search, const GridTable& tab,
-                               float* scales, int8_t* codes, uint8_t* grid_idx,
-                               hipStream_t s) {
+    uint32_t c[16];  // 64 codes, 4 per word, little-endian bytes; padding v = 0
+    if (vec16 && n == kGroup) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = s4[q];
+            c[4 * q + 0] = v.x;
+            c[4 * q + 1] = v.y;
+            c[4 * q + 2] = v.z;
+            c[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            uint32_t wv = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int j = 4 * q + b;
+                const uint32_t byte = j < n ? (uint8_t)src[j] : 0u;
+                wv |= byte << (8 * b);
+            }
+            c[q] = wv;
+        }
+    }
+    uint32_t out[8];
+#pragma unroll
+    for (int q = 0; q < 16; q += 2) {
+        uint32_t h[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            // u = (v + 8) mod 16 in every byte: flipping bit 3 of the low four
+            // bits of v; then bytes (u0, u1, u2, u3) -> half-word u0 | u1 << 4
+            // | u2 << 8 | u3 << 12
+            const uint32_t u = (c[q + k] & 0x0F0F0F0Fu) ^ 0x08080808u;
+            const uint32_t t = u | (u >> 4);  // byte 0: u0 | u1 << 4, byte 2: u2 | u3 << 4
+            h[k] = (t & 0xFFu) | ((t >> 8) & 0xFF00u);
+        }
+        out[q >> 1] = h[0] | (h[1] << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(packed + grp * kGroupBytesI4);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+template <int BITS>
+hipError_t quantize_bits(const float* W, int64_t O, int64_t I, const float* d, int ncand,
+                         int n2, bool signed_search, const GridTable& tab, float* scales,
+                         int8_t* codes, uint8_t* grid_idx, hipStream_t s) {
     const int64_t G = (I + kGroup - 1) / kGroup;
     if (ncand > 1 || signed_search) {
         // lane-per-group search: blocks = G * ceil(O / 64)
@@ -411,15 +485,19 @@ hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float
         const int vec = (w16 && I % 4 == 0) ? ((c16 && I % 16 == 0) ? 2 : 1) : 0;
         const int64_t blocks = G * ((O + kSearchRows - 1) / kSearchRows);
         if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-#define QT_SEARCH(WT, SG)                                                                    \
-    hipLaunchKernelGGL((search_g64_kernel<WT, SG>), dim3((unsigned)blocks), dim3(kSearchRows), \
-                       0, s, W, O, (int32_t)I, (int32_t)G, d, ncand, n2, tab, vec, scales,   \
-                       codes, grid_idx)
+#define QT_SEARCH(WT, SG)                                                                \
+    hipLaunchKernelGGL((search_g64_kernel<WT, SG, BITS>), dim3((unsigned)blocks),          \
+                       dim3(kSearchRows), 0, s, W, O, (int32_t)I, (int32_t)G, d, ncand, n2, \
+                       tab, vec, scales, codes, grid_idx)
         if (signed_search) {
-            if (d)
-                QT_SEARCH(true, true);
-            else
-                QT_SEARCH(false, true);
+            if constexpr (BITS == 3) {
+                if (d)
+                    QT_SEARCH(true, true);
+                else
+                    QT_SEARCH(false, true);
+            } else {
+                return hipErrorInvalidValue;  // the signed search is int3 only
+            }
         } else {
             if (d)
                 QT_SEARCH(true, false);
@@ -433,14 +511,29 @@ hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float
     const int64_t per_block = kQuantBlock / kLanesPerGroup;
     const int64_t blocks = (n_groups + per_block - 1) / per_block;
     if (d)
-        hipLaunchKernelGGL(quantize_g64_kernel<true>, dim3((unsigned)blocks), dim3(kQuantBlock), 0,
-                           s, W, n_groups, (int32_t)I, (int32_t)G, d, ncand, tab, scales, codes,
-                           grid_idx);
+        hipLaunchKernelGGL((quantize_g64_kernel<true, BITS>), dim3((unsigned)blocks),
+                           dim3(kQuantBlock), 0, s, W, n_groups, (int32_t)I, (int32_t)G, d, ncand,
+                           tab, scales, codes, grid_idx);
     else
-        hipLaunchKernelGGL(quantize_g64_kernel<false>, dim3((unsigned)blocks), dim3(kQuantBlock), 0,
-                           s, W, n_groups, (int32_t)I, (int32_t)G, d, ncand, tab, scales, codes,
-                           grid_idx);
+        hipLaunchKernelGGL((quantize_g64_kernel<false, BITS>), dim3((unsigned)blocks),
+                           dim3(kQuantBlock), 0, s, W, n_groups, (int32_t)I, (int32_t)G, d, ncand,
+                           tab, scales, codes, grid_idx);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_g64(const float* W, int64_t O, int64_t I, const float* d,
+                               int ncand, int n2, bool signed_search, int bits,
+                               const GridTable& tab, float* scales, int8_t* codes,
+                               uint8_t* grid_idx, hipStream_t s) {
+    if (bits == 3)
+        return quantize_bits<3>(W, O, I, d, ncand, n2, signed_search, tab, scales, codes,
+                                grid_idx, s);
+    if (bits == 4)
+        return quantize_bits<4>(W, O, I, d, ncand, n2, signed_search, tab, scales, codes,
+                                grid_idx, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed,
@@ -450,6 +543,17 @@ hipError_t launch_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* pa
     const int vec16 = ((reinterpret_cast<uintptr_t>(codes) & 15) == 0) && (I % 16 == 0);
     const int64_t blocks = (n_groups + 255) / 256;
     hipLaunchKernelGGL(pack_i3_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes,
+                       n_groups, (int32_t)I, (int32_t)G, vec16, packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_i4(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed,
+                          hipStream_t s) {
+    const int64_t G = (I + kGroup - 1) / kGroup;
+    const int64_t n_groups = O * G;
+    const int vec16 = ((reinterpret_cast<uintptr_t>(codes) & 15) == 0) && (I % 16 == 0);
+    const int64_t blocks = (n_groups + 255) / 256;
+    hipLaunchKernelGGL(pack_i4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes,
                        n_groups, (int32_t)I, (int32_t)G, vec16, packed);
     return hipGetLastError();
 }

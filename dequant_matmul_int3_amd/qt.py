@@ -40,6 +40,15 @@ _SIGS = {
     "qt_matvec_i3_grouped": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
                                        C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
                                        C.c_void_p, C.c_void_p]),
+    "qt_packed_bytes_i4": (C.c_int64, [C.c_int64, C.c_int64]),
+    "qt_quantize_g64_i4": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
+                                     C.c_float, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p]),
+    "qt_pack_i4": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]),
+    "qt_matvec_i4": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
+                               C.c_void_p, C.c_void_p]),
+    "qt_matmul_i4": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
+                               C.c_int, C.c_int64, C.c_void_p, C.c_void_p]),
 }
 
 
@@ -127,10 +136,11 @@ def qt_hessian_diag(X, d=None, accumulate: bool = False, workspace=None, stream=
     return d
 
 
-def qt_quantize_g64(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0,
-                    scales=None, codes=None, grid_idx=None, want_grid_idx: bool = True,
-                    stream=None):
-    """W [O, I] f32 -> (scales [O, G] f32, codes [O, I] int8, grid_idx [O, G] uint8 or None)."""
+def qt_packed_bytes_i4(O: int, I: int) -> int:
+    return int(lib().qt_packed_bytes_i4(O, I))
+
+
+def _quantize(name, W, d, n_grid, lo, hi, scales, codes, grid_idx, want_grid_idx, stream):
     O, I = W.shape
     G = qt_groups(I)
     if scales is None:
@@ -142,10 +152,25 @@ def qt_quantize_g64(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0
     dev = _dev(W, d, scales, codes, grid_idx)
     if W.dtype != torch.float32 or (d is not None and d.dtype != torch.float32):
         raise ValueError("W and d must be float32")
-    _check(lib().qt_quantize_g64(_ptr(W), O, I, _ptr(d), n_grid, lo, hi, _ptr(scales),
-                                 _ptr(codes), _ptr(grid_idx), _stream(stream, dev)),
-           "qt_quantize_g64")
+    _check(getattr(lib(), name)(_ptr(W), O, I, _ptr(d), n_grid, lo, hi, _ptr(scales),
+                                _ptr(codes), _ptr(grid_idx), _stream(stream, dev)), name)
     return scales, codes, grid_idx
+
+
+def qt_quantize_g64(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0,
+                    scales=None, codes=None, grid_idx=None, want_grid_idx: bool = True,
+                    stream=None):
+    """W [O, I] f32 -> (scales [O, G] f32, codes [O, I] int8, grid_idx [O, G] uint8 or None)."""
+    return _quantize("qt_quantize_g64", W, d, n_grid, lo, hi, scales, codes, grid_idx,
+                     want_grid_idx, stream)
+
+
+def qt_quantize_g64_i4(W, d=None, n_grid: int = 0, lo: float = 0.5, hi: float = 1.0,
+                       scales=None, codes=None, grid_idx=None, want_grid_idx: bool = True,
+                       stream=None):
+    """Grouped int4: W [O, I] f32 -> (scales [O, G], codes [O, I] in [-8, 7], grid_idx)."""
+    return _quantize("qt_quantize_g64_i4", W, d, n_grid, lo, hi, scales, codes, grid_idx,
+                     want_grid_idx, stream)
 
 
 def qt_quantize_g64_signed(W, d=None, n1: int = 64, n2: int = 32, lo: float = 0.5,
@@ -166,36 +191,63 @@ def qt_quantize_g64_signed(W, d=None, n1: int = 64, n2: int = 32, lo: float = 0.
     return scales, codes
 
 
-def qt_pack_i3(codes, packed=None, stream=None):
-    """codes [O, I] int8 -> packed [O*G*24] uint8."""
+def _pack(name, nbytes, codes, packed, stream):
     O, I = codes.shape
     if packed is None:
-        packed = torch.empty(qt_packed_bytes(O, I), dtype=torch.uint8, device=codes.device)
+        packed = torch.empty(nbytes(O, I), dtype=torch.uint8, device=codes.device)
     dev = _dev(codes, packed)
-    _check(lib().qt_pack_i3(_ptr(codes), O, I, _ptr(packed), _stream(stream, dev)), "qt_pack_i3")
+    _check(getattr(lib(), name)(_ptr(codes), O, I, _ptr(packed), _stream(stream, dev)), name)
     return packed
+
+
+def qt_pack_i3(codes, packed=None, stream=None):
+    """codes [O, I] int8 -> packed [O*G*24] uint8."""
+    return _pack("qt_pack_i3", qt_packed_bytes, codes, packed, stream)
+
+
+def qt_pack_i4(codes, packed=None, stream=None):
+    """codes [O, I] int8 in [-8, 7] -> packed [O*G*32] uint8."""
+    return _pack("qt_pack_i4", qt_packed_bytes_i4, codes, packed, stream)
+
+
+def _matvec(name, packed, scales, O, I, x, y, stream):
+    if y is None:
+        y = torch.empty(O, dtype=torch.float32, device=x.device)
+    dev = _dev(packed, scales, x, y)
+    _check(getattr(lib(), name)(_ptr(packed), _ptr(scales), O, I, _ptr(x), _ptr(y),
+                                _stream(stream, dev)), name)
+    return y
 
 
 def qt_matvec_i3(packed, scales, O: int, I: int, x, y=None, stream=None):
     """y [O] f32 = W x for x [I] f32."""
-    if y is None:
-        y = torch.empty(O, dtype=torch.float32, device=x.device)
-    dev = _dev(packed, scales, x, y)
-    _check(lib().qt_matvec_i3(_ptr(packed), _ptr(scales), O, I, _ptr(x), _ptr(y),
-                              _stream(stream, dev)), "qt_matvec_i3")
-    return y
+    return _matvec("qt_matvec_i3", packed, scales, O, I, x, y, stream)
 
 
-def qt_matmul_i3(packed, scales, O: int, I: int, X, Y=None, stream=None):
-    """Y [B, O] f32 = X W^T for X [B, I] f32 or bf16."""
+def qt_matvec_i4(packed, scales, O: int, I: int, x, y=None, stream=None):
+    """y [O] f32 = W x for int4 weights and x [I] f32."""
+    return _matvec("qt_matvec_i4", packed, scales, O, I, x, y, stream)
+
+
+def _matmul(name, packed, scales, O, I, X, Y, stream):
     B = X.shape[0]
     if Y is None:
         Y = torch.empty((B, O), dtype=torch.float32, device=X.device)
     dev = _dev(packed, scales, X, Y)
     xt = QT_BF16 if X.dtype == torch.bfloat16 else QT_F32 if X.dtype == torch.float32 else -1
-    _check(lib().qt_matmul_i3(_ptr(packed), _ptr(scales), O, I, _ptr(X), xt, B, _ptr(Y),
-                              _stream(stream, dev)), "qt_matmul_i3")
+    _check(getattr(lib(), name)(_ptr(packed), _ptr(scales), O, I, _ptr(X), xt, B, _ptr(Y),
+                                _stream(stream, dev)), name)
     return Y
+
+
+def qt_matmul_i3(packed, scales, O: int, I: int, X, Y=None, stream=None):
+    """Y [B, O] f32 = X W^T for X [B, I] f32 or bf16."""
+    return _matmul("qt_matmul_i3", packed, scales, O, I, X, Y, stream)
+
+
+def qt_matmul_i4(packed, scales, O: int, I: int, X, Y=None, stream=None):
+    """Y [B, O] f32 = X W^T for int4 weights and X [B, I] f32 or bf16."""
+    return _matmul("qt_matmul_i4", packed, scales, O, I, X, Y, stream)
 
 
 def qt_matvec_i3_grouped(packed, scales, E: int, O: int, I: int, X, expert_offsets, P: int,

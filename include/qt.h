@@ -194,6 +194,59 @@ qt_status qt_matvec_i3_grouped(const uint8_t* packed, const float* scales,
                                const int32_t* expert_offsets, int32_t P,
                                float* Y, void* stream);
 
+/*
+ * Grouped int4 (the pull request page's discussion: group-scaled int4 took
+ * its own format number beside int3-g64 and carries the same O*ceil(I/64)
+ * scale count; the per-projection ablation table lists int4-g64 and
+ * int4-g64-up3, experts at grouped int4 with up_proj at int3-g64).  The page
+ * prints no layout; this library reads it as:
+ *   the 4-bit symmetric quantizer per 64-input group: base = absmax * 0.125,
+ *   codes v in [-8, 7]; every group packs to 32 bytes of u = v + 8, value j
+ *   of the group in the low nibble of byte j/2 for even j and in the high
+ *   nibble for odd j; short groups padded with v = 0 (u = 8); group (o, g)
+ *   starts at byte (o*G + g)*32; scales[O x G] f32 as for int3-g64.
+ */
+
+/* Host: bytes of the packed int4 weights, O*ceil(I/64)*32 (0 for a
+ * non-positive size). */
+int64_t qt_packed_bytes_i4(int64_t O, int64_t I);
+
+/*
+ * qt_quantize_g64 for int4 codes: base = max_j |w_j| * 0.125 and
+ * q_j(s) = 0 if s == 0, else clamp(rne(w_j / s), -8, 7); candidates,
+ * objective, halving sum and tie rule exactly as qt_quantize_g64, and the
+ * outputs are bit-exact functions of the inputs.  Arguments as
+ * qt_quantize_g64.
+ */
+qt_status qt_quantize_g64_i4(const float* W, int64_t O, int64_t I, const float* d,
+                             int32_t n_grid, float lo, float hi, float* scales,
+                             int8_t* codes, uint8_t* grid_idx, void* stream);
+
+/*
+ * Nibble packer: codes [O x I] int8 in [-8, 7] -> packed [O*G*32] bytes in
+ * the layout above.  Codes outside [-8, 7] are masked to the low 4 bits of
+ * v + 8.
+ */
+qt_status qt_pack_i4(const int8_t* codes, int64_t O, int64_t I,
+                     uint8_t* packed, void* stream);
+
+/*
+ * qt_matvec_i3 on int4 weights: y[o] = sum_g scales[o,g] * sum_j v * x in
+ * f32 with per-group scale accumulation; tolerance 1e-5 of sum_i |w_oi x_i|.
+ *   packed [O*G*32], scales [O x G] f32, x [I] f32, y [O] f32 out.
+ */
+qt_status qt_matvec_i4(const uint8_t* packed, const float* scales, int64_t O,
+                       int64_t I, const float* x, float* y, void* stream);
+
+/*
+ * qt_matmul_i3 on int4 weights, every batch size on the exact-f32 path (bf16
+ * inputs widened exactly); tolerance 1e-5 of sum_i |w_oi X_ti|.
+ *   X [B x I] of type xt (B >= 1), Y [B x O] f32 out.
+ */
+qt_status qt_matmul_i4(const uint8_t* packed, const float* scales, int64_t O,
+                       int64_t I, const void* X, qt_dtype xt, int64_t B,
+                       float* Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

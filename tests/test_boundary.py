@@ -145,6 +145,39 @@ def test_hessian_rejects():
     assert f(A, 0, 8, 64, A + 64, 0, None, 0, None) == QT_ERR_ALIAS
 
 
+def test_int4_sizes():
+    assert qt.qt_packed_bytes_i4(2048, 7168) == 2048 * 112 * 32
+    assert qt.qt_packed_bytes_i4(2048, 7200) == 2048 * 113 * 32
+    assert qt.qt_packed_bytes_i4(0, 5) == 0 and qt.qt_packed_bytes_i4(3, -1) == 0
+    assert qt.qt_packed_bytes_i4(1 << 62, 1 << 20) == 0
+
+
+def test_int4_rejects():
+    f = L.qt_quantize_g64_i4
+    assert f(None, 4, 64, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_NULL
+    assert f(A, 4, 0, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_SHAPE
+    assert f(A, 4, 64, None, 1, 0.5, 1.0, B, Cc, None, None) == QT_ERR_ARG
+    assert f(A, 4, 64, None, 64, 1.0, 0.5, B, Cc, None, None) == QT_ERR_ARG
+    assert f(A + 2, 4, 64, None, 0, 0.5, 1.0, B, Cc, None, None) == QT_ERR_ALIGN
+    assert f(A, 4, 64, None, 0, 0.5, 1.0, B, A + 8, None, None) == QT_ERR_ALIAS
+    f = L.qt_pack_i4
+    assert f(None, 2, 64, B, None) == QT_ERR_NULL
+    assert f(A, 2, 0, B, None) == QT_ERR_SHAPE
+    assert f(A, 2, 64, B + 8, None) == QT_ERR_ALIGN
+    # 2 x 64 codes end at A + 128; the 64 packed bytes from A + 96 overlap them
+    assert f(A, 2, 64, A + 96, None) == QT_ERR_ALIAS
+    f = L.qt_matvec_i4
+    assert f(A, B, 4, 64, Cc, None, None) == QT_ERR_NULL
+    assert f(A + 8, B, 4, 64, Cc, D, None) == QT_ERR_ALIGN
+    # 4 rows x 32 bytes: a y at A + 100 lies inside the int4 weights
+    assert f(A, B, 4, 64, Cc, A + 100, None) == QT_ERR_ALIAS
+    f = L.qt_matmul_i4
+    assert f(A, B, 4, 64, Cc, 7, 2, D, None) == QT_ERR_DTYPE
+    assert f(A, B, 4, 64, Cc, 0, 0, D, None) == QT_ERR_SHAPE
+    assert f(A, B, 4, 64, Cc + 8, 1, 32, D, None) == QT_ERR_ALIGN
+    assert f(A, B, 4, 64, Cc, 0, 2, A + 100, None) == QT_ERR_ALIAS
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
