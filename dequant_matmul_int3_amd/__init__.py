@@ -5,12 +5,12 @@ include/qt.h); this package only marshals torch device tensors into that ABI.
 """
 from .qt import (QtError, QT_BF16, QT_F32, lib, qt_groups, qt_hessian_diag,
                  qt_hessian_workspace_bytes, qt_matmul_i3, qt_matmul_i4, qt_matvec_i3,
-                 qt_matvec_i3_grouped, qt_matvec_i4, qt_pack_i3, qt_pack_i4, qt_packed_bytes,
+                 qt_matvec_i3_grouped, qt_matvec_i4, qt_matvec_i4_grouped, qt_pack_i3, qt_pack_i4, qt_packed_bytes,
                  qt_packed_bytes_i4, qt_quantize_g64, qt_quantize_g64_i4,
                  qt_quantize_g64_signed, qt_status_str)
 
 __all__ = ["QtError", "QT_BF16", "QT_F32", "lib", "qt_groups", "qt_hessian_diag",
            "qt_hessian_workspace_bytes", "qt_matmul_i3", "qt_matmul_i4", "qt_matvec_i3",
-           "qt_matvec_i3_grouped", "qt_matvec_i4", "qt_pack_i3", "qt_pack_i4",
+           "qt_matvec_i3_grouped", "qt_matvec_i4", "qt_matvec_i4_grouped", "qt_pack_i3", "qt_pack_i4",
            "qt_packed_bytes", "qt_packed_bytes_i4", "qt_quantize_g64", "qt_quantize_g64_i4",
            "qt_quantize_g64_signed", "qt_status_str"]

@@ -300,17 +300,20 @@ qt_status qt_matmul_i3(const uint8_t* packed, const float* scales, int64_t O, in
                                           as_stream(stream)));
 }
 
-qt_status qt_matvec_i3_grouped(const uint8_t* packed, const float* scales, int32_t E, int64_t O,
-                               int64_t I, const float* X, int64_t n_x_rows,
-                               const int32_t* pair_row, const int32_t* expert_offsets, int32_t P,
-                               float* Y, void* stream) {
+namespace {
+
+qt_status grouped_bits(const uint8_t* packed, const float* scales, int32_t E, int64_t O,
+                       int64_t I, const float* X, int64_t n_x_rows, const int32_t* pair_row,
+                       const int32_t* expert_offsets, int32_t P, float* Y, void* stream,
+                       int bits) {
     if (!packed || !scales || !X || !expert_offsets || !Y) return QT_ERR_NULL;
-    qt_status st = shape_ok(O, I);
+    const int64_t gbytes = bits == 3 ? kGroupBytes : kGroupBytesI4;
+    qt_status st = shape_ok(O, I, gbytes);
     if (st != QT_OK) return st;
     if (E < 1 || E > 65535 || P < 1 || n_x_rows < 1) return QT_ERR_SHAPE;
     if (!pair_row && n_x_rows < P) return QT_ERR_SHAPE;
     const int64_t G = qt_groups(I);
-    const int64_t pk = mul3(E, O * G, kGroupBytes), sk = mul3(E, O * G, 4);
+    const int64_t pk = mul3(E, O * G, gbytes), sk = mul3(E, O * G, 4);
     const int64_t xb = mul3(n_x_rows, I, 4), yb = mul3(P, O, 4);
     if (pk < 0 || sk < 0 || xb < 0 || yb < 0) return QT_ERR_SHAPE;
     if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(X, 4) || !aligned(Y, 4) ||
@@ -321,7 +324,25 @@ qt_status qt_matvec_i3_grouped(const uint8_t* packed, const float* scales, int32
         (pair_row && overlap(Y, yb, pair_row, (int64_t)P * 4)))
         return QT_ERR_ALIAS;
     return launched(qt::launch_gemv_grouped(packed, scales, E, O, I, X, n_x_rows, pair_row,
-                                            expert_offsets, P, Y, as_stream(stream)));
+                                            expert_offsets, P, Y, as_stream(stream), bits));
+}
+
+}  // namespace
+
+qt_status qt_matvec_i3_grouped(const uint8_t* packed, const float* scales, int32_t E, int64_t O,
+                               int64_t I, const float* X, int64_t n_x_rows,
+                               const int32_t* pair_row, const int32_t* expert_offsets, int32_t P,
+                               float* Y, void* stream) {
+    return grouped_bits(packed, scales, E, O, I, X, n_x_rows, pair_row, expert_offsets, P, Y,
+                        stream, 3);
+}
+
+qt_status qt_matvec_i4_grouped(const uint8_t* packed, const float* scales, int32_t E, int64_t O,
+                               int64_t I, const float* X, int64_t n_x_rows,
+                               const int32_t* pair_row, const int32_t* expert_offsets, int32_t P,
+                               float* Y, void* stream) {
+    return grouped_bits(packed, scales, E, O, I, X, n_x_rows, pair_row, expert_offsets, P, Y,
+                        stream, 4);
 }
 
 }  // extern "C"

@@ -1,10 +1,12 @@
-// Grouped (mixture-of-experts) int3-g64 dequantize-and-multiply on the gfx950
-// matrix cores, exact-f32 semantics.
+// Grouped (mixture-of-experts) int3-g64 and grouped-int4 dequantize-and-
+// multiply on the gfx950 matrix cores, exact-f32 semantics.
 //
 // Y[p, o] = sum_g s_e[o,g] * sum_{j<64} v_e[o,64g+j] * x_p[64g+j] for every
 // routed pair p of expert e: the per-group scale accumulation of the matmul_i3
 // kernel ("int3-g64 (fmt=5)" pull request page, "Design", Kernel bullet) with
-// f32 inputs.
+// f32 inputs.  Mixed per-projection bits (the same page's per-projection
+// ablation: experts at grouped int4 with up_proj at int3-g64) run each
+// projection through the instantiation of its own format.
 //
 // Why the matrix cores.  A vector-ALU GEMV spends one FMA per code per token
 // on top of the unpacking; with a few tokens per expert that, not the weight
@@ -17,6 +19,10 @@
 // Code times piece products are exact in the matrix core's f32 accumulation,
 // so every group's dot product is an f32 sum of exact products, as on the
 // vector path; the pieces of a token are summed after the groups.
+//
+// int4 codes enter as v/16: v_cvt_off_f32_i4 turns a two's-complement nibble
+// into that f32 value exactly, whose high half is its bf16 encoding; the
+// results are multiplied by 16 at the end (exact: a power of two).
 //
 // Tiling.  A block of 4 waves owns 64 consecutive output rows of one expert;
 // wave w multiplies rows [16w, 16w+16) as the A operand (16 rows x 32 inputs
@@ -39,11 +45,18 @@ constexpr int kRows = 64;             // output rows per block
 constexpr int kThreads = 256;         // 4 waves
 constexpr int kCG = 16;               // groups per chunk
 constexpr int kTok = 5;               // tokens per pass (3 B columns each)
-constexpr int kWRow = kCG * kGroupBytes + 16;  // LDS bytes per weight row (+16: conflict-free reads)
 constexpr int kPRow = kCG * kGroup * 2 + 16;   // LDS bytes per piece column
-constexpr int kWPieces = kRows * kCG * kGroupBytes / 16;  // 16-byte pieces per chunk (1536)
-constexpr int kWPer = kWPieces / kThreads;                 // 6
-static_assert(kWPieces % kThreads == 0, "weight chunk split");
+
+// Weight staging geometry of a format: bytes per group, LDS bytes per weight
+// row (+16: conflict-free reads), 16-byte pieces per thread per chunk.
+template <int BITS>
+struct Geo {
+    static constexpr int kGB = BITS == 3 ? kGroupBytes : kGroupBytesI4;
+    static constexpr int kWRow = kCG * kGB + 16;
+    static constexpr int kWPieces = kRows * kCG * kGB / 16;  // 1536 or 2048
+    static constexpr int kWPer = kWPieces / kThreads;        // 6 or 8
+    static_assert(kWPieces % kThreads == 0, "weight chunk split");
+};
 
 // bf16 bit patterns of v = u - 4 for four codes u (one per byte), as the pairs
 // [c0 | c1 << 16] and [c2 | c3 << 16].  bf16(v) for v = -4..3 is c080 c040 c000
@@ -79,6 +92,39 @@ __device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t h16, u32x4_
     hi8 = u32x4_t{p89, p1011, p1213, p1415};
 }
 
+// v/16 of the two's-complement nibble in the low four bits of byte B of t.
+template <int B>
+__device__ __forceinline__ float nib(uint32_t t) {
+    float r;
+    if constexpr (B == 0)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0"
+            : "=v"(r) : "v"(t));
+    else if constexpr (B == 1)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+            : "=v"(r) : "v"(t));
+    else if constexpr (B == 2)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+            : "=v"(r) : "v"(t));
+    else
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+            : "=v"(r) : "v"(t));
+    return r;
+}
+
+// bf16 pair [f(a) | f(b) << 16] of two f32 values with zero low halves.
+__device__ __forceinline__ uint32_t hi_pair(float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// One int4 word (code n of the word in nibble n, u = v + 8) -> its 8 codes
+// as v/16 in bf16, natural order.  u ^ 8 is the two's-complement nibble of v.
+__device__ __forceinline__ u32x4_t dequant_word_i4(uint32_t w) {
+    const uint32_t t = w ^ 0x88888888u;  // even codes: low nibble of each byte
+    const uint32_t h = t >> 4;           // odd codes: low nibble of each byte
+    return u32x4_t{hi_pair(nib<0>(t), nib<0>(h)), hi_pair(nib<1>(t), nib<1>(h)),
+                   hi_pair(nib<2>(t), nib<2>(h)), hi_pair(nib<3>(t), nib<3>(h))};
+}
+
 // The three bf16 pieces of four f32 inputs, as [piece][pair] words.
 __device__ __forceinline__ void split3(const float (&x)[4], uint32_t (&w)[3][2]) {
     uint32_t h[4], m[4], l[4];
@@ -109,14 +155,17 @@ __device__ __forceinline__ float from_lane_plus(float a) {
 }
 
 // grid: (row blocks of 64, experts).  W16: every row's chunk bytes start on a
-// 16-byte boundary (G even); else 8-byte pieces.  XV: inputs allow 16-byte
-// loads (I % 4 == 0, X 16-byte aligned).
-template <bool W16, bool XV>
+// 16-byte boundary (int4, or int3 with G even); else 8-byte pieces.  XV:
+// inputs allow 16-byte loads (I % 4 == 0, X 16-byte aligned).
+template <int BITS, bool W16, bool XV>
 __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int32_t I,
     int32_t G, const float* __restrict__ X, int64_t n_x_rows,
     const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t P,
     float* __restrict__ Y) {
+    constexpr int kGB = Geo<BITS>::kGB;
+    constexpr int kWRow = Geo<BITS>::kWRow;
+    constexpr int kWPer = Geo<BITS>::kWPer;
     __shared__ __attribute__((aligned(16))) uint8_t wl[kRows * kWRow];   // weight bytes
     __shared__ __attribute__((aligned(16))) float sl[kCG][kRows];        // scales [group][row]
     __shared__ __attribute__((aligned(16))) uint8_t pl[16 * kPRow];      // pieces [col][k]
@@ -134,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
     const int l16 = lane & 15;
     const int j4 = lane >> 4;  // quarter of the group (A), k slot (B)
     const int64_t r0 = (int64_t)blockIdx.x * kRows;
-    const uint8_t* pk = packed + (int64_t)e * O * G * kGroupBytes;
+    const uint8_t* pk = packed + (int64_t)e * O * G * kGB;
     const float* sk = scales + (int64_t)e * O * G;
 
     // column 15 of the pieces is never written by the staging: zero it once
@@ -143,16 +192,16 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
 
     // ---- per-thread staging assignments (rows past O read row O-1, unused)
     // weights: piece i of this thread = 16-byte piece (tid + 256 i) of the
-    // chunk, row-major over [row][kCG * 24 bytes]
+    // chunk, row-major over [row][kCG * kGB bytes]
     const uint8_t* wrow0[kWPer];  // the row's first byte (always a valid 16 bytes)
     int wdst[kWPer];
     int wpart[kWPer];
 #pragma unroll
     for (int i = 0; i < kWPer; ++i) {
         const int id = tid + kThreads * i;
-        const int row = id / (kCG * kGroupBytes / 16), part = id % (kCG * kGroupBytes / 16);
+        const int row = id / (kCG * kGB / 16), part = id % (kCG * kGB / 16);
         const int64_t gr = min<int64_t>(r0 + row, O - 1);
-        wrow0[i] = pk + gr * G * kGroupBytes;
+        wrow0[i] = pk + gr * G * kGB;
         wdst[i] = row * kWRow + 16 * part;
         wpart[i] = part;
     }
@@ -172,13 +221,14 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < kWPer; ++i) {
             const int b0 = wpart[i] * 16;
-            const uint8_t* rc = wrow0[i] + (int64_t)c0 * kGroupBytes;
+            const uint8_t* rc = wrow0[i] + (int64_t)c0 * kGB;
             if constexpr (W16) {
-                const uint8_t* src = b0 < gn * kGroupBytes ? rc + b0 : wrow0[i];
+                const uint8_t* src = b0 < gn * kGB ? rc + b0 : wrow0[i];
                 c.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
             } else {
-                const uint8_t* sa = b0 < gn * kGroupBytes ? rc + b0 : wrow0[i];
-                const uint8_t* sb = b0 + 8 < gn * kGroupBytes ? rc + b0 + 8 : wrow0[i];
+                static_assert(BITS == 3, "int4 groups are always 16-byte aligned");
+                const uint8_t* sa = b0 < gn * kGB ? rc + b0 : wrow0[i];
+                const uint8_t* sb = b0 + 8 < gn * kGB ? rc + b0 + 8 : wrow0[i];
                 const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sa));
                 const u32x2_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sb));
                 c.w[i] = u32x4_t{a.x, a.y, b.x, b.y};
@@ -261,11 +311,19 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
             const uint8_t* wrow = wl + (16 * wave + l16) * kWRow;
             const uint8_t* prow = pl + l16 * kPRow + 32 * j4;
             for (int g = 0; g < gn; ++g) {
-                const uint32_t lo = *reinterpret_cast<const uint32_t*>(wrow + g * kGroupBytes + 4 * j4);
-                const uint32_t hw = *reinterpret_cast<const uint32_t*>(
-                    wrow + g * kGroupBytes + 16 + 4 * (j4 >> 1));
                 u32x4_t a0, a1;
-                dequant_quarter(lo, (hw >> (16 * (j4 & 1))) & 0xFFFFu, a0, a1);
+                if constexpr (BITS == 3) {
+                    const uint32_t lo =
+                        *reinterpret_cast<const uint32_t*>(wrow + g * kGB + 4 * j4);
+                    const uint32_t hw = *reinterpret_cast<const uint32_t*>(
+                        wrow + g * kGB + 16 + 4 * (j4 >> 1));
+                    dequant_quarter(lo, (hw >> (16 * (j4 & 1))) & 0xFFFFu, a0, a1);
+                } else {
+                    // quarter j4 = codes 16 j4 .. 16 j4 + 15 = bytes 8 j4 .. 8 j4 + 7
+                    const u32x2_t q = *reinterpret_cast<const u32x2_t*>(wrow + g * kGB + 8 * j4);
+                    a0 = dequant_word_i4(q.x);
+                    a1 = dequant_word_i4(q.y);
+                }
                 const u32x4_t b0 = *reinterpret_cast<const u32x4_t*>(prow + g * 128);
                 const u32x4_t b1 = *reinterpret_cast<const u32x4_t*>(prow + g * 128 + 16);
                 f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -287,6 +345,7 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
             const float v1 = from_lane_plus<1>(acc[r]);
             const float v2 = from_lane_plus<2>(acc[r]);
             acc[r] = (acc[r] + v1) + v2;
+            if constexpr (BITS == 4) acc[r] *= 16.0f;  // the codes entered as v/16
         }
         const int t = l16 / 3;
         if (l16 % 3 == 0 && t < nt && tout[t] >= 0) {
@@ -304,23 +363,33 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
 hipError_t launch_gemv_grouped(const uint8_t* packed, const float* scales, int32_t E,
                                int64_t O, int64_t I, const float* X, int64_t n_x_rows,
                                const int32_t* pair_row, const int32_t* expert_offsets,
-                               int32_t P, float* Y, hipStream_t s) {
+                               int32_t P, float* Y, hipStream_t s, int bits) {
     const int64_t G = (I + kGroup - 1) / kGroup;
     const dim3 grid((unsigned)((O + kRows - 1) / kRows), (unsigned)E);
-    const bool w16 = (G % 2 == 0) && ((reinterpret_cast<uintptr_t>(packed) & 15) == 0);
+    const bool a16 = (reinterpret_cast<uintptr_t>(packed) & 15) == 0;
     const bool xv = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-#define QT_GROUPED(W, V)                                                                        \
-    hipLaunchKernelGGL((gemv_grouped_mfma_kernel<W, V>), grid, dim3(kThreads), 0, s, packed, \
-                       scales, O, (int32_t)I, (int32_t)G, X, n_x_rows, pair_row,            \
+#define QT_GROUPED(B, W, V)                                                                   \
+    hipLaunchKernelGGL((gemv_grouped_mfma_kernel<B, W, V>), grid, dim3(kThreads), 0, s,     \
+                       packed, scales, O, (int32_t)I, (int32_t)G, X, n_x_rows, pair_row,  \
                        expert_offsets, P, Y)
+    if (bits == 4) {
+        if (!a16) return hipErrorInvalidValue;
+        if (xv)
+            QT_GROUPED(4, true, true);
+        else
+            QT_GROUPED(4, true, false);
+        return hipGetLastError();
+    }
+    if (bits != 3) return hipErrorInvalidValue;
+    const bool w16 = (G % 2 == 0) && a16;
     if (w16 && xv)
-        QT_GROUPED(true, true);
+        QT_GROUPED(3, true, true);
     else if (w16)
-        QT_GROUPED(true, false);
+        QT_GROUPED(3, true, false);
     else if (xv)
-        QT_GROUPED(false, true);
+        QT_GROUPED(3, false, true);
     else
-        QT_GROUPED(false, false);
+        QT_GROUPED(3, false, false);
 #undef QT_GROUPED
     return hipGetLastError();
 }

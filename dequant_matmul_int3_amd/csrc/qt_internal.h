@@ -39,10 +39,11 @@ hipError_t launch_gemv_batch(const uint8_t* packed, const float* scales, int64_t
                              int64_t I, const void* X, bool bf16, int64_t ntok,
                              float* Y, hipStream_t s, int bits = 3);
 
+// bits: 3 (int3-g64 experts) or 4 (grouped int4 experts).
 hipError_t launch_gemv_grouped(const uint8_t* packed, const float* scales, int32_t E,
                                int64_t O, int64_t I, const float* X, int64_t n_x_rows,
                                const int32_t* pair_row, const int32_t* expert_offsets,
-                               int32_t P, float* Y, hipStream_t s);
+                               int32_t P, float* Y, hipStream_t s, int bits = 3);
 
 // bf16 MFMA path, B >= 16.
 hipError_t launch_gemm_mfma(const uint8_t* packed, const float* scales, int64_t O,

@@ -40,6 +40,9 @@ _SIGS = {
     "qt_matvec_i3_grouped": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
                                        C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
                                        C.c_void_p, C.c_void_p]),
+    "qt_matvec_i4_grouped": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                       C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
+                                       C.c_void_p, C.c_void_p]),
     "qt_packed_bytes_i4": (C.c_int64, [C.c_int64, C.c_int64]),
     "qt_quantize_g64_i4": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
                                      C.c_float, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -250,13 +253,25 @@ def qt_matmul_i4(packed, scales, O: int, I: int, X, Y=None, stream=None):
     return _matmul("qt_matmul_i4", packed, scales, O, I, X, Y, stream)
 
 
-def qt_matvec_i3_grouped(packed, scales, E: int, O: int, I: int, X, expert_offsets, P: int,
-                         pair_row=None, Y=None, stream=None):
-    """Y [P, O] f32: Y[p] = W_{e(p)} X[row(p)] for pairs sorted by expert."""
+def _grouped(name, packed, scales, E, O, I, X, expert_offsets, P, pair_row, Y, stream):
     if Y is None:
         Y = torch.empty((P, O), dtype=torch.float32, device=X.device)
     dev = _dev(packed, scales, X, expert_offsets, pair_row, Y)
-    _check(lib().qt_matvec_i3_grouped(_ptr(packed), _ptr(scales), E, O, I, _ptr(X), X.shape[0],
-                                      _ptr(pair_row), _ptr(expert_offsets), P, _ptr(Y),
-                                      _stream(stream, dev)), "qt_matvec_i3_grouped")
+    _check(getattr(lib(), name)(_ptr(packed), _ptr(scales), E, O, I, _ptr(X), X.shape[0],
+                                _ptr(pair_row), _ptr(expert_offsets), P, _ptr(Y),
+                                _stream(stream, dev)), name)
     return Y
+
+
+def qt_matvec_i3_grouped(packed, scales, E: int, O: int, I: int, X, expert_offsets, P: int,
+                         pair_row=None, Y=None, stream=None):
+    """Y [P, O] f32: Y[p] = W_{e(p)} X[row(p)] for pairs sorted by expert."""
+    return _grouped("qt_matvec_i3_grouped", packed, scales, E, O, I, X, expert_offsets, P,
+                    pair_row, Y, stream)
+
+
+def qt_matvec_i4_grouped(packed, scales, E: int, O: int, I: int, X, expert_offsets, P: int,
+                         pair_row=None, Y=None, stream=None):
+    """qt_matvec_i3_grouped for grouped int4 experts."""
+    return _grouped("qt_matvec_i4_grouped", packed, scales, E, O, I, X, expert_offsets, P,
+                    pair_row, Y, stream)

@@ -247,6 +247,21 @@ qt_status qt_matmul_i4(const uint8_t* packed, const float* scales, int64_t O,
                        int64_t I, const void* X, qt_dtype xt, int64_t B,
                        float* Y, void* stream);
 
+/*
+ * qt_matvec_i3_grouped on grouped int4 experts (packed [E][O*G*32]); the
+ * per-projection mix of the ablation table (experts at int4 with up_proj at
+ * int3-g64) calls qt_matvec_i3_grouped for the int3 projection and this for
+ * the others.  Arguments, routing layout and tolerance as
+ * qt_matvec_i3_grouped; the int4 codes enter the matrix cores as exact bf16
+ * values of v/16 and the result is scaled back by 16 (exact).
+ */
+qt_status qt_matvec_i4_grouped(const uint8_t* packed, const float* scales,
+                               int32_t E, int64_t O, int64_t I,
+                               const float* X, int64_t n_x_rows,
+                               const int32_t* pair_row,
+                               const int32_t* expert_offsets, int32_t P,
+                               float* Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -182,3 +182,12 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         qt.qt_pack_i3(torch.zeros((2, 64), dtype=torch.int8))
+
+
+def test_int4_grouped_rejects():
+    f = L.qt_matvec_i4_grouped
+    assert f(A, B, 8, 4, 64, Cc, 4, None, None, 4, D, None) == QT_ERR_NULL
+    assert f(A, B, 0, 4, 64, Cc, 4, None, A, 4, D, None) == QT_ERR_SHAPE
+    assert f(A + 8, B, 8, 4, 64, Cc, 4, None, A + (1 << 30), 4, D, None) == QT_ERR_ALIGN
+    # 8 experts x 4 rows x 32 bytes = 1024 packed bytes from A: Y at A + 1000 overlaps
+    assert f(A, B, 8, 4, 64, Cc, 4, None, A + (1 << 30), 4, A + 1000, None) == QT_ERR_ALIAS

@@ -201,3 +201,87 @@ def test_i4_reconstruction_beats_int3_on_the_same_weights():
     r4 = np.repeat(host(s4).astype(np.float64), 64, axis=1)[:, :I] * host(c4) - W
     r3 = np.repeat(host(s3).astype(np.float64), 64, axis=1)[:, :I] * host(c3) - W
     assert np.all((r4 ** 2).sum(axis=1) < (r3 ** 2).sum(axis=1))
+
+
+# ---------------------------------------------------------------- grouped (MoE)
+def _grouped_i4_case(E, O, I, T, topk, seed):
+    rng = workloads.rng_for("generic", 900 + seed, E, O, I)
+    logits = rng.random((T, E))
+    top = np.argsort(-logits, axis=1, kind="stable")[:, :topk].astype(np.int32)
+    tok, exp, offs = workloads.route_pairs(top, E)
+    Ws = [workloads.generic_weights(O, I, seed=3000 * seed + e) for e in range(E)]
+    q = [oracle.quantize_g64_i4(w) for w in Ws]
+    so = np.stack([a[0] for a in q])
+    po = np.stack([oracle.pack_i4(a[1]) for a in q])
+    X = workloads.generic_matrix(T, I, seed=seed + 50)
+    return tok, exp, offs, so, po, X
+
+
+@pytest.mark.parametrize("E,O,I,T,topk", [(4, 40, 300, 6, 2), (16, 64, 1000, 32, 8),
+                                          (3, 100, 64, 40, 3), (8, 33, 7200, 5, 1),
+                                          (5, 130, 450, 12, 3), (3, 70, 130, 9, 2),
+                                          (2, 65, 97, 7, 2)])
+def test_i4_grouped_matvec(E, O, I, T, topk):
+    tok, exp, offs, so, po, X = _grouped_i4_case(E, O, I, T, topk, seed=E + T)
+    P = tok.size
+    say(f"int4 grouped E={E} O={O} I={I} P={P}")
+    Y = host(qt.qt_matvec_i4_grouped(dev(po), dev(so), E, O, I, dev(X), dev(offs), P,
+                                     pair_row=dev(tok)))
+    for p in range(P):
+        e, t = exp[p], tok[p]
+        yr, ar = matvec_ref(po[e], so[e], O, I, X[t])
+        assert componentwise_err(Y[p], yr, ar) <= TOL_F32, (p, e, t)
+    H = workloads.generic_matrix(P, I, seed=78)
+    Y2 = host(qt.qt_matvec_i4_grouped(dev(po), dev(so), E, O, I, dev(H), dev(offs), P))
+    for p in range(P):
+        yr, ar = matvec_ref(po[exp[p]], so[exp[p]], O, I, H[p])
+        assert componentwise_err(Y2[p], yr, ar) <= TOL_F32
+
+
+def test_i4_grouped_one_hot_is_exact_and_empty_experts():
+    # one-hot inputs pick single codes: v * s exactly, through the v/16 entry
+    # and the final scaling by 16
+    E, O, I = 4, 70, 200
+    offs = np.array([0, 0, 5, 5, 5], np.int32)
+    Ws = [workloads.generic_weights(O, I, seed=40 + e) for e in range(E)]
+    q = [oracle.quantize_g64_i4(w) for w in Ws]
+    so = np.stack([a[0] for a in q])
+    po = np.stack([oracle.pack_i4(a[1]) for a in q])
+    cols = [0, 1, 63, 64, 199]
+    X = np.zeros((5, I), np.float32)
+    for p, i in enumerate(cols):
+        X[p, i] = 1.0
+    say("int4 grouped one-hot")
+    Y = host(qt.qt_matvec_i4_grouped(dev(po), dev(so), E, O, I, dev(X), dev(offs), 5))
+    c1, s1 = q[1][1], q[1][0]
+    for p, i in enumerate(cols):
+        assert np.array_equal(Y[p], s1[:, i // 64] * c1[:, i].astype(np.float32))
+
+
+def test_mixed_bits_moe_step_up_int3_down_int4():
+    # the per-projection mix: up at int3-g64, down at grouped int4, on one
+    # routing; each projection against the oracle of its own format
+    E, T, topk, D, F = 8, 12, 2, 640, 256
+    rng = workloads.rng_for("generic", 4242)
+    top = np.argsort(-rng.random((T, E)), axis=1, kind="stable")[:, :topk].astype(np.int32)
+    tok, exp, offs = workloads.route_pairs(top, E)
+    P = tok.size
+    up = [oracle.quantize_g64(workloads.generic_weights(F, D, seed=60 + e)) for e in range(E)]
+    dn = [oracle.quantize_g64_i4(workloads.generic_weights(D, F, seed=80 + e))
+          for e in range(E)]
+    su = np.stack([a[0] for a in up])
+    pu = np.stack([oracle.pack_i3(a[1]) for a in up])
+    sdn = np.stack([a[0] for a in dn])
+    pdn = np.stack([oracle.pack_i4(a[1]) for a in dn])
+    X = workloads.generic_matrix(T, D, seed=91)
+    H = workloads.generic_matrix(P, F, seed=92)  # the down projection's own inputs
+    say(f"mixed-bit MoE step E={E} P={P}")
+    Yu = host(qt.qt_matvec_i3_grouped(dev(pu), dev(su), E, F, D, dev(X), dev(offs), P,
+                                      pair_row=dev(tok)))
+    Yd = host(qt.qt_matvec_i4_grouped(dev(pdn), dev(sdn), E, D, F, dev(H), dev(offs), P))
+    for p in range(P):
+        e = exp[p]
+        yr, ar = oracle.matvec_f64(pu[e], su[e], F, D, X[tok[p]])
+        assert componentwise_err(Yu[p], yr, ar) <= TOL_F32
+        yr, ar = matvec_ref(pdn[e], sdn[e], D, F, H[p])
+        assert componentwise_err(Yd[p], yr, ar) <= TOL_F32
