@@ -13,7 +13,9 @@ The other rows of the hot path are timed as "legs" on their own workloads:
 the Hessian diagonal and the weighted scale search (W[5120x17408],
 X[8192x17408]), plain quantize + pack at the decode shape, the grouped MoE
 GEMV (128 experts, 32 tokens, top-8) and the bf16 MFMA prefill GEMM
-(X[512x7168] x W[18432x7168]).  Every input is seeded synthetic data
+(X[512x7168] x W[18432x7168]); grouped int4: the decode GEMV with int4
+weights and the MoE step with every projection at int4 and with up at int3
+(the per-projection mix).  Every input is seeded synthetic data
 (workloads.py) resident on the GPU before its timed region starts.
 """
 import argparse
@@ -91,6 +93,26 @@ def time_launches(fn, n, torch, warmup=2):
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
     return total_ms / n
+
+
+def graph_ms(fn, n_copies, warmup, steps, torch):
+    """Per-call time of fn(j), j = 0..n_copies-1, captured once in a HIP
+    graph and replayed until `steps` calls are timed (so that host-side call
+    overhead does not pace the GPU)."""
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        for j in range(n_copies):
+            fn(j)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        for j in range(n_copies):
+            fn(j)
+    for _ in range(max(1, -(-warmup // n_copies))):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // n_copies))
+    return time_launches(lambda i: graph.replay(), reps, torch) / n_copies, reps * n_copies
 
 
 def per_launch_ms(fn, n, torch):
@@ -193,7 +215,7 @@ def main():
         unknown = which - set(LEG_NAMES)
         if unknown:
             raise SystemExit(f"unknown legs {sorted(unknown)}; choose from {LEG_NAMES}")
-        legs.update(run_legs(torch, qt, workloads, dev, which))
+        legs.update(run_legs(torch, qt, workloads, dev, which, args))
 
     cpu = cpu_baseline(W, x, args.cpu_seconds, bytes_step)
 
@@ -224,23 +246,62 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-LEG_NAMES = ["quant", "search", "moe", "prefill"]
+LEG_NAMES = ["quant", "search", "moe", "prefill", "int4", "moe_int4"]
 
 
-def run_legs(torch, qt, workloads, dev, which):
+def run_legs(torch, qt, workloads, dev, which, args):
     """Time the selected legs: quant (RTN quantize + pack at the decode shape),
     search (Hessian diagonal + weighted scale search), moe (grouped GEMV),
-    prefill (bf16 MFMA GEMM)."""
+    prefill (bf16 MFMA GEMM), int4 (grouped-int4 quantize, pack and decode
+    GEMV), moe_int4 (the MoE step at int4 and with up at int3)."""
     legs = {}
     if "quant" in which:
         quant_leg(torch, qt, workloads, dev, legs)
     if "search" in which:
         search_leg(torch, qt, workloads, dev, legs)
-    if "moe" in which:
-        moe_leg(torch, qt, workloads, dev, legs)
+    if "moe" in which or "moe_int4" in which:
+        moe_leg(torch, qt, workloads, dev, legs, "moe" in which, "moe_int4" in which)
     if "prefill" in which:
         prefill_leg(torch, qt, workloads, dev, legs)
+    if "int4" in which:
+        int4_leg(torch, qt, workloads, dev, legs, args)
     return legs
+
+
+def int4_leg(torch, qt, workloads, dev, legs, args):
+    # --------------------------------------------- grouped int4, decode shape
+    W, x = workloads.decode()
+    O, I = W.shape
+    G = qt.qt_groups(I)
+    Wd = torch.from_numpy(W).to(dev)
+    xd = torch.from_numpy(x).to(dev)
+    s, c, _ = qt.qt_quantize_g64_i4(Wd, want_grid_idx=False)
+    p = qt.qt_pack_i4(c)
+    torch.cuda.synchronize()
+    ms_q = time_launches(lambda i: qt.qt_quantize_g64_i4(Wd, scales=s, codes=c,
+                                                         want_grid_idx=False), 20, torch)
+    ms_p = time_launches(lambda i: qt.qt_pack_i4(c, p), 50, torch)
+    packs = torch.empty((N_COPIES, p.numel()), dtype=torch.uint8, device=dev)
+    scs = torch.empty((N_COPIES, O, G), dtype=torch.float32, device=dev)
+    packs.copy_(p.expand(N_COPIES, -1))
+    scs.copy_(s.expand(N_COPIES, -1, -1))
+    y = torch.empty(O, dtype=torch.float32, device=dev)
+    bytes_step = p.numel() + s.numel() * 4 + I * 4 + O * 4
+    ms, _ = graph_ms(lambda j: qt.qt_matvec_i4(packs[j], scs[j], O, I, xd, y), N_COPIES,
+                     args.warmup, args.steps, torch)
+    gbs = bytes_step / (ms * 1e-3) / 1e9
+    legs["gemv_decode_int4"] = {"us": round(ms * 1e3, 3), "GB_s": round(gbs, 1), "bound": "hbm",
+                                "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                "bytes_per_launch": int(bytes_step),
+                                "kernel": "gemv_batch_kernel<64,8,1,f32,vec,int4>"}
+    legs["quantize_rtn_decode_int4"] = {"ms": round(ms_q, 5),
+                                        "groups_per_s": round(O * G / (ms_q * 1e-3))}
+    bytes_p = O * I + p.numel()
+    legs["pack_decode_int4"] = {"ms": round(ms_p, 5),
+                                "GB_s": round(bytes_p / (ms_p * 1e-3) / 1e9, 1)}
+    log(f"leg int4: {legs['gemv_decode_int4']} {legs['quantize_rtn_decode_int4']} "
+        f"{legs['pack_decode_int4']}")
+    del packs, scs
 
 
 def quant_leg(torch, qt, workloads, dev, legs):
@@ -316,24 +377,37 @@ def search_leg(torch, qt, workloads, dev, legs):
     del Wd, s, c, k, d
 
 
-def moe_leg(torch, qt, workloads, dev, legs):
+def moe_leg(torch, qt, workloads, dev, legs, int3_step=True, int4_steps=False):
     # -------------------------------------------------------- grouped MoE GEMV
     E = workloads.MOE_EXPERTS
     log("leg moe: generating and quantizing 128 experts x (up, down)")
-    (Ou, Iu), (Od, Id) = workloads.MOE_UP_SHAPE, workloads.MOE_DOWN_SHAPE
-    pu = torch.empty((E, qt.qt_packed_bytes(Ou, Iu)), dtype=torch.uint8, device=dev)
-    su = torch.empty((E, Ou, qt.qt_groups(Iu)), dtype=torch.float32, device=dev)
-    pdn = torch.empty((E, qt.qt_packed_bytes(Od, Id)), dtype=torch.uint8, device=dev)
-    sdn = torch.empty((E, Od, qt.qt_groups(Id)), dtype=torch.float32, device=dev)
-    for which, pk, sc in (("up", pu, su), ("down", pdn, sdn)):
+    shapes = {"up": workloads.MOE_UP_SHAPE, "down": workloads.MOE_DOWN_SHAPE}
+    need = set()
+    if int3_step:
+        need |= {("up", 3), ("down", 3)}
+    if int4_steps:
+        need |= {("up", 4), ("down", 4), ("up", 3)}
+    fmt = {3: (qt.qt_packed_bytes, qt.qt_quantize_g64, qt.qt_pack_i3),
+           4: (qt.qt_packed_bytes_i4, qt.qt_quantize_g64_i4, qt.qt_pack_i4)}
+    store = {}
+    for proj, bits in need:
+        O_, I_ = shapes[proj]
+        store[proj, bits] = (
+            torch.empty((E, fmt[bits][0](O_, I_)), dtype=torch.uint8, device=dev),
+            torch.empty((E, O_, qt.qt_groups(I_)), dtype=torch.float32, device=dev))
+    for proj in ("up", "down"):
+        bl = sorted(b for (pr, b) in need if pr == proj)
         for e0 in range(0, E, 16):
-            mats = workloads.moe_experts_parallel(which, range(e0, e0 + 16), workers=16)
+            mats = workloads.moe_experts_parallel(proj, range(e0, e0 + 16), workers=16)
             for j, m in enumerate(mats):
                 md = torch.from_numpy(m).to(dev)
-                s_, c_, _ = qt.qt_quantize_g64(md, want_grid_idx=False)
-                sc[e0 + j].copy_(s_)
-                qt.qt_pack_i3(c_, pk[e0 + j])
+                for bits in bl:
+                    pk, sc = store[proj, bits]
+                    s_, c_, _ = fmt[bits][1](md, want_grid_idx=False)
+                    sc[e0 + j].copy_(s_)
+                    fmt[bits][2](c_, pk[e0 + j])
             torch.cuda.synchronize()
+    (Ou, Iu), (Od, Id) = shapes["up"], shapes["down"]
     Xm, top = workloads.moe_tokens()
     tok, exp, offs = workloads.route_pairs(top, E)
     P = tok.size
@@ -342,23 +416,34 @@ def moe_leg(torch, qt, workloads, dev, legs):
     offd = torch.from_numpy(offs).to(dev)
     h = torch.empty((P, Ou), dtype=torch.float32, device=dev)
     yo = torch.empty((P, Od), dtype=torch.float32, device=dev)
-
-    def moe_step(i):
-        qt.qt_matvec_i3_grouped(pu, su, E, Ou, Iu, Xmd, offd, P, pair_row=tokd, Y=h)
-        qt.qt_matvec_i3_grouped(pdn, sdn, E, Od, Id, h, offd, P, Y=yo)
-
-    for i in range(5):
-        moe_step(i)
-    ms = time_launches(moe_step, 20, torch)
     hit = int(np.count_nonzero(np.diff(offs)))
-    per_exp = pu.shape[1] + su[0].numel() * 4 + pdn.shape[1] + sdn[0].numel() * 4
-    mb = hit * per_exp + Xm.nbytes + P * (Ou + Od) * 4 * 2
-    legs["moe_grouped"] = {"ms": round(ms, 4), "experts_hit": hit, "pairs": int(P),
-                           "GB_s": round(mb / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
-                           "frac": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "bytes_per_step": int(mb)}
-    log(f"leg moe: {legs['moe_grouped']}")
-    del pu, su, pdn, sdn, h, yo
+    grouped = {3: qt.qt_matvec_i3_grouped, 4: qt.qt_matvec_i4_grouped}
+
+    steps = []
+    if int3_step:
+        steps.append(("moe_grouped", 3, 3))
+    if int4_steps:
+        steps += [("moe_grouped_int4", 4, 4), ("moe_grouped_int4_up3", 3, 4)]
+    for name, bu, bd in steps:
+        pu, su = store["up", bu]
+        pdn, sdn = store["down", bd]
+
+        def moe_step(i):
+            grouped[bu](pu, su, E, Ou, Iu, Xmd, offd, P, pair_row=tokd, Y=h)
+            grouped[bd](pdn, sdn, E, Od, Id, h, offd, P, Y=yo)
+
+        for i in range(5):
+            moe_step(i)
+        ms = time_launches(moe_step, 20, torch)
+        per_exp = pu.shape[1] + su[0].numel() * 4 + pdn.shape[1] + sdn[0].numel() * 4
+        mb = hit * per_exp + Xm.nbytes + P * (Ou + Od) * 4 * 2
+        legs[name] = {"ms": round(ms, 4), "experts_hit": hit, "pairs": int(P),
+                      "up_bits": bu, "down_bits": bd,
+                      "GB_s": round(mb / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
+                      "frac": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "bytes_per_step": int(mb)}
+        log(f"leg {name}: {legs[name]}")
+    del store, h, yo
 
 
 def prefill_leg(torch, qt, workloads, dev, legs):
