@@ -46,6 +46,14 @@ def lib():
         L.qto_hessian_diag.argtypes = [P, I64, I64, P, P]
         L.qto_rowint_recon.argtypes = [P, I64, I64, I32, P]
         L.qto_dequant_f64.argtypes = [P, P, I64, I64, P]
+        L.qto_hessian_full.argtypes = [P, I64, I64, P]
+        L.qto_gptq_factor.restype = I32
+        L.qto_gptq_factor.argtypes = [P, I64, C.c_double, P]
+        L.qto_gptq_i3.argtypes = [P, I64, I64, P, I32, P, P]
+        L.qto_gptq_replay.argtypes = [P, I64, I64, P, P, P, P, P]
+        L.qto_proxy_terms.argtypes = [P, I64, I64, P, P, P, P, P]
+        for f in ("qto_hessian_full", "qto_gptq_i3", "qto_gptq_replay", "qto_proxy_terms"):
+            getattr(L, f).restype = None
         for f in ("qto_quantize_g64_i4", "qto_pack_i4", "qto_unpack_i4", "qto_matvec_i4_f64",
                   "qto_quantize_g64", "qto_quantize_g64_signed", "qto_pack_i3", "qto_unpack_i3", "qto_matvec_f64",
                   "qto_matmul_f64_sampled", "qto_matvec_f32", "qto_hessian_diag",
@@ -220,3 +228,60 @@ def rowint_recon(W, bits: int = 4):
     out = np.empty((O, I), np.float64)
     lib().qto_rowint_recon(_p(W), O, I, bits, _p(out))
     return out
+
+
+# ---------------------------------------------------------------- GPTQ / LDLQ
+def hessian_full(X):
+    """H [I, I] f64 = sum_t X[t]^T X[t] for X [T, I] f32."""
+    X = _c(X, np.float32)
+    T, I = X.shape
+    H = np.empty((I, I), np.float64)
+    lib().qto_hessian_full(_p(X), T, I, _p(H))
+    return H
+
+
+def gptq_factor(H, damp: float = 0.01):
+    """U [n, n] f64: the upper Cholesky factor of (H + damp*mean(diag H)*I)^-1."""
+    H = _c(H, np.float64)
+    n = H.shape[0]
+    U = np.empty((n, n), np.float64)
+    if lib().qto_gptq_factor(_p(H), n, float(damp), _p(U)) != 0:
+        raise ValueError("matrix is not positive definite")
+    return U
+
+
+def gptq_i3(W, U, block: int = 128):
+    """GPTQ sweep with the int3-g64 rounder: -> (scales [O, G] f32, codes [O, I] int8)."""
+    W = _c(W, np.float32)
+    U = _c(U, np.float32)
+    O, I = W.shape
+    scales = np.empty((O, groups(I)), np.float32)
+    codes = np.empty((O, I), np.int8)
+    lib().qto_gptq_i3(_p(W), O, I, _p(U), block, _p(scales), _p(codes))
+    return scales, codes
+
+
+def gptq_replay(W, U, scales, codes):
+    """-> (column values [O, I] f64 at decision time, group bases [O, G] f64)."""
+    W = _c(W, np.float32)
+    U = _c(U, np.float32)
+    scales = _c(scales, np.float32)
+    codes = _c(codes, np.int8)
+    O, I = W.shape
+    wt = np.empty((O, I), np.float64)
+    base = np.empty((O, groups(I)), np.float64)
+    lib().qto_gptq_replay(_p(W), O, I, _p(U), _p(scales), _p(codes), _p(wt), _p(base))
+    return wt, base
+
+
+def proxy_terms(W, codes, scales, H):
+    """(tr(E H E^T), tr(W H W^T)) in f64 with E = W - s*v; H [I, I] f32."""
+    W = _c(W, np.float32)
+    codes = _c(codes, np.int8)
+    scales = _c(scales, np.float32)
+    H = _c(H, np.float32)
+    O, I = W.shape
+    num = C.c_double()
+    den = C.c_double()
+    lib().qto_proxy_terms(_p(W), O, I, _p(codes), _p(scales), _p(H), C.byref(num), C.byref(den))
+    return num.value, den.value

@@ -9,6 +9,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 #define GROUP 64
 
@@ -416,4 +417,200 @@ void qto_matvec_i4_f64(const uint8_t* packed, const float* scales, int64_t O, in
         y[o] = acc;
         if (absy) absy[o] = aacc;
     }
+}
+
+
+/* ------------------------------------------------------------------ GPTQ / LDLQ
+ * tt-stack issue page, pipeline table: step 1 accumulates the full
+ * H = sum over tokens of X^T X per linear input; step 2 factors H (Cholesky /
+ * inverse, host LAPACK in f32/f64 there); step 3 is the GPTQ/LDLQ column sweep:
+ * serial rounding inside 128-column blocks, then the matmul
+ * W[:, rest] -= E Hinv[blk, rest] carrying each block's scaled rounding errors
+ * E to the later columns.  The "Risks" paragraph gates on the proxy error
+ * tr(E H E^T) / tr(W H W^T).  The page names the algorithm and prints none of
+ * its formulas.  Readings, each stated where it applies:
+ *   - damping: A = H + damp * mean(diag H) * I;
+ *   - Hinv is the upper Cholesky factor U of A^-1 (U^T U = A^-1), the GPTQ
+ *     form of the sweep: for column i, err = (w_i - s q_i) / U[i][i] and every
+ *     later column j takes w_j -= err U[i][j];
+ *   - Q is the int3-g64 rounder with the group scale fixed when the sweep
+ *     reaches the group's first column: absmax/4 of the group's current
+ *     (already updated) values;
+ *   - precision: the factorization in f64; the sweep in f32 as the page's host
+ *     propagator, every in-block update one fused multiply-add in column
+ *     order; the propagation of a finished block summed in f64 and applied
+ *     with one f32 rounding. */
+void qto_hessian_full(const float* X, int64_t T, int64_t I, double* H) {
+    for (int64_t i = 0; i < I; ++i)
+        for (int64_t j = 0; j < I; ++j) H[i * I + j] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        const float* x = X + t * I;
+        for (int64_t i = 0; i < I; ++i) {
+            const double xi = (double)x[i];
+            for (int64_t j = 0; j < I; ++j) H[i * I + j] += xi * (double)x[j];
+        }
+    }
+}
+
+/* U = the upper Cholesky factor of A^-1, A = H + damp * mean(diag H) * I.
+ * With J the reversal, J A J = C C^T (textbook Cholesky, C lower); then
+ * A = V V^T for the upper V = J C J, A^-1 = (V^-1)^T V^-1, and U = V^-1 =
+ * J C^-1 J (upper, positive diagonal: the Cholesky factor).  C^-1 comes from
+ * forward substitution against the identity.  U is written as a full n x n
+ * matrix with zeros below the diagonal.  Returns 0, or -1 when A is not
+ * positive definite. */
+int qto_gptq_factor(const double* H, int64_t n, double damp, double* U) {
+    double mean = 0.0;
+    for (int64_t i = 0; i < n; ++i) mean += H[i * n + i];
+    mean /= (double)n;
+    const double add = damp * mean;
+    double* C = (double*)malloc((size_t)(n * n) * sizeof(double));
+    if (!C) return -1;
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double a = H[(n - 1 - i) * n + (n - 1 - j)];
+            if (i == j) a += add;
+            C[i * n + j] = a;
+        }
+    for (int64_t j = 0; j < n; ++j) {
+        double s = C[j * n + j];
+        for (int64_t k = 0; k < j; ++k) s -= C[j * n + k] * C[j * n + k];
+        if (!(s > 0.0)) {
+            free(C);
+            return -1;
+        }
+        const double cjj = sqrt(s);
+        C[j * n + j] = cjj;
+        for (int64_t i = j + 1; i < n; ++i) {
+            double t = C[i * n + j];
+            for (int64_t k = 0; k < j; ++k) t -= C[i * n + k] * C[j * n + k];
+            C[i * n + j] = t / cjj;
+        }
+    }
+    /* Ci = C^-1, column c: C x = e_c by forward substitution (x_i = 0 for
+     * i < c); then U[i][j] = Ci[n-1-i][n-1-j]. */
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < n; ++j) U[i * n + j] = 0.0;
+    double* x = (double*)malloc((size_t)n * sizeof(double));
+    if (!x) {
+        free(C);
+        return -1;
+    }
+    for (int64_t c = 0; c < n; ++c) {
+        for (int64_t i = c; i < n; ++i) {
+            double t = (i == c) ? 1.0 : 0.0;
+            for (int64_t k = c; k < i; ++k) t -= C[i * n + k] * x[k];
+            x[i] = t / C[i * n + i];
+        }
+        for (int64_t i = c; i < n; ++i) U[(n - 1 - i) * n + (n - 1 - c)] = x[i];
+    }
+    free(x);
+    free(C);
+    return 0;
+}
+
+/* The GPTQ sweep with the int3-g64 rounder, one row at a time (rows are
+ * independent): w holds the row's current values. */
+void qto_gptq_i3(const float* W, int64_t O, int64_t I, const float* U, int block,
+                 float* scales, int8_t* codes) {
+    const int64_t G = qto_groups(I);
+    float* w = (float*)malloc((size_t)I * sizeof(float));
+    float* err = (float*)malloc((size_t)I * sizeof(float));
+    if (!w || !err) {
+        free(w);
+        free(err);
+        return;
+    }
+    for (int64_t o = 0; o < O; ++o) {
+        for (int64_t j = 0; j < I; ++j) w[j] = W[o * I + j];
+        for (int64_t b0 = 0; b0 < I; b0 += block) {
+            const int64_t b1 = (b0 + block < I) ? b0 + block : I;
+            float s = 0.0f;
+            for (int64_t i = b0; i < b1; ++i) {
+                if (i % GROUP == 0) { /* group start: the scale of the current values */
+                    const int64_t n = (I - i < GROUP) ? I - i : GROUP;
+                    float amax = 0.0f;
+                    for (int64_t m = 0; m < n; ++m) {
+                        const float a = fabsf(w[i + m]);
+                        if (a > amax) amax = a;
+                    }
+                    s = amax * 0.25f;
+                    scales[o * G + i / GROUP] = s;
+                }
+                const int q = code_for(w[i], s);
+                codes[o * I + i] = (int8_t)q;
+                const float t = s * (float)q;
+                const float r = w[i] - t;
+                err[i] = r / U[i * I + i];
+                for (int64_t j = i + 1; j < b1; ++j) w[j] = fmaf(-err[i], U[i * I + j], w[j]);
+            }
+            /* the finished block's errors reach every later column */
+            for (int64_t j = b1; j < I; ++j) {
+                double acc = 0.0;
+                for (int64_t k = b0; k < b1; ++k) acc += (double)err[k] * (double)U[k * I + j];
+                w[j] = (float)((double)w[j] - acc);
+            }
+        }
+    }
+    free(w);
+    free(err);
+}
+
+/* The same sweep in f64, unblocked, along given codes and scales: wt[o][i]
+ * receives the value of column i when it is rounded, base[o][g] the
+ * absmax/4 of the group's values when the sweep reaches its first column.  A
+ * sweep that followed the algorithm chose codes that round wt/s (up to the
+ * rounding of its own arithmetic) and scales equal to base. */
+void qto_gptq_replay(const float* W, int64_t O, int64_t I, const float* U,
+                     const float* scales, const int8_t* codes, double* wt_out,
+                     double* base_out) {
+    const int64_t G = qto_groups(I);
+    double* w = (double*)malloc((size_t)I * sizeof(double));
+    if (!w) return;
+    for (int64_t o = 0; o < O; ++o) {
+        for (int64_t j = 0; j < I; ++j) w[j] = (double)W[o * I + j];
+        for (int64_t i = 0; i < I; ++i) {
+            if (i % GROUP == 0) {
+                const int64_t n = (I - i < GROUP) ? I - i : GROUP;
+                double amax = 0.0;
+                for (int64_t m = 0; m < n; ++m) {
+                    const double a = fabs(w[i + m]);
+                    if (a > amax) amax = a;
+                }
+                base_out[o * G + i / GROUP] = amax * 0.25;
+            }
+            wt_out[o * I + i] = w[i];
+            const double e = (w[i] - (double)scales[o * G + i / GROUP] * (double)codes[o * I + i]) /
+                             (double)U[i * I + i];
+            for (int64_t j = i + 1; j < I; ++j) w[j] -= e * (double)U[i * I + j];
+        }
+    }
+    free(w);
+}
+
+/* Proxy terms of the gate: num = sum_o e_o H e_o^T with e = W - s*v (the
+ * dequantized codes), den = sum_o w_o H w_o^T, in f64. */
+void qto_proxy_terms(const float* W, int64_t O, int64_t I, const int8_t* codes,
+                     const float* scales, const float* H, double* num, double* den) {
+    const int64_t G = qto_groups(I);
+    double* e = (double*)malloc((size_t)I * sizeof(double));
+    if (!e) return;
+    double sn = 0.0, sd = 0.0;
+    for (int64_t o = 0; o < O; ++o) {
+        const float* w = W + o * I;
+        for (int64_t i = 0; i < I; ++i)
+            e[i] = (double)w[i] - (double)scales[o * G + i / GROUP] * (double)codes[o * I + i];
+        for (int64_t i = 0; i < I; ++i) {
+            double hn = 0.0, hd = 0.0;
+            for (int64_t j = 0; j < I; ++j) {
+                hn += (double)H[i * I + j] * e[j];
+                hd += (double)H[i * I + j] * (double)w[j];
+            }
+            sn += e[i] * hn;
+            sd += (double)w[i] * hd;
+        }
+    }
+    *num = sn;
+    *den = sd;
+    free(e);
 }

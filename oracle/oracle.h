@@ -110,6 +110,25 @@ void qto_unpack_i4(const uint8_t* packed, int64_t O, int64_t I, int8_t* codes);
 void qto_matvec_i4_f64(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
                        const float* x, double* y, double* absy);
 
+/* GPTQ / LDLQ (tt-stack issue page, pipeline table steps 1-3 and the proxy
+ * gate of its "Risks" paragraph; readings in oracle.c).  H f64 [I x I]. */
+void qto_hessian_full(const float* X, int64_t T, int64_t I, double* H);
+/* U [n x n] f64: the upper Cholesky factor of (H + damp mean(diag H) I)^-1,
+ * zeros below the diagonal; 0 or -1 (not positive definite). */
+int qto_gptq_factor(const double* H, int64_t n, double damp, double* U);
+/* The GPTQ sweep with the int3-g64 rounder; U f32 [I x I]; block a multiple
+ * of 64. */
+void qto_gptq_i3(const float* W, int64_t O, int64_t I, const float* U, int block,
+                 float* scales, int8_t* codes);
+/* f64 replay along given codes/scales: column values at decision time and
+ * the group bases the algorithm would take. */
+void qto_gptq_replay(const float* W, int64_t O, int64_t I, const float* U,
+                     const float* scales, const int8_t* codes, double* wt_out,
+                     double* base_out);
+/* tr(E H E^T) and tr(W H W^T), E = W - s*v. */
+void qto_proxy_terms(const float* W, int64_t O, int64_t I, const int8_t* codes,
+                     const float* scales, const float* H, double* num, double* den);
+
 #ifdef __cplusplus
 }
 #endif

@@ -560,3 +560,164 @@ def test_i4_matvec_f64_against_numpy(O, I):
     ar = np.abs(what * x.astype(np.float64)[None, :]).sum(axis=1)
     assert componentwise_err(y, yr, ar) < 1e-13
     assert np.allclose(a, ar, rtol=1e-13, atol=0)
+
+
+# ---------------------------------------------------------------- GPTQ / LDLQ
+def _correlated_x(T, I, seed):
+    # tokens with correlated features: Z M, M a random mixing matrix plus the
+    # identity, and lognormal column scales (the search workload's recipe)
+    rng = np.random.default_rng(seed)
+    Z = rng.standard_normal((T, I))
+    M = np.eye(I) + 0.3 * rng.standard_normal((I, I)) / np.sqrt(I)
+    c = np.exp(rng.standard_normal(I))
+    return ((Z @ M) * c).astype(np.float32)
+
+
+def test_hessian_full_against_numpy_and_the_diagonal():
+    X = _correlated_x(300, 72, 1)
+    H = oracle.hessian_full(X)
+    X64 = X.astype(np.float64)
+    assert np.allclose(H, X64.T @ X64, rtol=1e-12, atol=1e-9)
+    assert np.array_equal(H, H.T)
+    d = oracle.hessian_diag(X)
+    assert np.allclose(np.diag(H), d, rtol=1e-6)
+
+
+def test_gptq_factor_two_by_two_closed_form():
+    # A = [[5, 2], [2, 4]] (no damping): A^-1 = [[4, -2], [-2, 5]] / 16, whose
+    # upper Cholesky factor is U = [[1/2, -1/4], [0, 1/2]] (U^T U = A^-1)
+    U = oracle.gptq_factor(np.array([[5.0, 2.0], [2.0, 4.0]]), 0.0)
+    assert U.tolist() == [[0.5, -0.25], [0.0, 0.5]]
+
+
+@pytest.mark.parametrize("damp", [0.0, 0.01])
+def test_gptq_factor_against_numpy(damp):
+    X = _correlated_x(400, 96, 2)
+    H = X.astype(np.float64).T @ X.astype(np.float64)
+    U = oracle.gptq_factor(H, damp)
+    A = H + damp * np.mean(np.diag(H)) * np.eye(96)
+    assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
+    Un = np.linalg.cholesky(np.linalg.inv(A)).T
+    assert np.abs(U - Un).max() <= 1e-9 * np.abs(Un).max()
+    assert np.abs(U.T @ U @ A - np.eye(96)).max() <= 1e-9
+
+
+def test_gptq_factor_rejects_an_indefinite_matrix():
+    with pytest.raises(ValueError):
+        oracle.gptq_factor(np.array([[1.0, 2.0], [2.0, 1.0]]), 0.0)
+
+
+def test_gptq_with_a_diagonal_hessian_is_plain_rtn():
+    # a diagonal H has a diagonal U: nothing propagates, every column is
+    # rounded as it is
+    W = workloads.generic_weights(20, 300, seed=8)
+    H = np.diag(np.exp(np.random.default_rng(3).standard_normal(300)))
+    U = oracle.gptq_factor(H, 0.01)
+    assert not np.triu(U, 1).any()
+    s, c = oracle.gptq_i3(W, U.astype(np.float32), 128)
+    s0, c0, _ = oracle.quantize_g64(W)
+    assert np.array_equal(s.view(np.uint32), s0.view(np.uint32))
+    assert np.array_equal(c, c0)
+
+
+def test_gptq_two_column_worked_example():
+    # A = [[5, 2], [2, 4]]: U = [[1/2, -1/4], [0, 1/2]].  W = [1, 5/16]: the
+    # group scale is absmax/4 = 1/4; column 0 rounds 4 -> clamps to 3, scaled
+    # error (1 - 3/4) / (1/2) = 1/2; column 1 becomes 5/16 - 1/2 * (-1/4) =
+    # 7/16 = 1.75 s -> code 2 (plain RTN would give 1)
+    U = oracle.gptq_factor(np.array([[5.0, 2.0], [2.0, 4.0]]), 0.0).astype(np.float32)
+    W = np.array([[1.0, 0.3125]], np.float32)
+    s, c = oracle.gptq_i3(W, U, 128)
+    assert s[0, 0] == 0.25
+    assert c.tolist() == [[3, 2]]
+    assert oracle.quantize_g64(W)[1].tolist() == [[3, 1]]
+
+
+def _classical_gptq(W, U):
+    """The GPTQ sweep written out in numpy f64, unblocked (scales rounded to
+    f32 as the rounder stores them): -> scales, codes, decision values."""
+    Wc = W.astype(np.float64).copy()
+    O, I = W.shape
+    G = (I + 63) // 64
+    codes = np.zeros((O, I), np.int8)
+    scales = np.zeros((O, G), np.float32)
+    vals = np.zeros((O, I))
+    s = None
+    for i in range(I):
+        if i % 64 == 0:
+            s = (np.abs(Wc[:, i:i + 64]).max(axis=1) * 0.25).astype(np.float32)
+            scales[:, i // 64] = s
+        sd = s.astype(np.float64)
+        vals[:, i] = Wc[:, i]
+        q = np.where(sd > 0, np.clip(np.rint(Wc[:, i] / np.where(sd > 0, sd, 1)), -4, 3), 0)
+        codes[:, i] = q
+        err = (Wc[:, i] - sd * q) / U[i, i]
+        Wc[:, i + 1:] -= err[:, None] * U[i, i + 1:][None, :]
+    return scales, codes, vals
+
+
+def test_gptq_replay_agrees_with_a_numpy_sweep():
+    X = _correlated_x(500, 160, 4)
+    H = X.astype(np.float64).T @ X.astype(np.float64)
+    U = oracle.gptq_factor(H, 0.01)
+    W = workloads.generic_weights(24, 160, seed=9)
+    sc, cc, vals = _classical_gptq(W, U)
+    wt, base = oracle.gptq_replay(W, U.astype(np.float32), sc, cc)
+    assert np.abs(wt - vals).max() <= 1e-5 * np.abs(W).max()
+    assert np.allclose(base, sc, rtol=1e-5)
+
+
+def _valid_against_replay(W, U32, s, c, tol=1e-4):
+    """Every code rounds its column's replayed value and every scale is the
+    replayed group base, up to f32-versus-f64 differences of the sweep."""
+    wt, base = oracle.gptq_replay(W, U32, s, c)
+    I = W.shape[1]
+    sfull = np.repeat(s.astype(np.float64), 64, axis=1)[:, :I]
+    assert np.allclose(s, base, rtol=1e-4, atol=1e-30), "scales are not the group bases"
+    y = np.where(sfull > 0, wt / np.where(sfull > 0, sfull, 1), 0)
+    cf = c.astype(np.float64)
+    inner = (cf > -4) & (cf < 3)
+    assert np.all(np.abs(y - cf)[inner] <= 0.5 + tol)
+    assert np.all(y[cf == 3] >= 2.5 - tol) and np.all(y[cf == -4] <= -3.5 + tol)
+
+
+@pytest.mark.parametrize("O,I", [(16, 64), (12, 200), (8, 333), (10, 512)])
+def test_gptq_sweep_follows_the_algorithm(O, I):
+    X = _correlated_x(600, I, 5 + I)
+    H = X.astype(np.float64).T @ X.astype(np.float64)
+    U32 = oracle.gptq_factor(H, 0.01).astype(np.float32)
+    W = workloads.generic_weights(O, I, seed=I)
+    s, c = oracle.gptq_i3(W, U32, 128)
+    _valid_against_replay(W, U32, s, c)
+
+
+def test_gptq_beats_rtn_on_correlated_inputs():
+    for seed in (6, 7, 8):
+        X = _correlated_x(800, 256, seed)
+        H = X.astype(np.float64).T @ X.astype(np.float64)
+        U = oracle.gptq_factor(H, 0.01)
+        W = workloads.generic_weights(32, 256, seed=seed)
+        s, c = oracle.gptq_i3(W, U.astype(np.float32), 128)
+        s0, c0, _ = oracle.quantize_g64(W)
+        H32 = H.astype(np.float32)
+        n1, d1 = oracle.proxy_terms(W, c, s, H32)
+        n0, d0 = oracle.proxy_terms(W, c0, s0, H32)
+        assert d1 == d0
+        assert n1 < n0, (seed, n1 / d1, n0 / d0)
+
+
+def test_proxy_terms_against_numpy_and_the_weighted_objective():
+    W = workloads.generic_weights(6, 130, seed=10)
+    s, c, _ = oracle.quantize_g64(W)
+    rng = np.random.default_rng(11)
+    B = rng.standard_normal((130, 130)).astype(np.float32)
+    H = (B @ B.T).astype(np.float32)
+    num, den = oracle.proxy_terms(W, c, s, H)
+    E = W.astype(np.float64) - np.repeat(s.astype(np.float64), 64, axis=1)[:, :130] * c
+    H64 = H.astype(np.float64)
+    assert np.isclose(num, np.einsum("oi,ij,oj->", E, H64, E), rtol=1e-12)
+    assert np.isclose(den, np.einsum("oi,ij,oj->", W.astype(np.float64), H64, W), rtol=1e-12)
+    # diagonal H: the numerator is the search objective summed over groups
+    d = np.exp(rng.standard_normal(130)).astype(np.float32)
+    num_d, _ = oracle.proxy_terms(W, c, s, np.diag(d))
+    assert np.isclose(num_d, np.sum(E ** 2 * d[None, :]), rtol=1e-12)
