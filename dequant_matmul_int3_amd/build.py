@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 SO = os.path.join(PKG, "libqt.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "grouped.hip", "gemm.hip", "hessian.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "grouped.hip", "gemm.hip", "hessian.hip",
+           "syrk.hip", "factor.hip", "gptq.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -345,4 +345,113 @@ qt_status qt_matvec_i4_grouped(const uint8_t* packed, const float* scales, int32
                         stream, 4);
 }
 
+// ---------------------------------------------------------------- GPTQ
+size_t qt_hessian_full_workspace_bytes(int64_t T, int64_t I, qt_dtype xt) {
+    if (T < 1 || I < 1 || I > 65535 * 128LL || (xt != QT_F32 && xt != QT_BF16)) return 0;
+    const int64_t b = mul3(qt::hessian_full_rows(I), qt::hessian_full_tokens(T),
+                           xt == QT_F32 ? 4 : 2);
+    return b < 0 ? 0 : (size_t)b;
+}
+
+qt_status qt_hessian_full(const void* X, qt_dtype xt, int64_t T, int64_t I, float* H,
+                          int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+    if (!X || !H || !workspace) return QT_ERR_NULL;
+    if (xt != QT_F32 && xt != QT_BF16) return QT_ERR_DTYPE;
+    if (T < 1 || I < 1 || I > 65535 * 128LL) return QT_ERR_SHAPE;
+    const int64_t esz = xt == QT_F32 ? 4 : 2;
+    const int64_t xb = mul3(T, I, esz), hb = mul3(I, I, 4);
+    if (xb < 0 || hb < 0) return QT_ERR_SHAPE;
+    if (accumulate != 0 && accumulate != 1) return QT_ERR_ARG;
+    const size_t need = qt_hessian_full_workspace_bytes(T, I, xt);
+    if (need == 0) return QT_ERR_SHAPE;
+    if (ws_bytes < need) return QT_ERR_WORKSPACE;
+    if (!aligned(X, 16) || !aligned(H, 4) || !aligned(workspace, 16)) return QT_ERR_ALIGN;
+    if (overlap(H, hb, X, xb) || overlap(workspace, (int64_t)need, X, xb) ||
+        overlap(workspace, (int64_t)need, H, hb))
+        return QT_ERR_ALIAS;
+    return launched(qt::launch_hessian_full(X, xt == QT_BF16, T, I, H, accumulate, workspace,
+                                            as_stream(stream)));
+}
+
+size_t qt_gptq_factor_workspace_bytes(int64_t I) {
+    if (I < 1 || I > 65535) return 0;
+    return qt::gptq_factor_workspace(I);
+}
+
+qt_status qt_gptq_factor(const float* H, int64_t I, double damp, float* U, int32_t* info,
+                         void* workspace, size_t ws_bytes, void* stream) {
+    if (!H || !U || !info || !workspace) return QT_ERR_NULL;
+    if (I < 1 || I > 65535) return QT_ERR_SHAPE;
+    if (!(damp >= 0.0) || !(damp < 1e30)) return QT_ERR_ARG;
+    const size_t need = qt_gptq_factor_workspace_bytes(I);
+    if (ws_bytes < need) return QT_ERR_WORKSPACE;
+    if (!aligned(H, 4) || !aligned(U, 4) || !aligned(info, 4) || !aligned(workspace, 16))
+        return QT_ERR_ALIGN;
+    const int64_t hb = I * I * 4;
+    if (overlap(U, hb, H, hb) || overlap(info, 4, H, hb) || overlap(info, 4, U, hb) ||
+        overlap(workspace, (int64_t)need, H, hb) || overlap(workspace, (int64_t)need, U, hb) ||
+        overlap(workspace, (int64_t)need, info, 4))
+        return QT_ERR_ALIAS;
+    return launched(qt::launch_gptq_factor(H, I, damp, U, info, workspace, as_stream(stream)));
+}
+
+size_t qt_gptq_workspace_bytes(int64_t O, int64_t I) {
+    if (O < 1 || I < 1 || I > QT_MAX_I) return 0;
+    if (mul3(O, I + 128, 4) < 0) return 0;
+    return qt::gptq_workspace(O, I);
+}
+
+qt_status qt_gptq_i3(const float* W, int64_t O, int64_t I, const float* U, float* scales,
+                     int8_t* codes, void* workspace, size_t ws_bytes, void* stream) {
+    if (!W || !U || !scales || !codes || !workspace) return QT_ERR_NULL;
+    qt_status st = shape_ok(O, I);
+    if (st != QT_OK) return st;
+    if (mul3(I, I, 4) < 0 || (O + 63) / 64 > 0x7fffffffLL) return QT_ERR_SHAPE;
+    const size_t need = qt_gptq_workspace_bytes(O, I);
+    if (need == 0) return QT_ERR_SHAPE;
+    if (ws_bytes < need) return QT_ERR_WORKSPACE;
+    if (!aligned(W, 4) || !aligned(U, 4) || !aligned(scales, 4) || !aligned(workspace, 16))
+        return QT_ERR_ALIGN;
+    const int64_t G = qt_groups(I);
+    const int64_t wb = O * I * 4, ub = I * I * 4, sb = O * G * 4, cb = O * I;
+    const void* outs[3] = {scales, codes, workspace};
+    const int64_t ob[3] = {sb, cb, (int64_t)need};
+    for (int k = 0; k < 3; ++k)
+        if (overlap(outs[k], ob[k], W, wb) || overlap(outs[k], ob[k], U, ub)) return QT_ERR_ALIAS;
+    if (overlap(scales, sb, codes, cb) || overlap(scales, sb, workspace, (int64_t)need) ||
+        overlap(codes, cb, workspace, (int64_t)need))
+        return QT_ERR_ALIAS;
+    return launched(qt::launch_gptq_i3(W, O, I, U, scales, codes, workspace, as_stream(stream)));
+}
+
+size_t qt_gptq_proxy_workspace_bytes(int64_t O, int64_t I) {
+    if (O < 1 || I < 1) return 0;
+    const int64_t Mp = qt::proxy_pad(2 * O), Kp = qt::proxy_pad(I);
+    if (Mp > 65535 || Kp > 65535) return 0;
+    return qt::gptq_proxy_workspace(O, I);
+}
+
+qt_status qt_gptq_proxy(const float* W, const uint8_t* packed, const float* scales, int64_t O,
+                        int64_t I, const float* H, double* terms, void* workspace,
+                        size_t ws_bytes, void* stream) {
+    if (!W || !packed || !scales || !H || !terms || !workspace) return QT_ERR_NULL;
+    qt_status st = shape_ok(O, I);
+    if (st != QT_OK) return st;
+    const size_t need = qt_gptq_proxy_workspace_bytes(O, I);
+    if (need == 0) return QT_ERR_SHAPE;
+    if (ws_bytes < need) return QT_ERR_WORKSPACE;
+    if (!aligned(W, 4) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(H, 4) ||
+        !aligned(terms, 8) || !aligned(workspace, 16))
+        return QT_ERR_ALIGN;
+    const int64_t G = qt_groups(I);
+    const int64_t ins[4] = {O * I * 4, O * G * kGroupBytes, O * G * 4, I * I * 4};
+    const void* inp[4] = {W, packed, scales, H};
+    for (int k = 0; k < 4; ++k)
+        if (overlap(terms, 16, inp[k], ins[k]) || overlap(workspace, (int64_t)need, inp[k], ins[k]))
+            return QT_ERR_ALIAS;
+    if (overlap(terms, 16, workspace, (int64_t)need)) return QT_ERR_ALIAS;
+    return launched(qt::launch_gptq_proxy(W, packed, scales, O, I, H, terms, workspace,
+                                          as_stream(stream)));
+}
+
 }  // extern "C"

@@ -50,6 +50,25 @@ hipError_t launch_gemm_mfma(const uint8_t* packed, const float* scales, int64_t 
                             int64_t I, const uint16_t* X, int64_t B, float* Y,
                             hipStream_t s);
 
+// Full Hessian, GPTQ factor, sweep and proxy (syrk.hip, factor.hip, gptq.hip).
+int64_t hessian_full_rows(int64_t I);
+int64_t hessian_full_tokens(int64_t T);
+hipError_t launch_hessian_full(const void* X, bool bf16, int64_t T, int64_t I, float* H,
+                               int accumulate, void* workspace, hipStream_t s);
+hipError_t launch_rowdot_nt(const float* A, int64_t Mp, const float* B, int64_t Np, int64_t Kp,
+                            float* part, hipStream_t s);
+size_t gptq_factor_workspace(int64_t n);
+hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, int32_t* info,
+                              void* workspace, hipStream_t s);
+size_t gptq_workspace(int64_t O, int64_t I);
+hipError_t launch_gptq_i3(const float* W, int64_t O, int64_t I, const float* U, float* scales,
+                          int8_t* codes, void* workspace, hipStream_t s);
+int64_t proxy_pad(int64_t n);
+size_t gptq_proxy_workspace(int64_t O, int64_t I);
+hipError_t launch_gptq_proxy(const float* W, const uint8_t* packed, const float* scales,
+                             int64_t O, int64_t I, const float* H, double* terms,
+                             void* workspace, hipStream_t s);
+
 int hessian_slabs(int64_t T, int64_t I);
 hipError_t launch_hessian_diag(const void* X, bool bf16, int64_t T, int64_t I, float* d,
                                int accumulate, float* workspace, hipStream_t s);

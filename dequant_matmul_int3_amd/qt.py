@@ -44,6 +44,18 @@ _SIGS = {
                                        C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
                                        C.c_void_p, C.c_void_p]),
     "qt_packed_bytes_i4": (C.c_int64, [C.c_int64, C.c_int64]),
+    "qt_hessian_full_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int]),
+    "qt_hessian_full": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_void_p, C.c_int,
+                                  C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qt_gptq_factor_workspace_bytes": (C.c_size_t, [C.c_int64]),
+    "qt_gptq_factor": (C.c_int, [C.c_void_p, C.c_int64, C.c_double, C.c_void_p, C.c_void_p,
+                                 C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qt_gptq_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
+    "qt_gptq_i3": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
+                             C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qt_gptq_proxy_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
+    "qt_gptq_proxy": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
+                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qt_quantize_g64_i4": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
                                      C.c_float, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p]),
@@ -275,3 +287,64 @@ def qt_matvec_i4_grouped(packed, scales, E: int, O: int, I: int, X, expert_offse
     """qt_matvec_i3_grouped for grouped int4 experts."""
     return _grouped("qt_matvec_i4_grouped", packed, scales, E, O, I, X, expert_offsets, P,
                     pair_row, Y, stream)
+
+
+# ---------------------------------------------------------------- GPTQ
+def _ws(nbytes, device, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def qt_hessian_full(X, H=None, accumulate: bool = False, workspace=None, stream=None):
+    """H [I, I] f32 (+)= X^T X for X [T, I] f32 or bf16."""
+    T, I = X.shape
+    xt = QT_BF16 if X.dtype == torch.bfloat16 else QT_F32 if X.dtype == torch.float32 else -1
+    if H is None:
+        H = torch.empty((I, I), dtype=torch.float32, device=X.device)
+    need = int(lib().qt_hessian_full_workspace_bytes(T, I, xt if xt >= 0 else 0))
+    workspace, wsb = _ws(need, X.device, workspace)
+    dev = _dev(X, H, workspace)
+    _check(lib().qt_hessian_full(_ptr(X), xt, T, I, _ptr(H), int(accumulate), _ptr(workspace),
+                                 wsb, _stream(stream, dev)), "qt_hessian_full")
+    return H
+
+
+def qt_gptq_factor(H, damp: float = 0.01, U=None, info=None, workspace=None, stream=None):
+    """-> (U [I, I] f32 upper Cholesky factor of the damped H^-1, info int32 [1])."""
+    I = H.shape[0]
+    if U is None:
+        U = torch.empty((I, I), dtype=torch.float32, device=H.device)
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=H.device)
+    workspace, wsb = _ws(lib().qt_gptq_factor_workspace_bytes(I), H.device, workspace)
+    dev = _dev(H, U, info, workspace)
+    _check(lib().qt_gptq_factor(_ptr(H), I, float(damp), _ptr(U), _ptr(info), _ptr(workspace),
+                                wsb, _stream(stream, dev)), "qt_gptq_factor")
+    return U, info
+
+
+def qt_gptq_i3(W, U, scales=None, codes=None, workspace=None, stream=None):
+    """GPTQ sweep: W [O, I] f32, U [I, I] -> (scales [O, G] f32, codes [O, I] int8)."""
+    O, I = W.shape
+    if scales is None:
+        scales = torch.empty((O, qt_groups(I)), dtype=torch.float32, device=W.device)
+    if codes is None:
+        codes = torch.empty((O, I), dtype=torch.int8, device=W.device)
+    workspace, wsb = _ws(lib().qt_gptq_workspace_bytes(O, I), W.device, workspace)
+    dev = _dev(W, U, scales, codes, workspace)
+    _check(lib().qt_gptq_i3(_ptr(W), O, I, _ptr(U), _ptr(scales), _ptr(codes), _ptr(workspace),
+                            wsb, _stream(stream, dev)), "qt_gptq_i3")
+    return scales, codes
+
+
+def qt_gptq_proxy(W, packed, scales, H, terms=None, workspace=None, stream=None):
+    """-> terms [2] f64 on the device: (tr(E H E^T), tr(W H W^T))."""
+    O, I = W.shape
+    if terms is None:
+        terms = torch.empty(2, dtype=torch.float64, device=W.device)
+    workspace, wsb = _ws(lib().qt_gptq_proxy_workspace_bytes(O, I), W.device, workspace)
+    dev = _dev(W, packed, scales, H, terms, workspace)
+    _check(lib().qt_gptq_proxy(_ptr(W), _ptr(packed), _ptr(scales), O, I, _ptr(H), _ptr(terms),
+                               _ptr(workspace), wsb, _stream(stream, dev)), "qt_gptq_proxy")
+    return terms

@@ -262,6 +262,77 @@ qt_status qt_matvec_i4_grouped(const uint8_t* packed, const float* scales,
                                const int32_t* expert_offsets, int32_t P,
                                float* Y, void* stream);
 
+/*
+ * GPTQ with the int3-g64 rounder (the tt-stack issue page, pipeline table:
+ * step 1 the full H = sum_t X^T X per linear input, fp32 accumulation on the
+ * device; step 2 a Cholesky / inverse of H; step 3 the GPTQ/LDLQ column
+ * sweep, serial rounding inside 128-column blocks and then the matmul
+ * W[:, rest] -= E Hinv[blk, rest]; the "Risks" paragraph's proxy error
+ * tr(E H E^T) / tr(W H W^T)).  The page prints no formulas; this library
+ * reads them as:
+ *   A = H + damp * mean(diag H) * I;  U = the upper Cholesky factor of A^-1;
+ *   per row, column by column: at a group's first column the group scale
+ *   s = absmax/4 of the group's current values; q = clamp(rne(w/s), -4, 3)
+ *   (IEEE division; 0 when s == 0); err = (w - s q) / U[i][i]; every later
+ *   column j takes w_j -= err U[i][j] (inside a 128-column block one fused
+ *   multiply-add per update in column order; from one block to the later
+ *   columns a matrix product in f32 on the matrix cores).
+ */
+
+/*
+ * Full Hessian: H [I x I] f32 (both triangles, exactly symmetric) = sum over
+ * the T rows of X of x^T x, or H += that (accumulate = 1).  X [T x I] f32 or
+ * bf16 (16-byte aligned).  bf16 products are exact (f32 sums); f32 inputs use
+ * the f32 matrix cores.  workspace: qt_hessian_full_workspace_bytes(T, I, xt)
+ * bytes (16-byte aligned; holds the transposed, padded X).  I <= 8388480.
+ */
+size_t qt_hessian_full_workspace_bytes(int64_t T, int64_t I, qt_dtype xt);
+qt_status qt_hessian_full(const void* X, qt_dtype xt, int64_t T, int64_t I, float* H,
+                          int accumulate, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * GPTQ factor: U [I x I] f32 = the upper Cholesky factor of
+ * (H + damp * mean(diag H) * I)^-1 (zeros below the diagonal), computed in
+ * f64 on the device.  *info (device int32) = 0 on success, else the 1-based
+ * index of the first non-positive pivot of the reversed matrix (the result is
+ * then not a factor of A).  damp >= 0 (0.01 is the usual choice).
+ * workspace: qt_gptq_factor_workspace_bytes(I) bytes (about 8 I^2).
+ * I <= 65535.
+ */
+size_t qt_gptq_factor_workspace_bytes(int64_t I);
+qt_status qt_gptq_factor(const float* H, int64_t I, double damp, float* U,
+                         int32_t* info, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * GPTQ sweep: W [O x I] f32 (not modified), U from qt_gptq_factor ->
+ * scales [O x G] f32 and codes [O x I] int8 in [-4, 3] (pack with
+ * qt_pack_i3).  Inside a 128-column block the arithmetic is the exact f32
+ * sequence stated above (a sweep with I <= 128 is bit-exact against it); the
+ * propagation between blocks sums in f32, so codes near a rounding boundary
+ * may differ from another implementation's.  workspace:
+ * qt_gptq_workspace_bytes(O, I) bytes (the current weights and the block
+ * errors, (O*I + 128*O) * 4).
+ */
+size_t qt_gptq_workspace_bytes(int64_t O, int64_t I);
+qt_status qt_gptq_i3(const float* W, int64_t O, int64_t I, const float* U,
+                     float* scales, int8_t* codes, void* workspace,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * Proxy error terms: terms[0] = tr(E H E^T), terms[1] = tr(W H W^T) (device
+ * f64 [2]) with E = W - s*v, the packed int3-g64 weights decoded; products on
+ * the f32 matrix cores, per-row partials and totals summed in a fixed order.
+ * The gate's ratio is terms[0] / terms[1].  workspace:
+ * qt_gptq_proxy_workspace_bytes(O, I) bytes; 2*O and I padded to 128 must not
+ * exceed 65535.
+ */
+size_t qt_gptq_proxy_workspace_bytes(int64_t O, int64_t I);
+qt_status qt_gptq_proxy(const float* W, const uint8_t* packed, const float* scales,
+                        int64_t O, int64_t I, const float* H, double* terms,
+                        void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,170 @@
+"""GPTQ with the int3-g64 rounder on the GPU against the CPU oracle, through
+the C ABI: the full Hessian, the damped inverse-Cholesky factor, the column
+sweep (bit-exact inside one 128-column block; across blocks every code must
+round its column's replayed value and the proxy error must agree within the
+1 % gate), and the proxy terms."""
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_int3_amd as qt
+import oracle
+import workloads
+from tests.gpu_util import bits, dev, dev_bf16, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def correlated_x(T, I, seed):
+    # correlated features with lognormal column scales (the search workload's
+    # recipe plus a random mixing)
+    rng = workloads.rng_for("generic", 7000 + seed, T, I)
+    Z = rng.standard_normal((T, I))
+    M = np.eye(I) + 0.3 * rng.standard_normal((I, I)) / np.sqrt(I)
+    c = np.exp(rng.standard_normal(I))
+    return ((Z @ M) * c).astype(np.float32)
+
+
+# ---------------------------------------------------------------- full Hessian
+@pytest.mark.parametrize("T,I", [(100, 64), (300, 200), (1000, 333), (64, 1), (129, 513),
+                                 (7, 130)])
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+def test_hessian_full(T, I, xt):
+    X = correlated_x(T, I, T + I)
+    say(f"hessian_full T={T} I={I} {xt}")
+    if xt == "bf16":
+        Xb = workloads.bf16_bits_rne(X)
+        Xd = dev_bf16(Xb)
+        Xf = workloads.bf16_bits_to_f32(Xb)
+    else:
+        Xd = dev(X)
+        Xf = X
+    H = host(qt.qt_hessian_full(Xd))
+    Href = oracle.hessian_full(Xf)
+    A = np.abs(Xf.astype(np.float64))
+    bound = A.T @ A
+    err = np.abs(H.astype(np.float64) - Href) / np.maximum(bound, 1e-300)
+    say(f"  max componentwise err {err.max():.3e}")
+    assert err.max() <= 2e-5
+    assert np.array_equal(bits(H), bits(np.ascontiguousarray(H.T))), "not exactly symmetric"
+    # accumulate: H + X^T X
+    H2 = host(qt.qt_hessian_full(Xd, H=qt.qt_hessian_full(Xd), accumulate=True))
+    err2 = np.abs(H2.astype(np.float64) - 2 * Href) / np.maximum(2 * bound, 1e-300)
+    assert err2.max() <= 2e-5
+
+
+# ---------------------------------------------------------------- factor
+@pytest.mark.parametrize("I,damp", [(64, 0.01), (100, 0.01), (200, 0.0), (333, 0.01), (1, 0.01),
+                                    (129, 0.1)])
+def test_gptq_factor(I, damp):
+    X = correlated_x(4 * I + 50, I, I)
+    H = (X.astype(np.float64).T @ X.astype(np.float64)).astype(np.float32)
+    say(f"gptq_factor I={I} damp={damp}")
+    Ud, info = qt.qt_gptq_factor(dev(H), damp)
+    U, info = host(Ud), host(info)
+    assert info[0] == 0
+    Uref = oracle.gptq_factor(H.astype(np.float64), damp)
+    err = np.abs(U.astype(np.float64) - Uref).max() / np.abs(Uref).max()
+    say(f"  max err / max |U| {err:.3e}")
+    assert err <= 1e-6
+    assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
+
+
+def test_gptq_factor_reports_an_indefinite_matrix():
+    # [[1, 2], [2, 1]] reversed is itself: the first pivot is 1, the second
+    # 1 - 2*2/1 = -3, so the factorization fails at column 2
+    H = np.array([[1.0, 2.0], [2.0, 1.0]], np.float32)
+    _, info = qt.qt_gptq_factor(dev(H), 0.0)
+    assert host(info)[0] == 2
+
+
+# ---------------------------------------------------------------- sweep
+def _factor32(I, seed, damp=0.01):
+    X = correlated_x(4 * I + 64, I, seed)
+    H = (X.astype(np.float64).T @ X.astype(np.float64))
+    return H.astype(np.float32), oracle.gptq_factor(H, damp).astype(np.float32)
+
+
+@pytest.mark.parametrize("O,I", [(1, 1), (64, 63), (100, 64), (70, 65), (64, 100), (130, 128),
+                                 (5, 128)])
+def test_gptq_sweep_one_block_is_bit_exact(O, I):
+    _, U = _factor32(I, 11 + I)
+    W = workloads.generic_weights(O, I, seed=O + I)
+    say(f"gptq one block O={O} I={I}")
+    sd, cd = qt.qt_gptq_i3(dev(W), dev(U))
+    s, c = host(sd), host(cd)
+    so, co = oracle.gptq_i3(W, U, 128)
+    assert np.array_equal(bits(s), bits(so)), "scales differ"
+    assert np.array_equal(c, co), "codes differ"
+
+
+def _replay_valid(W, U, s, c, tol=1e-3):
+    wt, base = oracle.gptq_replay(W, U, s, c)
+    I = W.shape[1]
+    assert np.allclose(s, base, rtol=1e-3, atol=1e-30), "scales are not the group bases"
+    sf = np.repeat(s.astype(np.float64), 64, axis=1)[:, :I]
+    y = np.where(sf > 0, wt / np.where(sf > 0, sf, 1), 0)
+    cf = c.astype(np.float64)
+    inner = (cf > -4) & (cf < 3)
+    assert np.all(np.abs(y - cf)[inner] <= 0.5 + tol)
+    assert np.all(y[cf == 3] >= 2.5 - tol) and np.all(y[cf == -4] <= -3.5 + tol)
+
+
+@pytest.mark.parametrize("O,I", [(64, 256), (40, 333), (100, 1000), (3, 129)])
+def test_gptq_sweep_follows_the_algorithm(O, I):
+    H, U = _factor32(I, 21 + I)
+    W = workloads.generic_weights(O, I, seed=3 * I)
+    say(f"gptq sweep O={O} I={I}")
+    sd, cd = qt.qt_gptq_i3(dev(W), dev(U))
+    s, c = host(sd), host(cd)
+    _replay_valid(W, U, s, c)
+    so, co = oracle.gptq_i3(W, U, 128)
+    agree = np.mean(c == co)
+    n1, d1 = oracle.proxy_terms(W, c, s, H)
+    n0, d0 = oracle.proxy_terms(W, co, so, H)
+    say(f"  code agreement {agree:.5f}, proxy {n1 / d1:.5f} vs oracle {n0 / d0:.5f}")
+    assert agree >= 0.99
+    assert abs(n1 / n0 - 1.0) <= 0.01
+
+
+# ---------------------------------------------------------------- proxy
+@pytest.mark.parametrize("O,I", [(8, 64), (33, 200), (64, 1000), (1, 1)])
+def test_gptq_proxy_terms(O, I):
+    X = correlated_x(3 * I + 10, I, 31 + I)
+    H = (X.astype(np.float64).T @ X.astype(np.float64)).astype(np.float32)
+    W = workloads.generic_weights(O, I, seed=5 + I)
+    so, co, _ = oracle.quantize_g64(W)
+    po = oracle.pack_i3(co)
+    say(f"gptq proxy O={O} I={I}")
+    t = host(qt.qt_gptq_proxy(dev(W), dev(po), dev(so), dev(H)))
+    num, den = oracle.proxy_terms(W, co, so, H)
+    say(f"  num {t[0]:.6e} vs {num:.6e}, den {t[1]:.6e} vs {den:.6e}")
+    assert abs(t[0] - num) <= 1e-4 * abs(num) + 1e-30
+    assert abs(t[1] - den) <= 1e-4 * abs(den) + 1e-30
+
+
+def test_gptq_pipeline_end_to_end_beats_rtn():
+    # X -> H -> U -> sweep -> pack -> proxy, all on the GPU, against the
+    # oracle's pipeline on the same X and against plain RTN
+    T, O, I = 2048, 96, 384
+    X = correlated_x(T, I, 77)
+    Xb = workloads.bf16_bits_rne(X)
+    Xf = workloads.bf16_bits_to_f32(Xb)
+    W = workloads.generic_weights(O, I, seed=78)
+    say("gptq end to end")
+    Hd = qt.qt_hessian_full(dev_bf16(Xb))
+    Ud, info = qt.qt_gptq_factor(Hd, 0.01)
+    Wd = dev(W)
+    sd, cd = qt.qt_gptq_i3(Wd, Ud)
+    pd = qt.qt_pack_i3(cd)
+    t = host(qt.qt_gptq_proxy(Wd, pd, sd, Hd))
+    assert host(info)[0] == 0
+    s0, c0, _ = qt.qt_quantize_g64(Wd)
+    t0 = host(qt.qt_gptq_proxy(Wd, qt.qt_pack_i3(c0), s0, Hd))
+    H = oracle.hessian_full(Xf)
+    U = oracle.gptq_factor(H, 0.01).astype(np.float32)
+    so, co = oracle.gptq_i3(W, U, 128)
+    num, den = oracle.proxy_terms(W, co, so, H.astype(np.float32))
+    say(f"  proxy GPU {t[0] / t[1]:.5f}, oracle {num / den:.5f}, RTN {t0[0] / t0[1]:.5f}")
+    assert abs((t[0] / t[1]) / (num / den) - 1.0) <= 0.01
+    assert t[0] < t0[0]
