@@ -246,7 +246,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-LEG_NAMES = ["quant", "search", "moe", "prefill", "int4", "moe_int4"]
+LEG_NAMES = ["quant", "search", "moe", "prefill", "int4", "moe_int4", "gptq"]
 
 
 def run_legs(torch, qt, workloads, dev, which, args):
@@ -265,7 +265,79 @@ def run_legs(torch, qt, workloads, dev, which, args):
         prefill_leg(torch, qt, workloads, dev, legs)
     if "int4" in which:
         int4_leg(torch, qt, workloads, dev, legs, args)
+    if "gptq" in which:
+        gptq_leg(torch, qt, workloads, dev, legs)
     return legs
+
+
+F32_MFMA_PEAK_TFLOPS = 157.3   # dense f32 matrix cores
+F64_PEAK_TFLOPS = 78.6         # f64 vector (the matrix rate is the same)
+
+
+def gptq_leg(torch, qt, workloads, dev, legs):
+    # ------------------------------------- GPTQ at the search shape (bf16 X)
+    log("leg gptq: X[8192x17408] bf16, W[5120x17408]")
+    Xb = workloads.bf16_bits_rne(workloads.search_x())
+    Xd = torch.from_numpy(Xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    del Xb
+    T, I = Xd.shape
+    H = torch.empty((I, I), dtype=torch.float32, device=dev)
+    ws = torch.empty(qt.qt_hessian_full_workspace_bytes(T, I, qt.QT_BF16), dtype=torch.uint8,
+                     device=dev)
+    qt.qt_hessian_full(Xd, H, workspace=ws)
+    ms_h = time_launches(lambda i: qt.qt_hessian_full(Xd, H, workspace=ws), 3, torch)
+    del ws, Xd
+    fl_h = T * I * (I + 1)  # the symmetric product: T I (I + 1) / 2 multiply-adds
+    U = torch.empty((I, I), dtype=torch.float32, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(qt.qt_gptq_factor_workspace_bytes(I), dtype=torch.uint8, device=dev)
+    qt.qt_gptq_factor(H, 0.01, U, info, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    qt.qt_gptq_factor(H, 0.01, U, info, workspace=ws)
+    torch.cuda.synchronize()
+    ms_f = (time.perf_counter() - t0) * 1e3
+    fl_f = 2 * I ** 3 / 3  # Cholesky n^3/3 + triangular inverse n^3/3
+    del ws
+    W = workloads.search_w()
+    O = W.shape[0]
+    Wd = torch.from_numpy(W).to(dev)
+    del W
+    G = qt.qt_groups(I)
+    s = torch.empty((O, G), dtype=torch.float32, device=dev)
+    c = torch.empty((O, I), dtype=torch.int8, device=dev)
+    ws = torch.empty(qt.qt_gptq_workspace_bytes(O, I), dtype=torch.uint8, device=dev)
+    qt.qt_gptq_i3(Wd, U, s, c, workspace=ws)
+    ms_s = time_launches(lambda i: qt.qt_gptq_i3(Wd, U, s, c, workspace=ws), 2, torch, warmup=0)
+    fl_s = O * I * I  # block propagation: sum over blocks of 2 O 128 (I - b1)
+    del ws
+    p = qt.qt_pack_i3(c)
+    ws = torch.empty(qt.qt_gptq_proxy_workspace_bytes(O, I), dtype=torch.uint8, device=dev)
+    terms = qt.qt_gptq_proxy(Wd, p, s, H, workspace=ws)
+    ms_p = time_launches(lambda i: qt.qt_gptq_proxy(Wd, p, s, H, terms, workspace=ws), 2, torch,
+                         warmup=0)
+    fl_p = 2 * 2 * O * I * I
+    s0, c0, _ = qt.qt_quantize_g64(Wd, want_grid_idx=False)
+    t_rtn = qt.qt_gptq_proxy(Wd, qt.qt_pack_i3(c0), s0, H, workspace=ws).cpu().numpy()
+    t_g = terms.cpu().numpy()
+    legs["gptq"] = {
+        "hessian_full": {"ms": round(ms_h, 3), "TFLOP_s": round(fl_h / ms_h / 1e9, 1),
+                         "bound": "mfma", "peak": 2500.0,
+                         "frac": round(fl_h / ms_h / 1e9 / 2500.0, 4)},
+        "factor": {"ms": round(ms_f, 2), "TFLOP_s": round(fl_f / ms_f / 1e9, 2), "bound": "f64",
+                   "peak": F64_PEAK_TFLOPS, "frac": round(fl_f / ms_f / 1e9 / F64_PEAK_TFLOPS, 4),
+                   "info": int(info.item())},
+        "sweep": {"ms": round(ms_s, 3), "TFLOP_s": round(fl_s / ms_s / 1e9, 1), "bound": "mfma",
+                  "peak": F32_MFMA_PEAK_TFLOPS,
+                  "frac": round(fl_s / ms_s / 1e9 / F32_MFMA_PEAK_TFLOPS, 4)},
+        "proxy": {"ms": round(ms_p, 3), "TFLOP_s": round(fl_p / ms_p / 1e9, 1), "bound": "mfma",
+                  "peak": F32_MFMA_PEAK_TFLOPS,
+                  "frac": round(fl_p / ms_p / 1e9 / F32_MFMA_PEAK_TFLOPS, 4)},
+        "proxy_error": round(float(t_g[0] / t_g[1]), 6),
+        "proxy_error_rtn": round(float(t_rtn[0] / t_rtn[1]), 6),
+        "shape": {"T": T, "O": O, "I": I}}
+    log(f"leg gptq: {legs['gptq']}")
+    del H, U, Wd, s, c, p, ws, terms, s0, c0
 
 
 def int4_leg(torch, qt, workloads, dev, legs, args):

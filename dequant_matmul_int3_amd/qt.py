@@ -290,6 +290,22 @@ def qt_matvec_i4_grouped(packed, scales, E: int, O: int, I: int, X, expert_offse
 
 
 # ---------------------------------------------------------------- GPTQ
+def qt_hessian_full_workspace_bytes(T: int, I: int, xt: int) -> int:
+    return int(lib().qt_hessian_full_workspace_bytes(T, I, xt))
+
+
+def qt_gptq_factor_workspace_bytes(I: int) -> int:
+    return int(lib().qt_gptq_factor_workspace_bytes(I))
+
+
+def qt_gptq_workspace_bytes(O: int, I: int) -> int:
+    return int(lib().qt_gptq_workspace_bytes(O, I))
+
+
+def qt_gptq_proxy_workspace_bytes(O: int, I: int) -> int:
+    return int(lib().qt_gptq_proxy_workspace_bytes(O, I))
+
+
 def _ws(nbytes, device, workspace):
     if workspace is None:
         workspace = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
