@@ -8,11 +8,11 @@
 // f64 vector and matrix rates are the same), in 64-wide panels:
 //   Cholesky, right-looking: factor the diagonal block in LDS, solve the
 //   panel below it row by row, subtract the panel's outer product from the
-//   trailing lower triangle;
-//   inverse, from the last panel back: invert the diagonal block, then the
-//   panel below it becomes -C^-1[rest, rest] C[rest, panel] Cinv[panel, panel]
-//   (the trailing inverse is already in place; the product goes through a
-//   scratch panel because it overwrites its own input).
+//   trailing lower triangle (128 x 128 tiles);
+//   inverse, recursively: every 64 x 64 diagonal block at once, then level
+//   by level [[A, 0], [B, D]]^-1 = [[A^-1, 0], [-D^-1 B A^-1, D^-1]] for all
+//   pairs of a level at once (two batched tile products through a scratch
+//   buffer; the triangular factors' zero halves are skipped).
 // A non-positive pivot sets *info to its 1-based column (of the reversed
 // matrix) and is replaced by 1 so that every later step stays finite.
 #include <algorithm>
@@ -120,62 +120,91 @@ __global__ __launch_bounds__(64) void trsm_panel_kernel(double* __restrict__ B, 
     for (int c = 0; c < kNB; ++c) row[c] = x[c];
 }
 
-// 64 x 64 tile product helper: acc[a][b] += sum_c P[c][4ty+a] * Q[c][4tx+b]
-// with P, Q in LDS as [c][row].
-__device__ __forceinline__ void tile_fma(const double (*P)[kNB + 2], const double (*Q)[kNB + 2],
-                                         int ty, int tx, double (&acc)[4][4]) {
-#pragma unroll 4
-    for (int c = 0; c < kNB; ++c) {
-        double a[4], b[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = P[c][4 * ty + u];
-            b[u] = Q[c][4 * tx + u];
+// ---------------------------------------------------------------- f64 tiles
+// A TILE x TILE output tile of 256 threads (16 x 16, R x R values each),
+// K staged through LDS 16 at a time: acc[u][v] += sum_k P(R ty + u, k) Q(k,
+// R tx + v) for k in [kbeg, kend), P and Q given by loaders that return 0
+// outside their operand.  QT: Q's memory is [c][k] (k contiguous), so its
+// loads walk k like P's.
+constexpr int kKC = 16;
+
+template <int TILE, bool QT = false, typename LP, typename LQ>
+__device__ __forceinline__ void tile_product(int64_t kbeg, int64_t kend, LP ldp, LQ ldq,
+                                             double (&acc)[TILE / 16][TILE / 16],
+                                             double (*Ps)[TILE + 2], double (*Qs)[TILE + 2]) {
+    constexpr int R = TILE / 16;
+    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    for (int64_t k0 = kbeg; k0 < kend; k0 += kKC) {
+        __syncthreads();  // the previous stage is consumed
+        for (int p = tid; p < kKC * TILE; p += 256) {
+            {   // P(r, k): consecutive threads walk k (row-major operands)
+                const int kk = p % kKC, r = p / kKC;
+                const int64_t k = k0 + kk;
+                Ps[kk][r] = k < kend ? ldp(r, k) : 0.0;
+            }
+            {   // Q(k, c): consecutive threads walk c (or k when QT)
+                const int c = QT ? p / kKC : p % TILE, kk = QT ? p % kKC : p / TILE;
+                const int64_t k = k0 + kk;
+                Qs[kk][c] = k < kend ? ldq(k, c) : 0.0;
+            }
         }
+        __syncthreads();
+#pragma unroll 2
+        for (int kk = 0; kk < kKC; ++kk) {
+            double a[R], b[R];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < R; ++u) {
+                a[u] = Ps[kk][R * ty + u];
+                b[u] = Qs[kk][R * tx + u];
+            }
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
+            for (int u = 0; u < R; ++u)
+#pragma unroll
+                for (int v = 0; v < R; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
+        }
     }
 }
 
-// Trailing update B[i][j] -= sum_c B[i][k0+c] B[j][k0+c] for k0+64 <= j <= i.
+// Trailing update B[i][j] -= sum_c B[i][k0+c] B[j][k0+c] for k0+64 <= j <= i,
+// on 128 x 128 tiles of the lower triangle.
 __global__ __launch_bounds__(256) void syrk_update_kernel(double* __restrict__ B, int64_t n,
                                                           int64_t k0) {
+    constexpr int TILE = 128, R = TILE / 16;
     const int ti = blockIdx.y, tj = blockIdx.x;
     if (tj > ti) return;  // lower tiles only; uniform over the block
-    __shared__ double P[kNB][kNB + 2];
-    __shared__ double Q[kNB][kNB + 2];
+    __shared__ __attribute__((aligned(16))) double Ps[kKC][TILE + 2];
+    __shared__ __attribute__((aligned(16))) double Qs[kKC][TILE + 2];
     const int64_t k1 = k0 + kNB;
-    const int64_t ri0 = k1 + (int64_t)ti * kNB, rj0 = k1 + (int64_t)tj * kNB;
-    const int tid = threadIdx.x;
-    for (int p = tid; p < kNB * kNB; p += 256) {
-        const int r = p / kNB, c = p % kNB;
-        P[c][r] = ri0 + r < n ? B[(ri0 + r) * n + k0 + c] : 0.0;
-        Q[c][r] = rj0 + r < n ? B[(rj0 + r) * n + k0 + c] : 0.0;
-    }
-    __syncthreads();
-    const int ty = tid >> 4, tx = tid & 15;
-    double acc[4][4] = {};
-    tile_fma(P, Q, ty, tx, acc);
+    const int64_t ri0 = k1 + (int64_t)ti * TILE, rj0 = k1 + (int64_t)tj * TILE;
+    auto ldp = [&](int r, int64_t k) -> double {
+        return ri0 + r < n ? B[(ri0 + r) * n + k] : 0.0;
+    };
+    auto ldq = [&](int64_t k, int c) -> double {  // Q(k, c) = L[rj0 + c][k]
+        return rj0 + c < n ? B[(rj0 + c) * n + k] : 0.0;
+    };
+    double acc[R][R] = {};
+    tile_product<TILE, true>(k0, k0 + kNB, ldp, ldq, acc, Ps, Qs);
+    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t i = ri0 + 4 * ty + u;
+    for (int u = 0; u < R; ++u) {
+        const int64_t i = ri0 + R * ty + u;
         if (i >= n) continue;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t j = rj0 + 4 * tx + v;
+        for (int v = 0; v < R; ++v) {
+            const int64_t j = rj0 + R * tx + v;
             if (j <= i) B[i * n + j] -= acc[u][v];
         }
     }
 }
 
-// Inverse of the lower-triangular diagonal block at (k0, k0), in place:
-// thread c forms column c by forward substitution.
-__global__ __launch_bounds__(64) void trtri_diag_kernel(double* __restrict__ B, int64_t n,
-                                                        int64_t k0, int kb) {
+// Inverse of every lower-triangular 64 x 64 diagonal block, in place
+// (block x of the grid takes the block at 64 x): thread c forms column c by
+// forward substitution.
+__global__ __launch_bounds__(64) void trtri_diag_kernel(double* __restrict__ B, int64_t n) {
     __shared__ double L[kNB][kNB + 1];
     __shared__ double X[kNB][kNB + 1];
+    const int64_t k0 = (int64_t)blockIdx.x * kNB;
+    const int kb = (int)std::min<int64_t>(kNB, n - k0);
     const int c = threadIdx.x;
     for (int p = c; p < kb * kb; p += 64) {
         const int i = p / kb, j = p % kb;
@@ -197,62 +226,57 @@ __global__ __launch_bounds__(64) void trtri_diag_kernel(double* __restrict__ B, 
     }
 }
 
-// Panel below the diagonal block in the inverse: for the 64-row tile at r0,
-// T = sum over 64-column tiles m0 in [k1, r0] of Cinv[r0.., m0..] C[m0.., k0..]
-// (Cinv of the trailing part is final; its diagonal tile is lower triangular),
-// then tmp[r0 - k1 ..] = -T Cinv[k0.., k0..].
-__global__ __launch_bounds__(256) void trmm_panel_kernel(const double* __restrict__ B, int64_t n,
-                                                         int64_t k0,
-                                                         double* __restrict__ tmp) {
-    __shared__ double P[kNB][kNB + 2];
-    __shared__ double Q[kNB][kNB + 2];
-    const int64_t k1 = k0 + kNB;
-    const int64_t r0 = k1 + (int64_t)blockIdx.x * kNB;
+// One level of the recursive inverse, block size bs: pair z has
+// A = [a0, a0 + bs), D = [a0 + bs, min(a0 + 2 bs, n)), a0 = 2 bs z; A^-1
+// and D^-1 are already in place and B = C[D][A] is still the factor.
+//   STEP 1: Tz[r][c] = sum_{k <= r} Dinv[r][k] B[k][c]  (T in scratch, pitch bs)
+//   STEP 2: C[D][A][r][c] = -sum_{k >= c} Tz[r][k] Ainv[k][c]
+template <int TILE, int STEP>
+__global__ __launch_bounds__(256) void inv_level_kernel(double* __restrict__ B, int64_t n,
+                                                        int64_t bs,
+                                                        double* __restrict__ tmp) {
+    constexpr int R = TILE / 16;
+    __shared__ __attribute__((aligned(16))) double Ps[kKC][TILE + 2];
+    __shared__ __attribute__((aligned(16))) double Qs[kKC][TILE + 2];
+    const int64_t a0 = 2 * bs * (int64_t)blockIdx.z, d0 = a0 + bs;
+    const int64_t dD = std::min<int64_t>(bs, n - d0);  // > 0: the host launches only such pairs
+    const int64_t r0 = (int64_t)blockIdx.y * TILE, c0 = (int64_t)blockIdx.x * TILE;
+    if (r0 >= dD) return;  // uniform
+    double* T = tmp + (int64_t)blockIdx.z * bs * bs;
+    double acc[R][R] = {};
+    if (STEP == 1) {
+        auto ldp = [&](int r, int64_t k) -> double {  // Dinv[r0 + r][k], k <= r
+            const int64_t rr = r0 + r;
+            return (rr < dD && k <= rr) ? B[(d0 + rr) * n + d0 + k] : 0.0;
+        };
+        auto ldq = [&](int64_t k, int c) -> double {  // B[d0 + k][a0 + c0 + c]
+            return B[(d0 + k) * n + a0 + c0 + c];      // k < dD, c0 + c < bs
+        };
+        tile_product<TILE>(0, std::min<int64_t>(r0 + TILE, dD), ldp, ldq, acc, Ps, Qs);
+    } else {
+        auto ldp = [&](int r, int64_t k) -> double {  // T[r0 + r][k]
+            const int64_t rr = r0 + r;
+            return rr < dD ? T[rr * bs + k] : 0.0;
+        };
+        auto ldq = [&](int64_t k, int c) -> double {  // Ainv[k][c0 + c], k >= c0 + c
+            return k >= c0 + c ? B[(a0 + k) * n + a0 + c0 + c] : 0.0;
+        };
+        tile_product<TILE>(c0, bs, ldp, ldq, acc, Ps, Qs);
+    }
     const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    double acc[4][4] = {};
-    for (int64_t m0 = k1; m0 <= r0; m0 += kNB) {
-        __syncthreads();
-        for (int p = tid; p < kNB * kNB; p += 256) {
-            const int a = p / kNB, b = p % kNB;
-            // P[c][r] = Cinv[r0 + r][m0 + c] (zero above the diagonal and past n)
-            const int64_t r = r0 + a, m = m0 + b;
-            P[b][a] = (r < n && m < n && m <= r) ? B[r * n + m] : 0.0;
-            // Q[c][j] = C[m0 + c][k0 + j]
-            Q[a][b] = (m0 + a < n) ? B[(m0 + a) * n + k0 + b] : 0.0;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int64_t rr = r0 + R * ty + u;
+        if (rr >= dD) continue;
+#pragma unroll
+        for (int v = 0; v < R; ++v) {
+            const int64_t cc = c0 + R * tx + v;
+            if (STEP == 1)
+                T[rr * bs + cc] = acc[u][v];
+            else
+                B[(d0 + rr) * n + a0 + cc] = -acc[u][v];
         }
-        __syncthreads();
-        tile_fma(P, Q, ty, tx, acc);
     }
-    // tmp tile = -T Cinv_kk: T to LDS as [row][c], then P[c][r] = T[r][c]
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) P[4 * tx + v][4 * ty + u] = acc[u][v];
-    for (int p = tid; p < kNB * kNB; p += 256) {
-        const int a = p / kNB, b = p % kNB;  // Q[c][j] = Cinv_kk[c][j]
-        Q[a][b] = b <= a ? B[(k0 + a) * n + k0 + b] : 0.0;
-    }
-    __syncthreads();
-    double out[4][4] = {};
-    tile_fma(P, Q, ty, tx, out);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t r = r0 + 4 * ty + u;
-        if (r >= n) continue;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) tmp[(r - k1) * kNB + 4 * tx + v] = -out[u][v];
-    }
-}
-
-__global__ __launch_bounds__(256) void copy_panel_kernel(double* __restrict__ B, int64_t n,
-                                                         int64_t k0,
-                                                         const double* __restrict__ tmp) {
-    const int64_t k1 = k0 + kNB;
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t r = k1 + p / kNB;
-    if (r >= n) return;
-    B[r * n + k0 + p % kNB] = tmp[p];
 }
 
 // U[i][j] = Cinv[n-1-i][n-1-j] for j >= i, 0 below the diagonal.
@@ -266,16 +290,27 @@ __global__ __launch_bounds__(256) void write_u_kernel(const double* __restrict__
 
 }  // namespace
 
+// Scratch of the recursive inverse: per level, pairs x bs x bs doubles,
+// at most about n^2 / 2.
+static int64_t inv_scratch(int64_t n) {
+    int64_t most = 0;
+    for (int64_t bs = kNB; bs < n; bs *= 2) {
+        const int64_t pairs = (n + 2 * bs - 1) / (2 * bs);
+        most = std::max(most, pairs * bs * bs);
+    }
+    return most;
+}
+
 size_t gptq_factor_workspace(int64_t n) {
-    // B (n x n f64) + scratch panel (n x 64 f64) + one f64 slot
-    return (size_t)(n * n + n * kNB + 2) * sizeof(double);
+    // B (n x n f64) + the inverse's scratch + one f64 slot
+    return (size_t)(n * n + inv_scratch(n) + 2) * sizeof(double);
 }
 
 hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, int32_t* info,
                               void* workspace, hipStream_t s) {
     double* B = static_cast<double*>(workspace);
     double* tmp = B + n * n;
-    double* add = tmp + n * kNB;
+    double* add = tmp + inv_scratch(n);
     const unsigned rows = (unsigned)n;  // one grid row per matrix row
     const unsigned cols = (unsigned)std::min<int64_t>((n + 255) / 256, 1024);
     hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, s, H, n, damp, add, info);
@@ -289,22 +324,27 @@ hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, 
         if (rest > 0) {  // kb == 64 here: only the last panel can be narrower
             hipLaunchKernelGGL(trsm_panel_kernel, dim3((unsigned)((rest + 63) / 64)), dim3(64), 0,
                                s, B, n, k0);
-            const unsigned mt = (unsigned)((rest + kNB - 1) / kNB);
+            const unsigned mt = (unsigned)((rest + 127) / 128);
             hipLaunchKernelGGL(syrk_update_kernel, dim3(mt, mt), dim3(256), 0, s, B, n, k0);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t last = (n - 1) / kNB * kNB;
-    for (int64_t k0 = last; k0 >= 0; k0 -= kNB) {
-        const int kb = (int)std::min<int64_t>(kNB, n - k0);
-        hipLaunchKernelGGL(trtri_diag_kernel, dim3(1), dim3(64), 0, s, B, n, k0, kb);
-        const int64_t rest = n - k0 - kb;
-        if (rest > 0) {
-            const unsigned mt = (unsigned)((rest + kNB - 1) / kNB);
-            hipLaunchKernelGGL(trmm_panel_kernel, dim3(mt), dim3(256), 0, s, B, n, k0, tmp);
-            hipLaunchKernelGGL(copy_panel_kernel, dim3((unsigned)((rest * kNB + 255) / 256)),
-                               dim3(256), 0, s, B, n, k0, tmp);
+    hipLaunchKernelGGL(trtri_diag_kernel, dim3((unsigned)((n + kNB - 1) / kNB)), dim3(64), 0, s,
+                       B, n);
+    for (int64_t bs = kNB; bs < n; bs *= 2) {
+        // pairs whose D half is not empty
+        const int64_t pairs = (n - bs + 2 * bs - 1) / (2 * bs);
+        if (pairs > 65535) return hipErrorInvalidConfiguration;
+        const int tile = bs >= 128 ? 128 : 64;
+        const unsigned tiles = (unsigned)((bs + tile - 1) / tile);
+        const dim3 grid(tiles, tiles, (unsigned)pairs);
+        if (tile == 128) {
+            hipLaunchKernelGGL((inv_level_kernel<128, 1>), grid, dim3(256), 0, s, B, n, bs, tmp);
+            hipLaunchKernelGGL((inv_level_kernel<128, 2>), grid, dim3(256), 0, s, B, n, bs, tmp);
+        } else {
+            hipLaunchKernelGGL((inv_level_kernel<64, 1>), grid, dim3(256), 0, s, B, n, bs, tmp);
+            hipLaunchKernelGGL((inv_level_kernel<64, 2>), grid, dim3(256), 0, s, B, n, bs, tmp);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
