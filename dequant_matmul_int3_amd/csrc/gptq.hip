@@ -70,26 +70,35 @@ __device__ __forceinline__ float group_pass(float (&w)[kGroup], const float* ubl
     return s;
 }
 
-// One wave (64 rows) per block, the block of columns [b0, min(b0+128, I)).
+// Four waves (256 rows) per block, the block of columns [b0, min(b0+128, I)).
 // U's 128 x 128 block sits in LDS, padded past I with 0 off the diagonal and
 // 1 on it; padded columns hold w = 0, so their codes and errors are 0 and
 // they change nothing (and are not stored).  Every row then runs one
 // branch-free path.  vec: codes rows allow 16-byte stores (I % 16 == 0).
-__global__ __launch_bounds__(64) void gptq_block_kernel(float* __restrict__ Wc, int64_t O,
-                                                        int64_t I, const float* __restrict__ U,
-                                                        int64_t b0, float* __restrict__ scales,
-                                                        int8_t* __restrict__ codes,
-                                                        float* __restrict__ Err, int vec) {
+constexpr int kSweepRows = 256;
+
+__global__ __launch_bounds__(kSweepRows) void gptq_block_kernel(
+    float* __restrict__ Wc, int64_t O, int64_t I, const float* __restrict__ U, int64_t b0,
+    float* __restrict__ scales, int8_t* __restrict__ codes, float* __restrict__ Err, int vec) {
     __shared__ __attribute__((aligned(16))) float Ub[kBlock * kUpitch];
-    __shared__ __attribute__((aligned(16))) float errs[64 * kErrPitch];
+    __shared__ __attribute__((aligned(16))) float errs[kSweepRows * kErrPitch];
     const int lane = threadIdx.x;
-    for (int p = lane; p < kBlock * kBlock; p += 64) {
-        const int i = p / kBlock, j = p % kBlock;
-        const int64_t gi = b0 + i, gj = b0 + j;
-        Ub[i * kUpitch + j] = (gi < I && gj < I) ? U[gi * I + gj] : (i == j ? 1.0f : 0.0f);
+    if (vec && b0 + kBlock <= I) {
+        // whole block inside U: 16-byte loads (I % 4 == 0 and b0 % 128 == 0)
+        for (int p = lane; p < kBlock * kBlock / 4; p += kSweepRows) {
+            const int i = p / (kBlock / 4), j4 = (p % (kBlock / 4)) * 4;
+            *reinterpret_cast<float4*>(Ub + i * kUpitch + j4) =
+                *reinterpret_cast<const float4*>(U + (b0 + i) * I + b0 + j4);
+        }
+    } else {
+        for (int p = lane; p < kBlock * kBlock; p += kSweepRows) {
+            const int i = p / kBlock, j = p % kBlock;
+            const int64_t gi = b0 + i, gj = b0 + j;
+            Ub[i * kUpitch + j] = (gi < I && gj < I) ? U[gi * I + gj] : (i == j ? 1.0f : 0.0f);
+        }
     }
     __syncthreads();
-    const int64_t o = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t o = (int64_t)blockIdx.x * kSweepRows + lane;
     if (o >= O) return;  // no cross-lane operations or barriers below
     const int64_t G = (I + kGroup - 1) / kGroup;
     const int64_t b1 = min(b0 + kBlock, I);
@@ -153,7 +162,7 @@ constexpr int kBpitch = kPT + 4;        // floats per B row in LDS ([k][n])
 __global__ __launch_bounds__(256) void gptq_prop_kernel(float* __restrict__ Wc, int64_t O,
                                                         int64_t I, const float* __restrict__ U,
                                                         int64_t b0,
-                                                        const float* __restrict__ Err) {
+                                                        const float* __restrict__ Err, int uvec) {
     __shared__ __attribute__((aligned(16))) float As[kPT * kApitch];
     __shared__ __attribute__((aligned(16))) float Bs[kPK * kBpitch];
     const int64_t b1 = b0 + kBlock;
@@ -176,10 +185,18 @@ __global__ __launch_bounds__(256) void gptq_prop_kernel(float* __restrict__ Wc, 
             if (m < O) v = *reinterpret_cast<const f32x4_t*>(Err + m * kBlock + kh + c4);
             *reinterpret_cast<f32x4_t*>(As + r * kApitch + c4) = v;
         }
-        for (int p = tid; p < kPK * kPT; p += 256) {
-            const int k = p / kPT, c = p % kPT;
-            const int64_t nn = n0 + c;
-            Bs[k * kBpitch + c] = nn < N ? U[(b0 + kh + k) * I + b1 + nn] : 0.0f;
+        if (uvec && n0 + kPT <= N) {  // 16-byte loads: I % 4 == 0, whole tile inside
+            for (int p = tid; p < kPK * kPT / 4; p += 256) {
+                const int k = p / (kPT / 4), c4 = (p % (kPT / 4)) * 4;
+                *reinterpret_cast<f32x4_t*>(Bs + k * kBpitch + c4) =
+                    *reinterpret_cast<const f32x4_t*>(U + (b0 + kh + k) * I + b1 + n0 + c4);
+            }
+        } else {
+            for (int p = tid; p < kPK * kPT; p += 256) {
+                const int k = p / kPT, c = p % kPT;
+                const int64_t nn = n0 + c;
+                Bs[k * kBpitch + c] = nn < N ? U[(b0 + kh + k) * I + b1 + nn] : 0.0f;
+            }
         }
         __syncthreads();
 #pragma unroll 4
@@ -307,15 +324,19 @@ hipError_t launch_gptq_i3(const float* W, int64_t O, int64_t I, const float* U, 
                        dim3(256), 0, s, W, nel, Wc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned rb = (unsigned)((O + 63) / 64);
-    const int vec = (I % 16 == 0) && ((reinterpret_cast<uintptr_t>(codes) & 15) == 0);
+    const unsigned rb = (unsigned)((O + kSweepRows - 1) / kSweepRows);
+    // 16-byte code stores need I % 16 == 0; 16-byte U loads need I % 4 == 0
+    const int vec = (I % 16 == 0) && ((reinterpret_cast<uintptr_t>(codes) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
+    const int uvec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
     for (int64_t b0 = 0; b0 < I; b0 += kBlock) {
-        hipLaunchKernelGGL(gptq_block_kernel, dim3(rb), dim3(64), 0, s, Wc, O, I, U, b0, scales,
-                           codes, Err, vec);
+        hipLaunchKernelGGL(gptq_block_kernel, dim3(rb), dim3(kSweepRows), 0, s, Wc, O, I, U, b0,
+                           scales, codes, Err, vec);
         const int64_t rest = I - (b0 + kBlock);
         if (rest > 0) {
             const dim3 grid((unsigned)((rest + kPT - 1) / kPT), (unsigned)((O + kPT - 1) / kPT));
-            hipLaunchKernelGGL(gptq_prop_kernel, grid, dim3(256), 0, s, Wc, O, I, U, b0, Err);
+            hipLaunchKernelGGL(gptq_prop_kernel, grid, dim3(256), 0, s, Wc, O, I, U, b0, Err,
+                               uvec);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
