@@ -285,3 +285,69 @@ def proxy_terms(W, codes, scales, H):
     den = C.c_double()
     lib().qto_proxy_terms(_p(W), O, I, _p(codes), _p(scales), _p(H), C.byref(num), C.byref(den))
     return num.value, den.value
+
+
+# ---------------------------------------------------------------- MoE expert layer
+# The pull request page's MoE setting (every routed expert's weights read once
+# per decode step; the per-projection ablation names gate_proj, up_proj and
+# down_proj of each expert) with the MoE decode configuration's top-8 routing.
+# The pages give no expert formula and no combine rule.  Readings:
+#   - expert e: y = W_down,e (silu(W_gate,e x) * (W_up,e x)), silu(z) = z / (1 + exp(-z));
+#   - routing: the k largest logits of the token (equal logits: the lower
+#     expert index first), combine weights a softmax over those k logits;
+#   - out_t = sum_j w_tj y_{e_tj}(x_t).
+def dequant_f64(packed, scales, O: int, I: int, bits: int = 3):
+    """The weights a packed matrix denotes, s * v, in f64 [O, I]."""
+    codes = unpack_i3(packed, O, I) if bits == 3 else unpack_i4(packed, O, I)
+    s = np.repeat(np.asarray(scales, np.float64).reshape(O, -1), 64, axis=1)[:, :I]
+    return s * codes.astype(np.float64)
+
+
+def moe_route(logits, k: int):
+    """-> (experts [T, k] int32 in descending logit order, weights [T, k] f64)."""
+    L = np.asarray(logits, np.float32)
+    idx = np.argsort(-L, axis=1, kind="stable")[:, :k]
+    sel = np.take_along_axis(L, idx, axis=1).astype(np.float64)
+    z = np.exp(sel - sel[:, :1])  # the first is the largest
+    return idx.astype(np.int32), z / z.sum(axis=1, keepdims=True)
+
+
+def silu_f64(z):
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore"):  # exp(-z) = inf for very negative z gives -0
+        return z / (1.0 + np.exp(-z))
+
+
+def moe_layer_f64(X, logits, k: int, gate, up, down):
+    """gate / up / down: (packed [E, bytes], scales [E, O, G], bits) with gate
+    and up [F x D] per expert and down [D x F].  -> (out [T, D] f64, bound
+    [T, D]): bound is the error budget of an implementation whose gate/up/
+    down products each meet 1e-5 of their absolute sums (the grouped
+    multiply's tolerance), scaled so that |out - ref| <= 1e-5 * bound."""
+    X = np.asarray(X, np.float32)
+    T, D = X.shape
+    F = gate[1].shape[1]
+    experts, w = moe_route(logits, k)
+    out = np.zeros((T, D))
+    bound = np.zeros((T, D))
+    cache = {}
+
+    def mats(e):
+        if e not in cache:
+            cache[e] = (dequant_f64(gate[0][e], gate[1][e], F, D, gate[2]),
+                        dequant_f64(up[0][e], up[1][e], F, D, up[2]),
+                        dequant_f64(down[0][e], down[1][e], D, F, down[2]))
+        return cache[e]
+
+    for t in range(T):
+        x = X[t].astype(np.float64)
+        for j in range(k):
+            Wg, Wu, Wd = mats(int(experts[t, j]))
+            g, u = Wg @ x, Wu @ x
+            ag, au = np.abs(Wg) @ np.abs(x), np.abs(Wu) @ np.abs(x)
+            h = silu_f64(g) * u
+            y = Wd @ h
+            dh = 1.1 * ag * np.abs(u) + np.abs(silu_f64(g)) * au  # |silu'| <= 1.1
+            out[t] += w[t, j] * y
+            bound[t] += w[t, j] * (np.abs(Wd) @ dh + np.abs(Wd) @ np.abs(h) + np.abs(y))
+    return out, bound

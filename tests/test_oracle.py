@@ -721,3 +721,94 @@ def test_proxy_terms_against_numpy_and_the_weighted_objective():
     d = np.exp(rng.standard_normal(130)).astype(np.float32)
     num_d, _ = oracle.proxy_terms(W, c, s, np.diag(d))
     assert np.isclose(num_d, np.sum(E ** 2 * d[None, :]), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- MoE expert layer
+def test_moe_route_worked_example():
+    # logits [0.1, 0.5, 0.5, 0.2]: the two 0.5 tie (lower index first)
+    e, w = oracle.moe_route(np.array([[0.1, 0.5, 0.5, 0.2]], np.float32), 2)
+    assert e.tolist() == [[1, 2]] and np.allclose(w, [[0.5, 0.5]], rtol=0, atol=1e-15)
+    e, w = oracle.moe_route(np.array([[0.1, 0.5, 0.5, 0.2]], np.float32), 3)
+    assert e.tolist() == [[1, 2, 3]]
+    # softmax of (0.5, 0.5, 0.2) in f64 of the f32 logits
+    z = np.exp(np.float64(np.float32(0.2)) - np.float64(np.float32(0.5)))
+    assert np.allclose(w, [[1 / (2 + z), 1 / (2 + z), z / (2 + z)]], rtol=1e-15)
+    # equal logits, k = E: uniform weights, experts in index order
+    e, w = oracle.moe_route(np.zeros((1, 5), np.float32), 5)
+    assert e.tolist() == [[0, 1, 2, 3, 4]] and np.allclose(w, 0.2, rtol=1e-15)
+
+
+def test_silu_closed_forms():
+    assert oracle.silu_f64(0.0) == 0.0
+    assert np.isclose(oracle.silu_f64(1.0), 1.0 / (1.0 + np.exp(-1.0)), rtol=1e-15)
+    assert oracle.silu_f64(-800.0) == -0.0 and oracle.silu_f64(800.0) == 800.0
+
+
+def _moe_experts(E, F, D, seed, bits=(3, 3, 3)):
+    out = []
+    for which, (O, I), b in (("gate", (F, D), bits[0]), ("up", (F, D), bits[1]),
+                             ("down", (D, F), bits[2])):
+        ps, ss = [], []
+        for e in range(E):
+            W = workloads.generic_weights(O, I, seed=seed * 100 + e + (7 if which == "up" else 0)
+                                          + (13 if which == "down" else 0))
+            if b == 3:
+                s, c, _ = oracle.quantize_g64(W)
+                p = oracle.pack_i3(c)
+            else:
+                s, c, _ = oracle.quantize_g64_i4(W)
+                p = oracle.pack_i4(c)
+            ps.append(p)
+            ss.append(s)
+        out.append((np.stack(ps), np.stack(ss), b))
+    return out
+
+
+def test_moe_layer_properties():
+    E, F, D, T, k = 6, 64, 128, 5, 2
+    gate, up, down = _moe_experts(E, F, D, 1)
+    X = workloads.generic_matrix(T, D, seed=2)
+    logits = np.random.default_rng(3).random((T, E)).astype(np.float32)
+    out, bound = oracle.moe_layer_f64(X, logits, k, gate, up, down)
+    assert np.all(bound > 0)
+    # zero gate weights: silu(0) = 0, so every output is exactly zero
+    zg = (gate[0], np.zeros_like(gate[1]), 3)
+    z, _ = oracle.moe_layer_f64(X, logits, k, zg, up, down)
+    assert not z.any()
+    # down scales doubled: the output doubles exactly
+    d2 = (down[0], down[1] * 2, 3)
+    o2, _ = oracle.moe_layer_f64(X, logits, k, gate, up, d2)
+    assert np.array_equal(o2, 2 * out)
+    # k = 1: the top expert alone, weight 1, against the dense formula
+    o1, _ = oracle.moe_layer_f64(X, logits, 1, gate, up, down)
+    e0 = np.argmax(logits, axis=1)
+    for t in range(T):
+        e = e0[t]
+        Wg = oracle.dequant_f64(gate[0][e], gate[1][e], F, D)
+        Wu = oracle.dequant_f64(up[0][e], up[1][e], F, D)
+        Wd = oracle.dequant_f64(down[0][e], down[1][e], D, F)
+        x = X[t].astype(np.float64)
+        g = Wg @ x
+        ref = Wd @ (g / (1 + np.exp(-g)) * (Wu @ x))
+        assert np.allclose(o1[t], ref, rtol=1e-12, atol=1e-15)
+    # relabelling the experts (and their logits) leaves the layer unchanged
+    perm = np.random.default_rng(4).permutation(E)
+    pg = (gate[0][perm], gate[1][perm], 3)
+    pu = (up[0][perm], up[1][perm], 3)
+    pd = (down[0][perm], down[1][perm], 3)
+    op, _ = oracle.moe_layer_f64(X, logits[:, perm], k, pg, pu, pd)
+    assert np.allclose(op, out, rtol=1e-12, atol=1e-15)
+
+
+def test_dequant_f64_matches_matvec():
+    W = workloads.generic_weights(9, 200, seed=5)
+    s, c, _ = oracle.quantize_g64(W)
+    p = oracle.pack_i3(c)
+    x = workloads.generic_vector(200, seed=6)
+    y, _ = oracle.matvec_f64(p, s, 9, 200, x)
+    assert np.allclose(oracle.dequant_f64(p, s, 9, 200) @ x.astype(np.float64), y, rtol=1e-12)
+    s4, c4, _ = oracle.quantize_g64_i4(W)
+    p4 = oracle.pack_i4(c4)
+    y4, _ = oracle.matvec_i4_f64(p4, s4, 9, 200, x)
+    assert np.allclose(oracle.dequant_f64(p4, s4, 9, 200, 4) @ x.astype(np.float64), y4,
+                       rtol=1e-12)
