@@ -10,7 +10,7 @@ from .qt import (QtError, QT_BF16, QT_F32, lib, qt_groups, qt_hessian_diag,
                  qt_quantize_g64_signed, qt_status_str, qt_hessian_full, qt_gptq_factor,
                  qt_gptq_i3, qt_gptq_proxy, qt_hessian_full_workspace_bytes,
                  qt_gptq_factor_workspace_bytes, qt_gptq_workspace_bytes,
-                 qt_gptq_proxy_workspace_bytes)
+                 qt_gptq_proxy_workspace_bytes, qt_moe_layer, qt_moe_layer_workspace_bytes)
 
 __all__ = ["QtError", "QT_BF16", "QT_F32", "lib", "qt_groups", "qt_hessian_diag",
            "qt_hessian_workspace_bytes", "qt_matmul_i3", "qt_matmul_i4", "qt_matvec_i3",
@@ -19,4 +19,4 @@ __all__ = ["QtError", "QT_BF16", "QT_F32", "lib", "qt_groups", "qt_hessian_diag"
            "qt_quantize_g64_signed", "qt_status_str", "qt_hessian_full", "qt_gptq_factor",
            "qt_gptq_i3", "qt_gptq_proxy", "qt_hessian_full_workspace_bytes",
            "qt_gptq_factor_workspace_bytes", "qt_gptq_workspace_bytes",
-           "qt_gptq_proxy_workspace_bytes"]
+           "qt_gptq_proxy_workspace_bytes", "qt_moe_layer", "qt_moe_layer_workspace_bytes"]

@@ -21,7 +21,7 @@ SO = os.path.join(PKG, "libqt.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "grouped.hip", "gemm.hip", "hessian.hip",
-           "syrk.hip", "factor.hip", "gptq.hip"]
+           "syrk.hip", "factor.hip", "gptq.hip", "moe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -32,7 +32,8 @@ FLAGS = [
 # The grouped matrix-core kernel scales every MFMA result on the vector ALUs:
 # ask the backend to keep MFMA results in VGPRs rather than AGPRs (saves one
 # copy per result).
-EXTRA = {"grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "moe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, verbose):

@@ -345,6 +345,58 @@ qt_status qt_matvec_i4_grouped(const uint8_t* packed, const float* scales, int32
                         stream, 4);
 }
 
+// ---------------------------------------------------------------- MoE layer
+size_t qt_moe_layer_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t D, int64_t F) {
+    if (T < 1 || k < 1 || E < 1 || D < 1 || F < 1) return 0;
+    if (mul3(T * k, D + 2 * F, 4) < 0) return 0;
+    return qt::moe_layer_workspace(T, k, E, D, F);
+}
+
+qt_status qt_moe_layer(const float* X, int64_t T, int64_t D, int64_t F, const float* logits,
+                       int32_t E, int32_t k, const uint8_t* gate_packed,
+                       const float* gate_scales, int32_t gate_bits, const uint8_t* up_packed,
+                       const float* up_scales, int32_t up_bits, const uint8_t* down_packed,
+                       const float* down_scales, int32_t down_bits, float* out,
+                       void* workspace, size_t ws_bytes, void* stream) {
+    if (!X || !logits || !gate_packed || !gate_scales || !up_packed || !up_scales ||
+        !down_packed || !down_scales || !out || !workspace)
+        return QT_ERR_NULL;
+    if (T < 1 || D < 128 || F < 128 || D % 128 || F % 128 || D > QT_MAX_I || F > QT_MAX_I)
+        return QT_ERR_SHAPE;
+    if (E < 1 || E > 65535 || k < 1 || k > 32 || k > E) return QT_ERR_SHAPE;
+    if (T * k > 0x7fffffffLL) return QT_ERR_SHAPE;
+    const int32_t bits[3] = {gate_bits, up_bits, down_bits};
+    for (int b : bits)
+        if (b != 3 && b != 4) return QT_ERR_ARG;
+    const int64_t gb = gate_bits == 3 ? kGroupBytes : kGroupBytesI4;
+    const int64_t ub = up_bits == 3 ? kGroupBytes : kGroupBytesI4;
+    const int64_t db = down_bits == 3 ? kGroupBytes : kGroupBytesI4;
+    const int64_t gpb = mul3(E, F * (D / 64), gb), upb = mul3(E, F * (D / 64), ub);
+    const int64_t dpb = mul3(E, D * (F / 64), db);
+    const int64_t gsb = mul3(E, F * (D / 64), 4), dsb = mul3(E, D * (F / 64), 4);
+    const int64_t xb = mul3(T, D, 4), lb = mul3(T, E, 4);
+    if (gpb < 0 || upb < 0 || dpb < 0 || gsb < 0 || dsb < 0 || xb < 0 || lb < 0)
+        return QT_ERR_SHAPE;
+    const size_t need = qt_moe_layer_workspace_bytes(T, k, E, D, F);
+    if (need == 0) return QT_ERR_SHAPE;
+    if (ws_bytes < need) return QT_ERR_WORKSPACE;
+    if (!aligned(X, 16) || !aligned(out, 16) || !aligned(logits, 4) || !aligned(gate_packed, 16) ||
+        !aligned(up_packed, 16) || !aligned(down_packed, 16) || !aligned(gate_scales, 4) ||
+        !aligned(up_scales, 4) || !aligned(down_scales, 4) || !aligned(workspace, 16))
+        return QT_ERR_ALIGN;
+    const void* ins[8] = {X, logits, gate_packed, gate_scales, up_packed, up_scales, down_packed,
+                          down_scales};
+    const int64_t inb[8] = {xb, lb, gpb, gsb, upb, gsb, dpb, dsb};
+    for (int q = 0; q < 8; ++q)
+        if (overlap(out, xb, ins[q], inb[q]) || overlap(workspace, (int64_t)need, ins[q], inb[q]))
+            return QT_ERR_ALIAS;
+    if (overlap(out, xb, workspace, (int64_t)need)) return QT_ERR_ALIAS;
+    return launched(qt::launch_moe_layer(X, T, D, F, logits, E, k, gate_packed, gate_scales,
+                                         gate_bits, up_packed, up_scales, up_bits, down_packed,
+                                         down_scales, down_bits, out, workspace,
+                                         as_stream(stream)));
+}
+
 // ---------------------------------------------------------------- GPTQ
 size_t qt_hessian_full_workspace_bytes(int64_t T, int64_t I, qt_dtype xt) {
     if (T < 1 || I < 1 || I > 65535 * 128LL || (xt != QT_F32 && xt != QT_BF16)) return 0;

@@ -1,0 +1,363 @@
+// The grouped (mixture-of-experts) matrix-core tile shared by the grouped
+// multiply and the MoE expert layer; see grouped.hip for the method.
+#pragma once
+#include "qt_internal.h"
+
+namespace qt {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kRows = 64;             // output rows per block
+constexpr int kThreads = 256;         // 4 waves
+constexpr int kCG = 16;               // groups per chunk
+constexpr int kTok = 5;               // tokens per pass (3 B columns each)
+constexpr int kPRow = kCG * kGroup * 2 + 16;   // LDS bytes per piece column
+
+// Weight staging geometry of a format: bytes per group, LDS bytes per weight
+// row (+16: conflict-free reads), 16-byte pieces per thread per chunk.
+template <int BITS>
+struct Geo {
+    static constexpr int kGB = BITS == 3 ? kGroupBytes : kGroupBytesI4;
+    static constexpr int kWRow = kCG * kGB + 16;
+    static constexpr int kWPieces = kRows * kCG * kGB / 16;  // 1536 or 2048
+    static constexpr int kWPer = kWPieces / kThreads;        // 6 or 8
+    static_assert(kWPieces % kThreads == 0, "weight chunk split");
+};
+
+// bf16 bit patterns of v = u - 4 for four codes u (one per byte), as the pairs
+// [c0 | c1 << 16] and [c2 | c3 << 16].  bf16(v) for v = -4..3 is c080 c040 c000
+// bf80 0000 3f80 4000 4040: one table gives the high bytes, one the low bytes.
+__device__ __forceinline__ void to_bf16_pairs(uint32_t W4, uint32_t& d0, uint32_t& d1) {
+    const uint32_t hi = __builtin_amdgcn_perm(0x40403F00u, 0xBFC0C0C0u, W4);
+    const uint32_t lo = __builtin_amdgcn_perm(0x40008000u, 0x80004080u, W4);
+    d0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    d1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+// One 16-code quarter: low-plane word L (code 4b+i at bits 8b+2i) and its 16
+// high bits h16 (code j at bit j) -> codes 0..7 and 8..15 as bf16x8 (natural
+// order).
+__device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t h16, u32x4_t& lo8,
+                                                u32x4_t& hi8) {
+    uint32_t sp = (h16 | (h16 << 8)) & 0x00FF00FFu;
+    sp = ((sp | (sp << 4)) & 0x0F0F0F0Fu) << 2;  // code 4b+i's high bit at bit 2+i of byte b
+    const uint32_t u0 = (L & 0x03030303u) | (sp & 0x04040404u);
+    const uint32_t u1 = ((L >> 2) & 0x03030303u) | ((sp >> 1) & 0x04040404u);
+    const uint32_t u2 = ((L >> 4) & 0x03030303u) | ((sp >> 2) & 0x04040404u);
+    const uint32_t u3 = ((L >> 6) & 0x03030303u) | ((sp >> 3) & 0x04040404u);
+    const uint32_t a0 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // codes 0 1 4 5
+    const uint32_t a1 = __builtin_amdgcn_perm(u1, u0, 0x07030602u);  // codes 8 9 12 13
+    const uint32_t b0 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);  // codes 2 3 6 7
+    const uint32_t b1 = __builtin_amdgcn_perm(u3, u2, 0x07030602u);  // codes 10 11 14 15
+    uint32_t p01, p45, p89, p1213, p23, p67, p1011, p1415;
+    to_bf16_pairs(a0, p01, p45);
+    to_bf16_pairs(a1, p89, p1213);
+    to_bf16_pairs(b0, p23, p67);
+    to_bf16_pairs(b1, p1011, p1415);
+    lo8 = u32x4_t{p01, p23, p45, p67};
+    hi8 = u32x4_t{p89, p1011, p1213, p1415};
+}
+
+// v/16 of the two's-complement nibble in the low four bits of byte B of t.
+template <int B>
+__device__ __forceinline__ float nib(uint32_t t) {
+    float r;
+    if constexpr (B == 0)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0"
+            : "=v"(r) : "v"(t));
+    else if constexpr (B == 1)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+            : "=v"(r) : "v"(t));
+    else if constexpr (B == 2)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+            : "=v"(r) : "v"(t));
+    else
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+            : "=v"(r) : "v"(t));
+    return r;
+}
+
+// bf16 pair [f(a) | f(b) << 16] of two f32 values with zero low halves.
+__device__ __forceinline__ uint32_t hi_pair(float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// One int4 word (code n of the word in nibble n, u = v + 8) -> its 8 codes
+// as v/16 in bf16, natural order.  u ^ 8 is the two's-complement nibble of v.
+__device__ __forceinline__ u32x4_t dequant_word_i4(uint32_t w) {
+    const uint32_t t = w ^ 0x88888888u;  // even codes: low nibble of each byte
+    const uint32_t h = t >> 4;           // odd codes: low nibble of each byte
+    return u32x4_t{hi_pair(nib<0>(t), nib<0>(h)), hi_pair(nib<1>(t), nib<1>(h)),
+                   hi_pair(nib<2>(t), nib<2>(h)), hi_pair(nib<3>(t), nib<3>(h))};
+}
+
+// The three bf16 pieces of four f32 inputs, as [piece][pair] words.
+__device__ __forceinline__ void split3(const float (&x)[4], uint32_t (&w)[3][2]) {
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float hf = __uint_as_float(__float_as_uint(x[e]) & 0xFFFF0000u);
+        const float r1 = x[e] - hf;
+        const float mf = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+        const float lf = r1 - mf;
+        h[e] = __float_as_uint(hf);
+        m[e] = __float_as_uint(mf);
+        l[e] = __float_as_uint(lf);
+    }
+    // high halves of two words -> one word (element 2k in the low half)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        w[0][k] = __builtin_amdgcn_perm(h[2 * k + 1], h[2 * k], 0x07060302u);
+        w[1][k] = __builtin_amdgcn_perm(m[2 * k + 1], m[2 * k], 0x07060302u);
+        w[2][k] = __builtin_amdgcn_perm(l[2 * k + 1], l[2 * k], 0x07060302u);
+    }
+}
+
+// lane l takes the value of lane l + M of its 16-lane row (0 past the row)
+template <int M>
+__device__ __forceinline__ float from_lane_plus(float a) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x100 + M, 0xF, 0xF, true));
+}
+
+// LDS of one tile; WROW: weight bytes per row (the larger format's for a
+// kernel that runs both).
+template <int WROW>
+struct TileLds {
+    __attribute__((aligned(16))) uint8_t wl[kRows * WROW];   // weight bytes
+    __attribute__((aligned(16))) float sl[kCG][kRows];       // scales [group][row]
+    __attribute__((aligned(16))) uint8_t pl[16 * kPRow];     // pieces [col][k]
+    int32_t trow[kTok];
+    int32_t tout[kTok];
+};
+
+enum XForm { kPlain = 0, kSwiGLU = 1 };
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// One item: the pairs of expert e against its rows [64 rb, 64 rb + 64).
+// W16: every row's chunk bytes start on a 16-byte boundary (int4, or int3
+// with G even); else 8-byte pieces.  XV: inputs allow 16-byte loads
+// (I % 4 == 0, X 16-byte aligned).  XF == kSwiGLU: input row r is
+// silu(X[r]) * X2[r] elementwise, formed as it is loaded.  Starts with a
+// barrier, so items can follow one another in a block.
+template <int BITS, bool W16, bool XV, int XF, int WROW>
+__device__ __forceinline__ void grouped_tile(
+    TileLds<WROW>& L, int e, int64_t rb, const uint8_t* __restrict__ packed,
+    const float* __restrict__ scales, int64_t O, int32_t I, int32_t G,
+    const float* __restrict__ X, const float* __restrict__ X2, int64_t n_x_rows,
+    const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t P,
+    float* __restrict__ Y) {
+    constexpr int kGB = Geo<BITS>::kGB;
+    constexpr int kWRow = Geo<BITS>::kWRow;
+    constexpr int kWPer = Geo<BITS>::kWPer;
+    static_assert(kWRow <= WROW, "tile LDS too small for the format");
+    uint8_t* wl = L.wl;
+    auto& sl = L.sl;
+    uint8_t* pl = L.pl;
+    int32_t* trow = L.trow;
+    int32_t* tout = L.tout;
+
+    const int32_t p0 = max(0, min(off[e], P));
+    const int32_t p1 = max(p0, min(off[e + 1], P));
+    if (p1 == p0) return;  // uniform over the block
+    __syncthreads();  // an earlier item of this block is done with the LDS
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l16 = lane & 15;
+    const int j4 = lane >> 4;  // quarter of the group (A), k slot (B)
+    const int64_t r0 = rb * kRows;
+    const uint8_t* pk = packed + (int64_t)e * O * G * kGB;
+    const float* sk = scales + (int64_t)e * O * G;
+
+    // column 15 of the pieces is never written by the staging: zero it once
+    for (int i = tid; i < kCG * kGroup / 2; i += kThreads)
+        reinterpret_cast<uint32_t*>(pl + 15 * kPRow)[i] = 0u;
+
+    // ---- per-thread staging assignments (rows past O read row O-1, unused)
+    // weights: piece i of this thread = 16-byte piece (tid + 256 i) of the
+    // chunk, row-major over [row][kCG * kGB bytes]
+    const uint8_t* wrow0[kWPer];  // the row's first byte (always a valid 16 bytes)
+    int wdst[kWPer];
+    int wpart[kWPer];
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+        const int id = tid + kThreads * i;
+        const int row = id / (kCG * kGB / 16), part = id % (kCG * kGB / 16);
+        const int64_t gr = min<int64_t>(r0 + row, O - 1);
+        wrow0[i] = pk + gr * G * kGB;
+        wdst[i] = row * kWRow + 16 * part;
+        wpart[i] = part;
+    }
+    // scales: 4 per thread, [row][16 groups] -> sl[group][row]
+    const int srow = tid >> 2, sg = (tid & 3) * 4;
+    const float* ssrc = sk + min<int64_t>(r0 + srow, O - 1) * G;
+
+    struct Chunk {
+        u32x4_t w[kWPer];
+        float s[4];
+        float x[kTok][4];
+    };
+    auto load_chunk = [&](int32_t c0, int nt, Chunk& c) {
+        const int gn = min(kCG, G - c0);
+        // pieces past the chunk's bytes re-read the row's first 16 bytes
+        // (unused); with G even every piece lies wholly inside or outside
+#pragma unroll
+        for (int i = 0; i < kWPer; ++i) {
+            const int b0 = wpart[i] * 16;
+            const uint8_t* rc = wrow0[i] + (int64_t)c0 * kGB;
+            if constexpr (W16) {
+                const uint8_t* src = b0 < gn * kGB ? rc + b0 : wrow0[i];
+                c.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+            } else {
+                static_assert(BITS == 3, "int4 groups are always 16-byte aligned");
+                const uint8_t* sa = b0 < gn * kGB ? rc + b0 : wrow0[i];
+                const uint8_t* sb = b0 + 8 < gn * kGB ? rc + b0 + 8 : wrow0[i];
+                const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sa));
+                const u32x2_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sb));
+                c.w[i] = u32x4_t{a.x, a.y, b.x, b.y};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c.s[q] = ssrc[min(c0 + sg + q, G - 1)];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+            if (t >= nt) break;  // uniform
+            const int64_t xr = trow[t];
+            const int32_t k0 = c0 * kGroup + 4 * tid;  // this thread's 4 inputs
+            const float* src = X + xr * I;
+            if constexpr (XV) {
+                const bool ok = k0 < I;
+                const float4 v = *reinterpret_cast<const float4*>(src + (ok ? k0 : 0));
+                c.x[t][0] = v.x;
+                c.x[t][1] = v.y;
+                c.x[t][2] = v.z;
+                c.x[t][3] = v.w;
+                if constexpr (XF == kSwiGLU) {
+                    const float4 u = *reinterpret_cast<const float4*>(X2 + xr * I + (ok ? k0 : 0));
+                    c.x[t][0] = silu(v.x) * u.x;
+                    c.x[t][1] = silu(v.y) * u.y;
+                    c.x[t][2] = silu(v.z) * u.z;
+                    c.x[t][3] = silu(v.w) * u.w;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t k = k0 + q < I ? k0 + q : 0;
+                    c.x[t][q] = src[k];
+                    if constexpr (XF == kSwiGLU) c.x[t][q] = silu(src[k]) * X2[xr * I + k];
+                }
+            }
+        }
+    };
+    auto store_chunk = [&](int32_t c0, int nt, const Chunk& c) {
+        const int gn = min(kCG, G - c0);
+#pragma unroll
+        for (int i = 0; i < kWPer; ++i)
+            *reinterpret_cast<u32x4_t*>(wl + wdst[i]) = c.w[i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sl[sg + q][srow] = sg + q < gn ? c.s[q] : 0.0f;
+        const int32_t k0 = c0 * kGroup + 4 * tid;
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+            if (t < nt) {  // uniform; columns of absent tokens stay zero
+                float x[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[q] = k0 + q < I ? c.x[t][q] : 0.0f;
+                uint32_t w[3][2];
+                split3(x, w);
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    *reinterpret_cast<u32x2_t*>(pl + (3 * t + p) * kPRow + 8 * tid) =
+                        u32x2_t{w[p][0], w[p][1]};
+            }
+        }
+    };
+
+    for (int32_t pb = p0; pb < p1; pb += kTok) {
+        const int nt = min(kTok, p1 - pb);
+        __syncthreads();  // the previous pass is done with trow/tout and LDS
+        if (tid < kTok) {
+            const int32_t p = pb + min(tid, nt - 1);
+            const int32_t xr = pair_row ? pair_row[p] : p;
+            // out-of-range rows read row 0 and are not written; the host
+            // documents the valid range, this only keeps accesses in bounds
+            const bool ok = xr >= 0 && xr < n_x_rows && tid < nt;
+            trow[tid] = (xr >= 0 && xr < n_x_rows) ? xr : 0;
+            tout[tid] = ok ? pb + tid : -1;
+        }
+        __syncthreads();
+
+        // columns of tokens past nt read zeros for the whole pass
+        for (int i = tid; i < (3 * (kTok - nt)) * (kCG * kGroup / 2); i += kThreads) {
+            const int col = 3 * nt + i / (kCG * kGroup / 2), w = i % (kCG * kGroup / 2);
+            reinterpret_cast<uint32_t*>(pl + col * kPRow)[w] = 0u;
+        }
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        Chunk cur;
+        load_chunk(0, nt, cur);
+        for (int32_t c0 = 0; c0 < G; c0 += kCG) {
+            const int gn = min(kCG, G - c0);
+            __syncthreads();  // everyone is done with the previous chunk
+            store_chunk(c0, nt, cur);
+            __syncthreads();
+            // next chunk in flight while this one is multiplied
+            if (c0 + kCG < G) load_chunk(c0 + kCG, nt, cur);
+            const uint8_t* wrow = wl + (16 * wave + l16) * kWRow;
+            const uint8_t* prow = pl + l16 * kPRow + 32 * j4;
+            for (int g = 0; g < gn; ++g) {
+                u32x4_t a0, a1;
+                if constexpr (BITS == 3) {
+                    const uint32_t lo =
+                        *reinterpret_cast<const uint32_t*>(wrow + g * kGB + 4 * j4);
+                    const uint32_t hw = *reinterpret_cast<const uint32_t*>(
+                        wrow + g * kGB + 16 + 4 * (j4 >> 1));
+                    dequant_quarter(lo, (hw >> (16 * (j4 & 1))) & 0xFFFFu, a0, a1);
+                } else {
+                    // quarter j4 = codes 16 j4 .. 16 j4 + 15 = bytes 8 j4 .. 8 j4 + 7
+                    const u32x2_t q = *reinterpret_cast<const u32x2_t*>(wrow + g * kGB + 8 * j4);
+                    a0 = dequant_word_i4(q.x);
+                    a1 = dequant_word_i4(q.y);
+                }
+                const u32x4_t b0 = *reinterpret_cast<const u32x4_t*>(prow + g * 128);
+                const u32x4_t b1 = *reinterpret_cast<const u32x4_t*>(prow + g * 128 + 16);
+                f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, b0),
+                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, a1), __builtin_bit_cast(bf16x8_t, b1), part, 0,
+                    0, 0);
+                const f32x4_t s4 =
+                    *reinterpret_cast<const f32x4_t*>(&sl[g][16 * wave + 4 * j4]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(s4[r], part[r], acc[r]);
+            }
+        }
+        // C layout: register r of lane l holds row 4*(l/16)+r of the wave's
+        // tile and column l%16 = 3t + piece; lane 3t adds its two neighbours
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v1 = from_lane_plus<1>(acc[r]);
+            const float v2 = from_lane_plus<2>(acc[r]);
+            acc[r] = (acc[r] + v1) + v2;
+            if constexpr (BITS == 4) acc[r] *= 16.0f;  // the codes entered as v/16
+        }
+        const int t = l16 / 3;
+        if (l16 % 3 == 0 && t < nt && tout[t] >= 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t o = r0 + 16 * wave + 4 * j4 + r;
+                if (o < O) Y[(int64_t)tout[t] * O + o] = acc[r];
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace qt

@@ -69,6 +69,14 @@ hipError_t launch_gptq_proxy(const float* W, const uint8_t* packed, const float*
                              int64_t O, int64_t I, const float* H, double* terms,
                              void* workspace, hipStream_t s);
 
+// MoE expert layer (moe.hip): one cooperative launch.
+size_t moe_layer_workspace(int64_t T, int64_t k, int64_t E, int64_t D, int64_t F);
+hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
+                            const float* logits, int32_t E, int32_t k, const uint8_t* gp,
+                            const float* gs, int gbits, const uint8_t* up, const float* us,
+                            int ubits, const uint8_t* dp, const float* ds, int dbits, float* out,
+                            void* workspace, hipStream_t s);
+
 int hessian_slabs(int64_t T, int64_t I);
 hipError_t launch_hessian_diag(const void* X, bool bf16, int64_t T, int64_t I, float* d,
                                int accumulate, float* workspace, hipStream_t s);

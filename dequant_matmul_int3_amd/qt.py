@@ -44,6 +44,12 @@ _SIGS = {
                                        C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32,
                                        C.c_void_p, C.c_void_p]),
     "qt_packed_bytes_i4": (C.c_int64, [C.c_int64, C.c_int64]),
+    "qt_moe_layer_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int32, C.c_int32, C.c_int64,
+                                                  C.c_int64]),
+    "qt_moe_layer": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
+                               C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                               C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
+                               C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qt_hessian_full_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int]),
     "qt_hessian_full": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_void_p, C.c_int,
                                   C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -364,3 +370,26 @@ def qt_gptq_proxy(W, packed, scales, H, terms=None, workspace=None, stream=None)
     _check(lib().qt_gptq_proxy(_ptr(W), _ptr(packed), _ptr(scales), O, I, _ptr(H), _ptr(terms),
                                _ptr(workspace), wsb, _stream(stream, dev)), "qt_gptq_proxy")
     return terms
+
+
+# ---------------------------------------------------------------- MoE layer
+def qt_moe_layer_workspace_bytes(T: int, k: int, E: int, D: int, F: int) -> int:
+    return int(lib().qt_moe_layer_workspace_bytes(T, k, E, D, F))
+
+
+def qt_moe_layer(X, logits, k: int, gate, up, down, out=None, workspace=None, stream=None):
+    """X [T, D] f32, logits [T, E] f32; gate / up / down = (packed [E, bytes],
+    scales [E, O, G], bits) with gate, up [F x D] and down [D x F] per expert
+    -> out [T, D] f32."""
+    T, D = X.shape
+    E = logits.shape[1]
+    F = gate[1].shape[1]
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=X.device)
+    workspace, wsb = _ws(qt_moe_layer_workspace_bytes(T, k, E, D, F), X.device, workspace)
+    dev = _dev(X, logits, gate[0], gate[1], up[0], up[1], down[0], down[1], out, workspace)
+    _check(lib().qt_moe_layer(_ptr(X), T, D, F, _ptr(logits), E, k, _ptr(gate[0]),
+                              _ptr(gate[1]), int(gate[2]), _ptr(up[0]), _ptr(up[1]), int(up[2]),
+                              _ptr(down[0]), _ptr(down[1]), int(down[2]), _ptr(out),
+                              _ptr(workspace), wsb, _stream(stream, dev)), "qt_moe_layer")
+    return out

@@ -333,6 +333,38 @@ qt_status qt_gptq_proxy(const float* W, const uint8_t* packed, const float* scal
                         int64_t O, int64_t I, const float* H, double* terms,
                         void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Mixture-of-experts expert layer in one persistent (cooperative) launch:
+ * routing, gate and up projections, SwiGLU, down projection and the combine
+ * of each token's experts (the pull request page's MoE decode setting; its
+ * per-projection ablation names gate_proj, up_proj and down_proj, each at
+ * int3-g64 or grouped int4).  The pages give no expert formula or combine
+ * rule; this library reads them as
+ *   experts of token t: the k largest logits[t] (equal logits: lower expert
+ *   index first); weights w_tj = softmax over those k logits (f32);
+ *   y_e(x) = W_down,e (silu(W_gate,e x) * (W_up,e x)), silu(z) = z/(1+e^-z);
+ *   out[t] = sum_j w_tj y_{e_tj}(x_t), j in descending-logit order.
+ * Each projection is the grouped multiply (exact codes and exact 3-piece
+ * splits of the f32 inputs on the matrix cores, f32 per-group sums).
+ *   X [T x D] f32 (16-byte aligned), logits [T x E] f32; experts stored back
+ *   to back: gate, up [E][F x D], down [E][D x F], each packed in its format
+ *   (bits 3: 24-byte int3-g64 groups, 4: 32-byte grouped int4) with scales
+ *   [E][rows x cols/64]; out [T x D] f32 (16-byte aligned).
+ *   D and F multiples of 128; 1 <= k <= min(32, E); E <= 65535.
+ *   workspace: qt_moe_layer_workspace_bytes(T, k, E, D, F) bytes (routing
+ *   tables and the f32 products, (T k)(2F + D) * 4 plus small tables).
+ * The launch keeps every block of its grid resident until its last barrier;
+ * results are deterministic.
+ */
+size_t qt_moe_layer_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t D, int64_t F);
+qt_status qt_moe_layer(const float* X, int64_t T, int64_t D, int64_t F, const float* logits,
+                       int32_t E, int32_t k, const uint8_t* gate_packed,
+                       const float* gate_scales, int32_t gate_bits,
+                       const uint8_t* up_packed, const float* up_scales, int32_t up_bits,
+                       const uint8_t* down_packed, const float* down_scales,
+                       int32_t down_bits, float* out, void* workspace, size_t ws_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

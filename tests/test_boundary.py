@@ -191,3 +191,27 @@ def test_int4_grouped_rejects():
     assert f(A + 8, B, 8, 4, 64, Cc, 4, None, A + (1 << 30), 4, D, None) == QT_ERR_ALIGN
     # 8 experts x 4 rows x 32 bytes = 1024 packed bytes from A: Y at A + 1000 overlaps
     assert f(A, B, 8, 4, 64, Cc, 4, None, A + (1 << 30), 4, A + 1000, None) == QT_ERR_ALIAS
+
+
+def test_moe_layer_rejects():
+    f = L.qt_moe_layer
+    ok = dict(T=4, D=256, F=128, E=8, k=2)
+
+    def call(X=A, T=4, D=256, F=128, lg=B, E=8, k=2, gb=3, ub=3, db=3, out=D_OUT, ws=WS,
+             wsb=1 << 30):
+        return f(X, T, D, F, lg, E, k, P1, S1, gb, P2, S2, ub, P3, S3, db, out, ws, wsb, None)
+    assert call(X=None) == QT_ERR_NULL
+    assert call(D=200) == QT_ERR_SHAPE          # not a multiple of 128
+    assert call(F=64) == QT_ERR_SHAPE
+    assert call(k=0) == QT_ERR_SHAPE and call(k=9, E=8) == QT_ERR_SHAPE and call(k=33, E=64) == QT_ERR_SHAPE
+    assert call(gb=5) == QT_ERR_ARG
+    assert call(wsb=16) == QT_ERR_WORKSPACE
+    assert call(X=A + 4) == QT_ERR_ALIGN
+    assert call(out=A + 1024) == QT_ERR_ALIAS    # inside X (4 x 256 f32)
+    assert ok
+
+
+P1, S1, P2, S2, P3, S3 = (0x7F4000000000, 0x7F5000000000, 0x7F6000000000, 0x7F7000000000,
+                          0x7F8000000000, 0x7F9000000000)
+D_OUT = 0x7FA000000000
+WS = 0x7FB000000000

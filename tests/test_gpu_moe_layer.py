@@ -1,0 +1,84 @@
+"""The MoE expert layer (one cooperative launch: routing, gate/up, SwiGLU,
+down, combine) against the oracle's f64 layer: every output within 1e-5 of
+the error budget the oracle derives from the grouped multiply's tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_int3_amd as qt
+import oracle
+import workloads
+from tests.gpu_util import bits as fbits, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def experts(E, F, D, seed, bits):
+    out = []
+    for n, ((O, I), b) in enumerate((((F, D), bits[0]), ((F, D), bits[1]), ((D, F), bits[2]))):
+        ps, ss = [], []
+        for e in range(E):
+            W = workloads.generic_weights(O, I, seed=seed * 1000 + 100 * n + e)
+            if b == 3:
+                s, c, _ = oracle.quantize_g64(W)
+                p = oracle.pack_i3(c)
+            else:
+                s, c, _ = oracle.quantize_g64_i4(W)
+                p = oracle.pack_i4(c)
+            ps.append(p)
+            ss.append(s)
+        out.append((np.stack(ps), np.stack(ss), b))
+    return out
+
+
+def run_gpu(X, logits, k, gate, up, down):
+    g = tuple(dev(a) if isinstance(a, np.ndarray) else a for a in gate)
+    u = tuple(dev(a) if isinstance(a, np.ndarray) else a for a in up)
+    d = tuple(dev(a) if isinstance(a, np.ndarray) else a for a in down)
+    return host(qt.qt_moe_layer(dev(X), dev(logits), k, g, u, d))
+
+
+def check(X, logits, k, gate, up, down, tag):
+    T, D = X.shape
+    say(f"moe layer {tag} T={T} D={D} E={logits.shape[1]} k={k}")
+    out = run_gpu(X, logits, k, gate, up, down)
+    ref, bound = oracle.moe_layer_f64(X, logits, k, gate, up, down)
+    err = np.max(np.abs(out - ref) / bound)
+    say(f"  max error / budget {err:.3e}")
+    assert err <= TOL
+    return out
+
+
+@pytest.mark.parametrize("scheme", [(3, 3, 3), (4, 3, 4), (4, 4, 4), (3, 4, 3)])
+def test_moe_layer_schemes(scheme):
+    E, F, D, T, k = 6, 128, 256, 5, 2
+    gate, up, down = experts(E, F, D, 1, scheme)
+    X = workloads.generic_matrix(T, D, seed=2)
+    logits = workloads.rng_for("generic", 900, T, E).random((T, E)).astype(np.float32)
+    check(X, logits, k, gate, up, down, f"bits {scheme}")
+
+
+@pytest.mark.parametrize("E,F,D,T,k", [(16, 256, 512, 12, 4), (8, 128, 128, 33, 8),
+                                       (3, 384, 256, 1, 1), (5, 128, 384, 7, 5)])
+def test_moe_layer_shapes(E, F, D, T, k):
+    gate, up, down = experts(E, F, D, E + T, (3, 3, 3))
+    X = workloads.generic_matrix(T, D, seed=T)
+    logits = workloads.rng_for("generic", 901, T, E).random((T, E)).astype(np.float32)
+    out1 = check(X, logits, k, gate, up, down, "shape")
+    out2 = run_gpu(X, logits, k, gate, up, down)
+    assert np.array_equal(fbits(out1), fbits(out2)), "not deterministic"
+
+
+def test_moe_layer_routing_ties_and_idle_experts():
+    # tied logits pick the lower expert first; experts nobody picks are idle
+    E, F, D, T, k = 8, 128, 128, 4, 3
+    gate, up, down = experts(E, F, D, 5, (3, 3, 3))
+    X = workloads.generic_matrix(T, D, seed=6)
+    logits = np.zeros((T, E), np.float32)
+    logits[0, [2, 5, 6]] = 1.0          # a three-way tie at the top
+    logits[1, [1, 2]] = [0.5, 0.5]      # tie for the first two, then index order
+    logits[2] = np.arange(E, dtype=np.float32)[::-1]
+    logits[3, 7] = 2.0
+    check(X, logits, k, gate, up, down, "ties")
