@@ -246,7 +246,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-LEG_NAMES = ["quant", "search", "moe", "prefill", "int4", "moe_int4", "gptq"]
+LEG_NAMES = ["quant", "search", "moe", "prefill", "int4", "moe_int4", "gptq", "moe_layer"]
 
 
 def run_legs(torch, qt, workloads, dev, which, args):
@@ -267,7 +267,61 @@ def run_legs(torch, qt, workloads, dev, which, args):
         int4_leg(torch, qt, workloads, dev, legs, args)
     if "gptq" in which:
         gptq_leg(torch, qt, workloads, dev, legs)
+    if "moe_layer" in which:
+        moe_layer_leg(torch, qt, workloads, dev, legs)
     return legs
+
+
+def moe_layer_leg(torch, qt, workloads, dev, legs):
+    # ------------------- MoE expert layer (gate/up/down, routing, combine)
+    E, T, k = workloads.MOE_EXPERTS, workloads.MOE_TOKENS, workloads.MOE_TOPK
+    (F, D) = workloads.MOE_UP_SHAPE
+    log("leg moe_layer: generating and quantizing 128 experts x (gate, up, down)")
+    fmt = {3: (qt.qt_packed_bytes, qt.qt_quantize_g64, qt.qt_pack_i3),
+           4: (qt.qt_packed_bytes_i4, qt.qt_quantize_g64_i4, qt.qt_pack_i4)}
+    need = {("gate", 3), ("up", 3), ("down", 3), ("gate", 4), ("down", 4)}
+    shapes = {"gate": (F, D), "up": (F, D), "down": (D, F)}
+    store = {}
+    for proj, b in need:
+        O_, I_ = shapes[proj]
+        store[proj, b] = (torch.empty((E, fmt[b][0](O_, I_)), dtype=torch.uint8, device=dev),
+                          torch.empty((E, O_, qt.qt_groups(I_)), dtype=torch.float32, device=dev), b)
+    for proj in ("gate", "up", "down"):
+        bl = sorted(b for (pr, b) in need if pr == proj)
+        for e0 in range(0, E, 16):
+            mats = workloads.moe_experts_parallel(proj, range(e0, e0 + 16), workers=16)
+            for j, m in enumerate(mats):
+                md = torch.from_numpy(m).to(dev)
+                for b in bl:
+                    pk, sc, _ = store[proj, b]
+                    s_, c_, _ = fmt[b][1](md, want_grid_idx=False)
+                    sc[e0 + j].copy_(s_)
+                    fmt[b][2](c_, pk[e0 + j])
+            torch.cuda.synchronize()
+    Xm, _ = workloads.moe_tokens()
+    Xd = torch.from_numpy(Xm).to(dev)
+    Ld = torch.from_numpy(workloads.moe_logits().astype(np.float32)).to(dev)
+    out = torch.empty((T, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(qt.qt_moe_layer_workspace_bytes(T, k, E, D, F), dtype=torch.uint8, device=dev)
+    _, topk = workloads.moe_tokens()
+    hit = len(np.unique(topk))
+    for name, (gb, ub, db) in (("moe_layer", (3, 3, 3)), ("moe_layer_int4_up3", (4, 3, 4))):
+        g, u, d = store["gate", gb], store["up", ub], store["down", db]
+
+        def step(i):
+            qt.qt_moe_layer(Xd, Ld, k, g, u, d, out=out, workspace=ws)
+
+        for i in range(3):
+            step(i)
+        ms = time_launches(step, 20, torch)
+        per_exp = sum(a[0].shape[1] + a[1][0].numel() * 4 for a in (g, u, d))
+        mb = hit * per_exp + Xm.nbytes + T * D * 4
+        legs[name] = {"ms": round(ms, 4), "experts_hit": hit, "bits": [gb, ub, db],
+                      "GB_s": round(mb / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
+                      "frac": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "bytes_per_step": int(mb), "launches": 1}
+        log(f"leg {name}: {legs[name]}")
+    del store, out, ws
 
 
 F32_MFMA_PEAK_TFLOPS = 157.3   # dense f32 matrix cores

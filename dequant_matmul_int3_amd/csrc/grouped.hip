@@ -43,8 +43,8 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
     const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t P,
     float* __restrict__ Y) {
     __shared__ TileLds<Geo<BITS>::kWRow> lds;
-    grouped_tile<BITS, W16, XV, kPlain>(lds, blockIdx.y, blockIdx.x, packed, scales, O, I, G, X,
-                                        nullptr, n_x_rows, pair_row, off, P, Y);
+    grouped_tile<BITS, W16, XV>(lds, blockIdx.y, blockIdx.x, packed, scales, O, I, G, X, n_x_rows,
+                                pair_row, off, P, Y);
 }
 
 }  // namespace

@@ -135,21 +135,18 @@ struct TileLds {
     int32_t tout[kTok];
 };
 
-enum XForm { kPlain = 0, kSwiGLU = 1 };
-
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // One item: the pairs of expert e against its rows [64 rb, 64 rb + 64).
 // W16: every row's chunk bytes start on a 16-byte boundary (int4, or int3
 // with G even); else 8-byte pieces.  XV: inputs allow 16-byte loads
-// (I % 4 == 0, X 16-byte aligned).  XF == kSwiGLU: input row r is
-// silu(X[r]) * X2[r] elementwise, formed as it is loaded.  Starts with a
-// barrier, so items can follow one another in a block.
-template <int BITS, bool W16, bool XV, int XF, int WROW>
+// (I % 4 == 0, X 16-byte aligned).  Starts with a barrier, so items can
+// follow one another in a block.
+template <int BITS, bool W16, bool XV, int WROW>
 __device__ __forceinline__ void grouped_tile(
     TileLds<WROW>& L, int e, int64_t rb, const uint8_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t O, int32_t I, int32_t G,
-    const float* __restrict__ X, const float* __restrict__ X2, int64_t n_x_rows,
+    const float* __restrict__ X, int64_t n_x_rows,
     const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t P,
     float* __restrict__ Y) {
     constexpr int kGB = Geo<BITS>::kGB;
@@ -239,20 +236,9 @@ __device__ __forceinline__ void grouped_tile(
                 c.x[t][1] = v.y;
                 c.x[t][2] = v.z;
                 c.x[t][3] = v.w;
-                if constexpr (XF == kSwiGLU) {
-                    const float4 u = *reinterpret_cast<const float4*>(X2 + xr * I + (ok ? k0 : 0));
-                    c.x[t][0] = silu(v.x) * u.x;
-                    c.x[t][1] = silu(v.y) * u.y;
-                    c.x[t][2] = silu(v.z) * u.z;
-                    c.x[t][3] = silu(v.w) * u.w;
-                }
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t k = k0 + q < I ? k0 + q : 0;
-                    c.x[t][q] = src[k];
-                    if constexpr (XF == kSwiGLU) c.x[t][q] = silu(src[k]) * X2[xr * I + k];
-                }
+                for (int q = 0; q < 4; ++q) c.x[t][q] = src[k0 + q < I ? k0 + q : 0];
             }
         }
     };

@@ -9,10 +9,10 @@
 //  0. block 0 routes: per token the k largest logits (equal logits: lower
 //     expert first), combine weights a softmax over them; the (expert,
 //     token) pairs sorted by expert, then token.
-//  1. items (gate | up, expert, 64-row block): the grouped matrix-core tile,
-//     g and u for every pair of the expert.
-//  2. items (expert, 64-row block of down): the same tile on the inputs
-//     h = silu(g) * u, formed as they are loaded (no h buffer, no pass).
+//  1. items (expert, 64-row block of gate and up): the grouped matrix-core
+//     tile for gate, then for up, then h = silu(g) * u for those rows of
+//     every pair of the expert.
+//  2. items (expert, 64-row block of down): the same tile on h.
 //  3. out[t] = sum_j w_tj y_{pair(t, j)} in j order.
 // Items are dealt round-robin over the blocks; experts without pairs cost a
 // read of two offsets.
@@ -26,6 +26,8 @@ namespace {
 namespace cg = cooperative_groups;
 
 constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 512;  // routing keeps a token's logits in registers (32 per lane)
+constexpr int kRouteLdsPairs = (20 * 1024 - 16 * 32 * 4 - 2 * 256 * 4) / 4;  // selections in LDS
 
 struct MoeArgs {
     const float* X;  // [T x D]
@@ -47,106 +49,161 @@ struct MoeArgs {
     int32_t* offs;   // [E + 1]
     float* Yg;       // [P x F]
     float* Yu;       // [P x F]
+    float* H;        // [P x F] silu(g) * u
     float* Yd;       // [P x D]
 };
 
-// Phase 0, one block.
-__device__ void route(const MoeArgs& a) {
+// Phase 0, one block: a wave per token picks its k experts one at a time
+// (each pick the largest logit after the previous one in the order
+// (-logit, expert): the lanes scan the logits, a butterfly keeps the larger,
+// on equal logits the lower expert); then counts per expert (order-free
+// atomics), offsets, and each pair's slot = its expert's offset + the number
+// of earlier tokens that chose the same expert.
+// value of lane (l - N) mod 16 of this lane's 16-lane row
+template <int N>
+__device__ __forceinline__ int row_ror(int v) {
+    return __builtin_amdgcn_mov_dpp(v, 0x120 + N, 0xF, 0xF, false);
+}
+
+__device__ void route(const MoeArgs& a, uint8_t* scratch /* >= 20 KB of LDS */) {
     const int tid = threadIdx.x;
-    const int E = a.E, k = a.k;
-    for (int t = tid; t < a.T; t += kThreads) {
-        const float* L = a.logits + (int64_t)t * E;
-        float sv[kMaxTopK];
-        int si[kMaxTopK];
-        // the j-th pick: the smallest key (-logit, expert) above the previous
+    const int sub = tid & 15;              // lane within the token's 16-lane row
+    const int row = tid >> 4;              // 16 tokens in flight per block
+    const int E = a.E, k = a.k, Pn = a.T * a.k;
+    float* svals = reinterpret_cast<float*>(scratch);           // [16][kMaxTopK]
+    int* part = reinterpret_cast<int*>(scratch + 16 * kMaxTopK * 4);  // [2][kThreads] scan
+    int* lsel = part + 2 * kThreads;                             // [Pn] if it fits
+    const bool sel_in_lds = Pn <= kRouteLdsPairs;
+    for (int e = tid; e <= E; e += kThreads) a.offs[e] = 0;
+    for (int t0 = 0; t0 < a.T; t0 += kThreads / 16) {
+        const int t = t0 + row;
+        const bool live = t < a.T;  // uniform over the 16-lane row
+        const float* L = a.logits + (int64_t)(live ? t : 0) * E;
+        float lv[kMaxExperts / 16];  // logits sub + 16 m, read once
+#pragma unroll
+        for (int m = 0; m < kMaxExperts / 16; ++m) {
+            const int e = sub + 16 * m;
+            lv[m] = e < E ? L[e] : 0.0f;
+        }
         float pv = 0.0f;
         int pi = -1;
         for (int j = 0; j < k; ++j) {
             float bv = 0.0f;
             int bi = -1;
-            for (int e = 0; e < E; ++e) {
-                const float v = L[e];
+#pragma unroll
+            for (int m = 0; m < kMaxExperts / 16; ++m) {
+                const int e = sub + 16 * m;
+                const float v = lv[m];
                 const bool after = pi < 0 || v < pv || (v == pv && e > pi);
-                if (after && (bi < 0 || v > bv)) {  // ascending e: ties keep the lower
+                if (e < E && after && (bi < 0 || v > bv)) {  // ascending e: ties keep the lower
                     bv = v;
                     bi = e;
                 }
             }
-            sv[j] = bv;
-            si[j] = bi;
+            // all 16 lanes of the row end with the row's best (rotations by
+            // 8, 4, 2, 1 combine every lane's candidate)
+#define QT_ROUTE_STEP(N)                                                              \
+    {                                                                                 \
+        const float ov = __int_as_float(row_ror<N>(__float_as_int(bv)));              \
+        const int oi = row_ror<N>(bi);                                                \
+        if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {                 \
+            bv = ov;                                                                  \
+            bi = oi;                                                                  \
+        }                                                                             \
+    }
+            QT_ROUTE_STEP(8)
+            QT_ROUTE_STEP(4)
+            QT_ROUTE_STEP(2)
+            QT_ROUTE_STEP(1)
+#undef QT_ROUTE_STEP
             pv = bv;
             pi = bi;
-        }
-        float z[kMaxTopK];
-        float sum = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            z[j] = expf(sv[j] - sv[0]);
-            sum += z[j];
-        }
-        for (int j = 0; j < k; ++j) {
-            a.sel[t * k + j] = si[j];
-            a.wgt[t * k + j] = z[j] / sum;
-        }
-    }
-    __syncthreads();
-    // counts per expert, then offsets (one thread), then placement in token order
-    for (int e = tid; e < E; e += kThreads) {
-        int c = 0;
-        for (int q = 0; q < a.T * k; ++q) c += a.sel[q] == e;
-        a.offs[e + 1] = c;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        a.offs[0] = 0;
-        for (int e = 0; e < E; ++e) a.offs[e + 1] += a.offs[e];
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kThreads) {
-        int pos = a.offs[e];
-        for (int q = 0; q < a.T * k; ++q)
-            if (a.sel[q] == e) {
-                a.prow[pos] = q / k;
-                a.slot[q] = pos;
-                ++pos;
+            if (live && sub == 0) {
+                a.sel[t * k + j] = bi;
+                if (sel_in_lds) lsel[t * k + j] = bi;
+                svals[row * kMaxTopK + j] = bv;
             }
+        }
+        if (live && sub == 0) {  // combine weights: softmax over the k picks
+            const float* sv = svals + row * kMaxTopK;
+            float sum = 0.0f;
+            for (int j = 0; j < k; ++j) sum += expf(sv[j] - sv[0]);
+            for (int j = 0; j < k; ++j) a.wgt[t * k + j] = expf(sv[j] - sv[0]) / sum;
+        }
+    }
+    __syncthreads();
+    const int* sel = sel_in_lds ? lsel : a.sel;
+    for (int q = tid; q < Pn; q += kThreads) atomicAdd(&a.offs[sel[q] + 1], 1);
+    __syncthreads();
+    // offsets: each thread totals a contiguous run of experts, the totals
+    // are scanned in LDS (log steps), then each run is rewritten from its base
+    const int run = (E + kThreads - 1) / kThreads;
+    const int e0 = tid * run, e1 = min(E, e0 + run);
+    int tot = 0;
+    for (int e = e0; e < e1; ++e) tot += a.offs[e + 1];
+    part[tid] = tot;
+    __syncthreads();
+    int cur = 0;
+    for (int d = 1; d < kThreads; d <<= 1) {
+        const int v = part[cur * kThreads + tid] + (tid >= d ? part[cur * kThreads + tid - d] : 0);
+        part[(cur ^ 1) * kThreads + tid] = v;
+        cur ^= 1;
+        __syncthreads();
+    }
+    int base = tid > 0 ? part[cur * kThreads + tid - 1] : 0;
+    for (int e = e0; e < e1; ++e) {
+        base += a.offs[e + 1];
+        a.offs[e + 1] = base;
+    }
+    __syncthreads();
+    for (int q = tid; q < Pn; q += kThreads) {
+        const int e = sel[q], t = q / k;
+        int rank = 0;
+        for (int q2 = 0; q2 < t * k; ++q2) rank += sel[q2] == e;  // a token picks e at most once
+        const int pos = a.offs[e] + rank;
+        a.prow[pos] = t;
+        a.slot[q] = pos;
     }
 }
 
-template <int XF>
-__device__ __forceinline__ void tile_bits(TileLds<Geo<4>::kWRow>& L, int bits, int e, int64_t rb,
+template <int BITS, int WROW>
+__device__ __forceinline__ void tile_bits(TileLds<WROW>& L, int e, int64_t rb,
                                           const uint8_t* packed, const float* scales, int64_t O,
-                                          int32_t I, const float* X, const float* X2,
-                                          int64_t nx, const int32_t* prow, const int32_t* offs,
-                                          int32_t P, float* Y) {
+                                          int32_t I, const float* X, int64_t nx,
+                                          const int32_t* prow, const int32_t* offs, int32_t P,
+                                          float* Y) {
     const int32_t G = (I + kGroup - 1) / kGroup;
-    if (bits == 3)
-        grouped_tile<3, true, true, XF>(L, e, rb, packed, scales, O, I, G, X, X2, nx, prow, offs,
-                                        P, Y);
-    else
-        grouped_tile<4, true, true, XF>(L, e, rb, packed, scales, O, I, G, X, X2, nx, prow, offs,
-                                        P, Y);
+    grouped_tile<BITS, true, true>(L, e, rb, packed, scales, O, I, G, X, nx, prow, offs, P, Y);
 }
 
+// GB, UB, DB: the formats (3 or 4 bits) of gate, up and down.
+template <int GB, int UB, int DB>
 __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
-    __shared__ TileLds<Geo<4>::kWRow> lds;
+    constexpr int kW = (GB == 4 || UB == 4 || DB == 4) ? Geo<4>::kWRow : Geo<3>::kWRow;
+    __shared__ TileLds<kW> lds;
+    static_assert(sizeof(lds.wl) >= 20 * 1024, "the routing borrows 20 KB of the weight LDS");
     cg::grid_group grid = cg::this_grid();
     const int P = a.T * a.k;
-    if (blockIdx.x == 0) route(a);
+    // the routing borrows the tile's weight LDS (no tile has run yet)
+    if (blockIdx.x == 0) route(a, lds.wl);
     grid.sync();
 
     const int64_t nf = (a.F + kRows - 1) / kRows, nd = (a.D + kRows - 1) / kRows;
-    const int64_t items1 = 2 * a.E * nf;
+    const int64_t items1 = a.E * nf;
     for (int64_t it = blockIdx.x; it < items1; it += gridDim.x) {
-        const int proj = (int)(it / (a.E * nf));
-        const int64_t rem = it % (a.E * nf);
-        const int e = (int)(rem / nf);
-        const int64_t rb = rem % nf;
-        if (proj == 0)
-            tile_bits<kPlain>(lds, a.gbits, e, rb, a.gp, a.gs, a.F, a.D, a.X, nullptr, a.T, a.prow,
-                              a.offs, P, a.Yg);
-        else
-            tile_bits<kPlain>(lds, a.ubits, e, rb, a.up, a.us, a.F, a.D, a.X, nullptr, a.T, a.prow,
-                              a.offs, P, a.Yu);
+        const int e = (int)(it / nf);
+        const int64_t rb = it % nf;
+        tile_bits<GB>(lds, e, rb, a.gp, a.gs, a.F, a.D, a.X, a.T, a.prow, a.offs, P, a.Yg);
+        tile_bits<UB>(lds, e, rb, a.up, a.us, a.F, a.D, a.X, a.T, a.prow, a.offs, P, a.Yu);
+        // h for this block's rows of every pair of the expert (the tiles'
+        // stores above come from this block: a barrier makes them visible)
+        const int p0 = a.offs[e], p1 = a.offs[e + 1];
+        __syncthreads();
+        const int64_t r0 = rb * kRows;
+        for (int q = threadIdx.x; q < (p1 - p0) * kRows; q += kThreads) {
+            const int64_t p = p0 + q / kRows, r = r0 + q % kRows;
+            if (r < a.F) a.H[p * a.F + r] = silu(a.Yg[p * a.F + r]) * a.Yu[p * a.F + r];
+        }
     }
     grid.sync();
 
@@ -154,8 +211,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     for (int64_t it = blockIdx.x; it < items2; it += gridDim.x) {
         const int e = (int)(it / nd);
         const int64_t rb = it % nd;
-        tile_bits<kSwiGLU>(lds, a.dbits, e, rb, a.dp, a.ds, a.D, a.F, a.Yg, a.Yu, P, nullptr,
-                           a.offs, P, a.Yd);
+        tile_bits<DB>(lds, e, rb, a.dp, a.ds, a.D, a.F, a.H, P, nullptr, a.offs, P, a.Yd);
     }
     grid.sync();
 
@@ -175,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 size_t moe_layer_workspace(int64_t T, int64_t k, int64_t E, int64_t D, int64_t F) {
     const int64_t P = T * k;
     auto up16 = [](int64_t b) { return (b + 15) / 16 * 16; };
-    return (size_t)(4 * up16(P * 4) + up16((E + 1) * 4) + up16(2 * P * F * 4) + up16(P * D * 4));
+    return (size_t)(4 * up16(P * 4) + up16((E + 1) * 4) + up16(3 * P * F * 4) + up16(P * D * 4));
 }
 
 hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
@@ -183,7 +239,7 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
                             const float* gs, int gbits, const uint8_t* up, const float* us,
                             int ubits, const uint8_t* dp, const float* ds, int dbits, float* out,
                             void* workspace, hipStream_t s) {
-    if (k > kMaxTopK) return hipErrorInvalidValue;
+    if (k > kMaxTopK || E > kMaxExperts) return hipErrorInvalidValue;
     const int64_t P = T * k;
     auto up16 = [](int64_t b) { return (b + 15) / 16 * 16; };
     uint8_t* w = static_cast<uint8_t*>(workspace);
@@ -217,20 +273,32 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
     w += up16((E + 1) * 4);
     a.Yg = reinterpret_cast<float*>(w);
     a.Yu = a.Yg + P * F;
-    w += up16(2 * P * F * 4);
+    a.H = a.Yu + P * F;
+    w += up16(3 * P * F * 4);
     a.Yd = reinterpret_cast<float*>(w);
 
+    const int code = (gbits - 3) * 4 + (ubits - 3) * 2 + (dbits - 3);
+    const void* kernels[8] = {
+        reinterpret_cast<const void*>(moe_layer_kernel<3, 3, 3>),
+        reinterpret_cast<const void*>(moe_layer_kernel<3, 3, 4>),
+        reinterpret_cast<const void*>(moe_layer_kernel<3, 4, 3>),
+        reinterpret_cast<const void*>(moe_layer_kernel<3, 4, 4>),
+        reinterpret_cast<const void*>(moe_layer_kernel<4, 3, 3>),
+        reinterpret_cast<const void*>(moe_layer_kernel<4, 3, 4>),
+        reinterpret_cast<const void*>(moe_layer_kernel<4, 4, 3>),
+        reinterpret_cast<const void*>(moe_layer_kernel<4, 4, 4>)};
+    if (code < 0 || code > 7) return hipErrorInvalidValue;
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layer_kernel, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernels[code], kThreads, 0);
     if (e != hipSuccess) return e;
     if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
     void* args[] = {&a};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(moe_layer_kernel),
-                                      dim3((unsigned)(per_cu * cus)), dim3(kThreads), args, 0, s);
+    return hipLaunchCooperativeKernel(kernels[code], dim3((unsigned)(per_cu * cus)), dim3(kThreads),
+                                      args, 0, s);
 }
 
 }  // namespace qt

@@ -52,7 +52,7 @@ SEARCH_TOKENS = 8192
 # independently of the others (and in parallel)
 _TAG = {"decode": 1, "decode_tail": 2, "moe_up": 3, "moe_down": 4, "moe_x": 5,
         "moe_route": 6, "prefill_w": 7, "prefill_x": 8, "search_w": 9,
-        "search_z": 10, "search_c": 11, "generic": 12}
+        "search_z": 10, "search_c": 11, "generic": 12, "moe_gate": 13}
 
 
 def rng_for(tag: str, *idx: int) -> np.random.Generator:
@@ -98,8 +98,8 @@ def decode(tail: bool = False):
 
 
 def moe_expert(e: int, which: str) -> np.ndarray:
-    """Weight matrix of expert e; which is 'up' [2048x7168] or 'down' [7168x2048]."""
-    shape = MOE_UP_SHAPE if which == "up" else MOE_DOWN_SHAPE
+    """Weight matrix of expert e; which is 'gate' or 'up' [2048x7168], or 'down' [7168x2048]."""
+    shape = MOE_DOWN_SHAPE if which == "down" else MOE_UP_SHAPE
     return outlier_weights(rng_for("moe_" + which, e), *shape)
 
 
@@ -109,10 +109,15 @@ def moe_experts_parallel(which: str, experts, workers: int = 8):
         return list(ex.map(lambda e: moe_expert(e, which), experts))
 
 
+def moe_logits() -> np.ndarray:
+    """Routing logits [32x128], uniform in [0, 1) (float64 draws)."""
+    return rng_for("moe_route").random(size=(MOE_TOKENS, MOE_EXPERTS))
+
+
 def moe_tokens():
     """X[32x7168] and the top-8 routing: (X, topk_experts[32x8])."""
     x = _normal_f32(rng_for("moe_x"), 1.0, (MOE_TOKENS, MOE_UP_SHAPE[1]))
-    logits = rng_for("moe_route").random(size=(MOE_TOKENS, MOE_EXPERTS))
+    logits = moe_logits()
     # top-8 by value, descending; stable order for equal logits (none occur)
     topk = np.argsort(-logits, axis=1, kind="stable")[:, :MOE_TOPK]
     return x, topk.astype(np.int32)
