@@ -192,7 +192,7 @@ def main():
     tr = traffic_for("gemv_decode", bytes_step)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": tr, "kernel": "gemv_batch_kernel<64,8,1,f32,vec>",
+                "traffic": tr, "kernel": "gemv_batch_kernel<128,16,1,128,f32,vec>",
                 "launch_us_mean": round(ms_step * 1e3, 3),
                 "eager_event_pair_us_mean": round(kmean * 1e3, 3),
                 "bytes_per_launch": bytes_step}
@@ -419,7 +419,7 @@ def int4_leg(torch, qt, workloads, dev, legs, args):
     legs["gemv_decode_int4"] = {"us": round(ms * 1e3, 3), "GB_s": round(gbs, 1), "bound": "hbm",
                                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                                 "bytes_per_launch": int(bytes_step),
-                                "kernel": "gemv_batch_kernel<64,8,1,f32,vec,int4>"}
+                                "kernel": "gemv_batch_kernel<128,16,1,128,f32,vec,int4>"}
     legs["quantize_rtn_decode_int4"] = {"ms": round(ms_q, 5),
                                         "groups_per_s": round(O * G / (ms_q * 1e-3))}
     bytes_p = O * I + p.numel()

@@ -12,7 +12,7 @@
 //    row, lane q taking groups q, q+LPR, q+2*LPR, ... of the current chunk.
 //  * The inputs of the current chunk of groups are staged in LDS as f32, one
 //    68-float slot per group (4 floats of padding shift consecutive groups by 4
-//    banks).  All rows of a wave read the same addresses, which LDS broadcasts.
+//    banks, so the 16-byte reads of 16 lanes at a time hit distinct banks).
 //  * Every thread issues its input loads, then its weight loads (24 packed
 //    bytes and a scale per group), and only then waits to store the inputs to
 //    LDS, so the two latencies overlap.
@@ -24,9 +24,15 @@
 //    f32 rounding.  int4 nibbles become f16 pairs by the 1024-bias trick: the
 //    f16 word 0x6400 | u is 1024 + u exactly, and one packed f16 subtraction
 //    of 1032 leaves v = u - 8.  Four interleaved accumulators per token hide
-//    FMA latency;
-//    the LPR partial row sums are combined by a fixed xor butterfly, so
-//    results are deterministic.
+//    FMA latency.
+//  * The LPR partial row sums are combined in a fixed order (DPP steps inside
+//    16-lane rows, lane reads across the rows of a wave, then the waves of a
+//    row through LDS), so results are deterministic.
+//  * Launch shapes: one token uses 16 waves of 128 lanes per row (one group
+//    per lane, 8 rows per block, one block per CU at the decode size), so that
+//    four waves per SIMD overlap their loads with the other waves' arithmetic;
+//    larger tiles use 8 waves of 64 lanes per row.  The inputs of a chunk of
+//    GC groups of all T tokens are staged at once.
 #include <algorithm>
 
 #include "qt_internal.h"
@@ -282,16 +288,45 @@ struct InputStage {
     }
 };
 
+// Sum over aligned groups of WL lanes (WL = 16, 32 or 64), valid in the
+// first lane of each group, in a fixed order: pairs and quads by quad
+// permutes, then rotations by 4 and 8 inside each 16-lane row, then the row
+// sums read from lanes 0, 16, 32, 48.
+template <int DPP>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), DPP, 0xF, 0xF, false));
+}
+
+template <int WL>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    static_assert(WL == 16 || WL == 32 || WL == 64, "16, 32 or 64 lanes");
+    v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x124>(v);  // row_ror 4
+    v += dpp_f<0x128>(v);  // row_ror 8
+    if constexpr (WL == 16) {
+        return v;
+    } else {
+        const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+        const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+        const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+        const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+        if constexpr (WL == 32)
+            return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+        else
+            return (r0 + r1) + (r2 + r3);
+    }
+}
+
 // Rows [r0, r0+RB) of one matrix against the tokens listed in tok_rows
 // (input row of each token) / tok_outs (output row of each token, -1 = do not
 // store), T tokens per pass over the weights.
-template <int LPR, int WAVES, int T, bool BF16, bool VEC, int BITS>
+template <int LPR, int WAVES, int T, int GC, bool BF16, bool VEC, int BITS>
 __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __restrict__ scales,
                           int64_t O, int64_t I, int64_t G, const void* __restrict__ X,
                           const int32_t* tok_rows, const int32_t* tok_outs, int ntok,
                           float* __restrict__ Y, int64_t r0, float* lds) {
     constexpr int NTHR = WAVES * 64;
-    constexpr int GC = 128 / T;               // groups per chunk
     constexpr int NG = (GC + LPR - 1) / LPR;  // groups per lane per chunk
     static_assert(GC >= LPR, "each lane needs at least one group per chunk");
     float* xs = lds;
@@ -336,19 +371,16 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
                 }
             }
         }
-        // combine the LPR partial sums of each row: a fixed xor butterfly
-        // inside the wave, then (rows wider than a wave) the per-wave sums in
-        // wave order through LDS
+        // combine the LPR partial sums of each row in a fixed order: DPP
+        // steps inside each 16-lane row, the rows of a wave through lane
+        // reads, then (rows wider than a wave) the per-wave sums in wave order
+        // through LDS
         constexpr int WL = LPR < 64 ? LPR : 64;
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-#pragma unroll
-            for (int m = WL / 2; m >= 1; m >>= 1) rowacc[t] += __shfl_xor(rowacc[t], m, WL);
-        }
+        for (int t = 0; t < T; ++t) rowacc[t] = lane_group_sum<WL>(rowacc[t]);
         if constexpr (LPR > 64) {
             constexpr int PARTS = LPR / 64;
-            __syncthreads();  // every wave is done reading the staged inputs
-            float* part = xs;  // [row in block][part][T]
+            __shared__ float part[WAVES * T];  // [row in block][part][T]
             const int rb = threadIdx.x / LPR, pw = q / 64;
             if ((q & 63) == 0) {
 #pragma unroll
@@ -374,15 +406,15 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
     }
 }
 
-template <int T>
+template <int T, int GC>
 constexpr size_t lds_bytes() {
-    return (size_t)T * (128 / T) * kSlot * sizeof(float);
+    return (size_t)T * GC * kSlot * sizeof(float);
 }
 
 // ---------------------------------------------------------------- kernels
 constexpr int kMaxTok = 16;  // token rows per launch chunk of the batch kernel
 
-template <int LPR, int WAVES, int T, bool BF16, bool VEC, int BITS>
+template <int LPR, int WAVES, int T, int GC, bool BF16, bool VEC, int BITS>
 __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
     int64_t G, const void* __restrict__ X, int64_t tok0, int ntok, float* __restrict__ Y) {
@@ -391,7 +423,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
     if (threadIdx.x < kMaxTok) rows[threadIdx.x] = (int32_t)(tok0 + threadIdx.x);
     __syncthreads();
     constexpr int RB = WAVES * 64 / LPR;
-    gemv_rows<LPR, WAVES, T, BF16, VEC, BITS>(packed, scales, O, I, G, X, rows, rows, ntok, Y,
+    gemv_rows<LPR, WAVES, T, GC, BF16, VEC, BITS>(packed, scales, O, I, G, X, rows, rows, ntok, Y,
                                               (int64_t)blockIdx.x * RB, lds);
 }
 
@@ -399,7 +431,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
 
 // Decode and small batches.  LPR/WAVES chosen so that O/RB blocks cover the
 // chip; tokens in tiles of T per pass over the weights.
-template <int LPR, int WAVES, int T, bool BF16, bool VEC, int BITS>
+template <int LPR, int WAVES, int T, int GC, bool BF16, bool VEC, int BITS>
 static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
                             const void* X, int64_t ntok, float* Y, hipStream_t s) {
     const int64_t G = (I + kGroup - 1) / kGroup;
@@ -407,8 +439,8 @@ static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t 
     const int64_t blocks = (O + RB - 1) / RB;
     for (int64_t t0 = 0; t0 < ntok; t0 += kMaxTok) {
         const int n = (int)std::min<int64_t>(kMaxTok, ntok - t0);
-        hipLaunchKernelGGL((gemv_batch_kernel<LPR, WAVES, T, BF16, VEC, BITS>),
-                           dim3((unsigned)blocks), dim3(WAVES * 64), lds_bytes<T>(), s, packed,
+        hipLaunchKernelGGL((gemv_batch_kernel<LPR, WAVES, T, GC, BF16, VEC, BITS>),
+                           dim3((unsigned)blocks), dim3(WAVES * 64), (lds_bytes<T, GC>()), s, packed,
                            scales, O, I, G, X, t0, n, Y);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -419,11 +451,11 @@ static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t 
 template <bool BF16, bool VEC, int BITS>
 static hipError_t batch_dispatch(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
                                  const void* X, int64_t ntok, float* Y, hipStream_t s) {
-    if (ntok == 1) return run_batch<64, 8, 1, BF16, VEC, BITS>(packed, scales, O, I, X, 1, Y, s);
-    if (ntok == 2) return run_batch<32, 4, 2, BF16, VEC, BITS>(packed, scales, O, I, X, 2, Y, s);
+    if (ntok == 1) return run_batch<128, 16, 1, 128, BF16, VEC, BITS>(packed, scales, O, I, X, 1, Y, s);
+    if (ntok == 2) return run_batch<128, 16, 2, 128, BF16, VEC, BITS>(packed, scales, O, I, X, 2, Y, s);
     if (ntok <= 4)
-        return run_batch<16, 4, 4, BF16, VEC, BITS>(packed, scales, O, I, X, ntok, Y, s);
-    return run_batch<16, 4, 8, BF16, VEC, BITS>(packed, scales, O, I, X, ntok, Y, s);
+        return run_batch<64, 8, 4, 128, BF16, VEC, BITS>(packed, scales, O, I, X, ntok, Y, s);
+    return run_batch<64, 8, 8, 64, BF16, VEC, BITS>(packed, scales, O, I, X, ntok, Y, s);
 }
 
 template <int BITS>

@@ -159,12 +159,24 @@ def _matmul_ref(po, so, O, I, X):
     return np.stack(ys), np.stack(zs)
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 9, 16, 17, 40])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 9, 16, 17, 40])
 def test_i4_matmul_f32(B):
     O, I = 70, 650
     so, po = _i4_packed_for(O, I, seed=B + 1)
     X = workloads.generic_matrix(B, I, seed=B + 2)
     say(f"int4 matmul f32 B={B}")
+    Y = host(qt.qt_matmul_i4(dev(po), dev(so), O, I, dev(X)))
+    yr, ar = _matmul_ref(po, so, O, I, X)
+    assert componentwise_err(Y, yr, ar) <= TOL_F32
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 6, 12])
+def test_i4_matmul_f32_several_chunks(B):
+    # 141 groups: more than one staged chunk of inputs for every tile width
+    O, I = 37, 9000
+    so, po = _i4_packed_for(O, I, seed=400 + B)
+    X = workloads.generic_matrix(B, I, seed=410 + B)
+    say(f"int4 matmul f32 chunks B={B}")
     Y = host(qt.qt_matmul_i4(dev(po), dev(so), O, I, dev(X)))
     yr, ar = _matmul_ref(po, so, O, I, X)
     assert componentwise_err(Y, yr, ar) <= TOL_F32

@@ -215,7 +215,7 @@ def _matmul_ref(po, so, O, I, X):
     return y.reshape(B, O), a.reshape(B, O)
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 9, 15, 16, 17, 40])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 9, 15, 16, 17, 40])
 def test_matmul_f32_exact_path(B):
     O, I = 70, 650
     so, po = _packed_for(O, I, seed=B)
@@ -226,7 +226,20 @@ def test_matmul_f32_exact_path(B):
     assert componentwise_err(Y, yr, ar) <= TOL_F32
 
 
-@pytest.mark.parametrize("B", [1, 7, 15])
+@pytest.mark.parametrize("B", [1, 2, 4, 6, 12])
+def test_matmul_f32_exact_path_several_chunks(B):
+    # 141 groups: more than one staged chunk of inputs for every tile width,
+    # 16-byte input rows, and a last block of rows that is only partly used
+    O, I = 37, 9000
+    so, po = _packed_for(O, I, seed=300 + B)
+    X = workloads.generic_matrix(B, I, seed=310 + B)
+    say(f"matmul f32 chunks B={B}")
+    Y = host(qt.qt_matmul_i3(dev(po), dev(so), O, I, dev(X)))
+    yr, ar = _matmul_ref(po, so, O, I, X)
+    assert componentwise_err(Y, yr, ar) <= TOL_F32
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 7, 15])
 def test_matmul_bf16_small_batch_exact_path(B):
     O, I = 50, 300
     so, po = _packed_for(O, I, seed=100 + B)
