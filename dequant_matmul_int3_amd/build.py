@@ -29,11 +29,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
-# The grouped matrix-core kernel scales every MFMA result on the vector ALUs:
+# The grouped matrix-core kernels scale every MFMA result on the vector ALUs:
 # ask the backend to keep MFMA results in VGPRs rather than AGPRs (saves one
-# copy per result).
+# copy per result).  The f64 tile products of the GPTQ factor fit two waves
+# per SIMD only in that form.
 EXTRA = {"grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "moe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "moe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "factor.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, verbose):

@@ -4,8 +4,8 @@
 // Cholesky on device later").
 //
 // With J the reversal, J A J = C C^T (C lower); then U = J C^-1 J is upper
-// with U^T U = A^-1.  Everything runs in f64 on the vector ALUs (gfx950's
-// f64 vector and matrix rates are the same), in 64-wide panels:
+// with U^T U = A^-1.  Everything runs in f64 (tile products on the f64 matrix
+// cores, the rest on the vector ALUs), in 64-wide panels:
 //   Cholesky, right-looking: factor the diagonal block in LDS, solve the
 //   panel below it row by row, subtract the panel's outer product from the
 //   trailing lower triangle (128 x 128 tiles);
@@ -22,7 +22,8 @@
 namespace qt {
 namespace {
 
-constexpr int kNB = 64;  // panel width
+constexpr int kNB = 64;      // panel width of the diagonal factorization
+constexpr int kOuter = 512;  // columns per rank-k trailing update
 
 // mean(diag H) * damp, summed in f64 in a fixed order by one block.
 __global__ __launch_bounds__(256) void damp_kernel(const float* __restrict__ H, int64_t n,
@@ -121,80 +122,128 @@ __global__ __launch_bounds__(64) void trsm_panel_kernel(double* __restrict__ B, 
 }
 
 // ---------------------------------------------------------------- f64 tiles
-// A TILE x TILE output tile of 256 threads (16 x 16, R x R values each),
-// K staged through LDS 16 at a time: acc[u][v] += sum_k P(R ty + u, k) Q(k,
-// R tx + v) for k in [kbeg, kend), P and Q given by loaders that return 0
-// outside their operand.  QT: Q's memory is [c][k] (k contiguous), so its
-// loads walk k like P's.
+// Tile products on the f64 matrix cores (v_mfma_f64_16x16x4_f64, the same
+// rate as the f64 vector ALUs but one LDS operand read per 16 products instead
+// of one per 4): a TILE x TILE output tile, 4 waves as 2 x 2 of (TILE/2)^2,
+// K staged through LDS kKC at a time as [row][k] with a 17-double pitch (the
+// operand reads of a half-wave and the staging stores hit distinct banks).
+// acc[m][n][r] of lane l is row (TILE/2) wm + 16 m + l/16 + 4 r, column
+// (TILE/2) wn + 16 n + l%16 of the tile (the instruction's result layout).
+// acc += sum_k P(row, k) Q(k, col) for k in [kbeg, kend); P and Q come from
+// loaders that return 0 outside their operand.  QT: Q's memory is [col][k]
+// (k contiguous), so its loads walk k like P's.
+typedef __attribute__((ext_vector_type(4))) double f64x4_t;
 constexpr int kKC = 16;
+constexpr int kKP = kKC + 1;
+
+template <int TILE>
+struct TileAcc {
+    static constexpr int MT = TILE / 32;  // 16 x 16 products per wave and dimension
+    f64x4_t v[MT][MT];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int n = 0; n < MT; ++n) v[m][n] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    }
+    // f(row, col, value) for every element this lane holds
+    template <typename F>
+    __device__ __forceinline__ void each(F f) const {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int rb = (TILE / 2) * (wave >> 1) + (lane >> 4), cb = (TILE / 2) * (wave & 1) + (lane & 15);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int n = 0; n < MT; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) f(rb + 16 * m + 4 * r, cb + 16 * n, v[m][n][r]);
+    }
+};
 
 template <int TILE, bool QT = false, typename LP, typename LQ>
 __device__ __forceinline__ void tile_product(int64_t kbeg, int64_t kend, LP ldp, LQ ldq,
-                                             double (&acc)[TILE / 16][TILE / 16],
-                                             double (*Ps)[TILE + 2], double (*Qs)[TILE + 2]) {
-    constexpr int R = TILE / 16;
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    for (int64_t k0 = kbeg; k0 < kend; k0 += kKC) {
-        __syncthreads();  // the previous stage is consumed
-        for (int p = tid; p < kKC * TILE; p += 256) {
-            {   // P(r, k): consecutive threads walk k (row-major operands)
+                                             TileAcc<TILE>& acc, double (*Ps)[kKP],
+                                             double (*Qs)[kKP]) {
+    constexpr int MT = TileAcc<TILE>::MT;
+    constexpr int NL = kKC * TILE / 256;  // staged values per thread and operand
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ra = (TILE / 2) * (wave >> 1) + (lane & 15), ca = (TILE / 2) * (wave & 1) + (lane & 15);
+    const int lq = lane >> 4;
+    // staging: P(r, k) with consecutive threads walking k (row-major
+    // operands), Q(k, c) walking c (or k when QT)
+    double pv[NL], qv[NL];
+    auto load = [&](int64_t k0) {
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const int p = tid + 256 * l;
+            {
                 const int kk = p % kKC, r = p / kKC;
                 const int64_t k = k0 + kk;
-                Ps[kk][r] = k < kend ? ldp(r, k) : 0.0;
+                pv[l] = k < kend ? ldp(r, k) : 0.0;
             }
-            {   // Q(k, c): consecutive threads walk c (or k when QT)
+            {
                 const int c = QT ? p / kKC : p % TILE, kk = QT ? p % kKC : p / TILE;
                 const int64_t k = k0 + kk;
-                Qs[kk][c] = k < kend ? ldq(k, c) : 0.0;
+                qv[l] = k < kend ? ldq(k, c) : 0.0;
             }
         }
+    };
+    if (kbeg < kend) load(kbeg);
+    for (int64_t k0 = kbeg; k0 < kend; k0 += kKC) {
+        __syncthreads();  // the previous stage is consumed
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const int p = tid + 256 * l;
+            Ps[p / kKC][p % kKC] = pv[l];
+            if (QT)
+                Qs[p / kKC][p % kKC] = qv[l];
+            else
+                Qs[p % TILE][p / TILE] = qv[l];
+        }
         __syncthreads();
-#pragma unroll 2
-        for (int kk = 0; kk < kKC; ++kk) {
-            double a[R], b[R];
+        if (k0 + kKC < kend) load(k0 + kKC);  // the next stage in flight
 #pragma unroll
-            for (int u = 0; u < R; ++u) {
-                a[u] = Ps[kk][R * ty + u];
-                b[u] = Qs[kk][R * tx + u];
-            }
+        for (int kk = 0; kk < kKC; kk += 4) {
+            double a[MT], b[MT];
 #pragma unroll
-            for (int u = 0; u < R; ++u)
+            for (int m = 0; m < MT; ++m) a[m] = Ps[ra + 16 * m][kk + lq];
 #pragma unroll
-                for (int v = 0; v < R; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
+            for (int n = 0; n < MT; ++n) b[n] = Qs[ca + 16 * n][kk + lq];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < MT; ++n)
+                    acc.v[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[m], b[n], acc.v[m][n], 0,
+                                                                       0, 0);
         }
     }
 }
 
-// Trailing update B[i][j] -= sum_c B[i][k0+c] B[j][k0+c] for k0+64 <= j <= i,
-// on 128 x 128 tiles of the lower triangle.
+// Trailing update B[i][j] -= sum_{kbeg <= c < kend} B[i][c] B[j][c] for
+// r0 <= j <= i < n and j < cend, on 128 x 128 tiles of the lower triangle
+// (tile (ti, tj) starts at row r0 + 128 ti, column r0 + 128 tj).
 __global__ __launch_bounds__(256) void syrk_update_kernel(double* __restrict__ B, int64_t n,
-                                                          int64_t k0) {
-    constexpr int TILE = 128, R = TILE / 16;
+                                                          int64_t kbeg, int64_t kend, int64_t r0,
+                                                          int64_t cend) {
+    constexpr int TILE = 128;
     const int ti = blockIdx.y, tj = blockIdx.x;
     if (tj > ti) return;  // lower tiles only; uniform over the block
-    __shared__ __attribute__((aligned(16))) double Ps[kKC][TILE + 2];
-    __shared__ __attribute__((aligned(16))) double Qs[kKC][TILE + 2];
-    const int64_t k1 = k0 + kNB;
-    const int64_t ri0 = k1 + (int64_t)ti * TILE, rj0 = k1 + (int64_t)tj * TILE;
+    __shared__ __attribute__((aligned(16))) double Ps[TILE][kKP];
+    __shared__ __attribute__((aligned(16))) double Qs[TILE][kKP];
+    const int64_t ri0 = r0 + (int64_t)ti * TILE, rj0 = r0 + (int64_t)tj * TILE;
     auto ldp = [&](int r, int64_t k) -> double {
         return ri0 + r < n ? B[(ri0 + r) * n + k] : 0.0;
     };
     auto ldq = [&](int64_t k, int c) -> double {  // Q(k, c) = L[rj0 + c][k]
-        return rj0 + c < n ? B[(rj0 + c) * n + k] : 0.0;
+        return rj0 + c < cend ? B[(rj0 + c) * n + k] : 0.0;
     };
-    double acc[R][R] = {};
-    tile_product<TILE, true>(k0, k0 + kNB, ldp, ldq, acc, Ps, Qs);
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int64_t i = ri0 + R * ty + u;
-        if (i >= n) continue;
-#pragma unroll
-        for (int v = 0; v < R; ++v) {
-            const int64_t j = rj0 + R * tx + v;
-            if (j <= i) B[i * n + j] -= acc[u][v];
-        }
-    }
+    TileAcc<TILE> acc;
+    acc.zero();
+    tile_product<TILE, true>(kbeg, kend, ldp, ldq, acc, Ps, Qs);
+    acc.each([&](int r, int c, double v) {
+        const int64_t i = ri0 + r, j = rj0 + c;
+        if (i < n && j <= i && j < cend) B[i * n + j] -= v;
+    });
 }
 
 // Inverse of every lower-triangular 64 x 64 diagonal block, in place
@@ -235,15 +284,15 @@ template <int TILE, int STEP>
 __global__ __launch_bounds__(256) void inv_level_kernel(double* __restrict__ B, int64_t n,
                                                         int64_t bs,
                                                         double* __restrict__ tmp) {
-    constexpr int R = TILE / 16;
-    __shared__ __attribute__((aligned(16))) double Ps[kKC][TILE + 2];
-    __shared__ __attribute__((aligned(16))) double Qs[kKC][TILE + 2];
+    __shared__ __attribute__((aligned(16))) double Ps[TILE][kKP];
+    __shared__ __attribute__((aligned(16))) double Qs[TILE][kKP];
     const int64_t a0 = 2 * bs * (int64_t)blockIdx.z, d0 = a0 + bs;
     const int64_t dD = std::min<int64_t>(bs, n - d0);  // > 0: the host launches only such pairs
     const int64_t r0 = (int64_t)blockIdx.y * TILE, c0 = (int64_t)blockIdx.x * TILE;
     if (r0 >= dD) return;  // uniform
     double* T = tmp + (int64_t)blockIdx.z * bs * bs;
-    double acc[R][R] = {};
+    TileAcc<TILE> acc;
+    acc.zero();
     if (STEP == 1) {
         auto ldp = [&](int r, int64_t k) -> double {  // Dinv[r0 + r][k], k <= r
             const int64_t rr = r0 + r;
@@ -263,20 +312,14 @@ __global__ __launch_bounds__(256) void inv_level_kernel(double* __restrict__ B, 
         };
         tile_product<TILE>(c0, bs, ldp, ldq, acc, Ps, Qs);
     }
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int64_t rr = r0 + R * ty + u;
-        if (rr >= dD) continue;
-#pragma unroll
-        for (int v = 0; v < R; ++v) {
-            const int64_t cc = c0 + R * tx + v;
-            if (STEP == 1)
-                T[rr * bs + cc] = acc[u][v];
-            else
-                B[(d0 + rr) * n + a0 + cc] = -acc[u][v];
-        }
-    }
+    acc.each([&](int r, int c, double v) {
+        const int64_t rr = r0 + r, cc = c0 + c;
+        if (rr >= dD) return;
+        if (STEP == 1)
+            T[rr * bs + cc] = v;
+        else
+            B[(d0 + rr) * n + a0 + cc] = -v;
+    });
 }
 
 // U[i][j] = Cinv[n-1-i][n-1-j] for j >= i, 0 below the diagonal.
@@ -317,16 +360,28 @@ hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, 
     hipLaunchKernelGGL(reverse_kernel, dim3(cols, rows), dim3(256), 0, s, H, n, add, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    for (int64_t k0 = 0; k0 < n; k0 += kNB) {
-        const int kb = (int)std::min<int64_t>(kNB, n - k0);
-        hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, B, n, k0, kb, info);
-        const int64_t rest = n - k0 - kb;
-        if (rest > 0) {  // kb == 64 here: only the last panel can be narrower
-            hipLaunchKernelGGL(trsm_panel_kernel, dim3((unsigned)((rest + 63) / 64)), dim3(64), 0,
-                               s, B, n, k0);
-            const unsigned mt = (unsigned)((rest + 127) / 128);
-            hipLaunchKernelGGL(syrk_update_kernel, dim3(mt, mt), dim3(256), 0, s, B, n, k0);
+    // Outer panels of kOuter columns, each factored in kNB-wide steps whose
+    // updates stay inside the panel; then one rank-kOuter update of
+    // everything right of and below it.
+    auto update = [&](int64_t kbeg, int64_t kend, int64_t r0, int64_t cend) {
+        const int64_t rows = n - r0, cols = cend - r0;
+        if (rows <= 0 || cols <= 0) return;
+        const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+        hipLaunchKernelGGL(syrk_update_kernel, grid, dim3(256), 0, s, B, n, kbeg, kend, r0, cend);
+    };
+    for (int64_t K0 = 0; K0 < n; K0 += kOuter) {
+        const int64_t K1 = std::min<int64_t>(K0 + kOuter, n);
+        for (int64_t k0 = K0; k0 < K1; k0 += kNB) {
+            const int kb = (int)std::min<int64_t>(kNB, n - k0);
+            hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, B, n, k0, kb, info);
+            const int64_t rest = n - k0 - kb;
+            if (rest > 0) {  // kb == 64 here: only the last panel can be narrower
+                hipLaunchKernelGGL(trsm_panel_kernel, dim3((unsigned)((rest + 63) / 64)),
+                                   dim3(64), 0, s, B, n, k0);
+                update(k0, k0 + kb, k0 + kb, K1);  // the rest of this outer panel
+            }
         }
+        update(K0, K1, K1, n);  // everything after it
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

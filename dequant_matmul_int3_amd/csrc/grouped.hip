@@ -26,9 +26,11 @@
 //
 // Tiling.  A block of 4 waves owns 64 consecutive output rows of one expert;
 // wave w multiplies rows [16w, 16w+16) as the A operand (16 rows x 32 inputs
-// per MFMA, lane l: row l%16, eight codes of quarter l/16 of the group).  The
-// B operand columns are (token t, piece p) = 3t+p for up to 5 tokens per pass
-// over the weights.  Weights, scales and inputs advance in chunks of 16
+// per MFMA, lane l: row l%16, eight codes of quarter l/16 of the group; for
+// int3 in the order 0 4 1 5 2 6 3 7 within each eight, which the table
+// unpacking produces without regrouping, and the inputs are staged in the same
+// order).  The B operand columns are (token t, piece p) = 3t+p for up to 5
+// tokens per pass over the weights.  Weights, scales and inputs advance in chunks of 16
 // groups: the next chunk is loaded into registers (16-byte loads of each
 // row's contiguous bytes) while the current one is multiplied out of LDS.
 #include "grouped_tile.h"

@@ -39,27 +39,27 @@ __device__ __forceinline__ void to_bf16_pairs(uint32_t W4, uint32_t& d0, uint32_
 }
 
 // One 16-code quarter: low-plane word L (code 4b+i at bits 8b+2i) and its 16
-// high bits h16 (code j at bit j) -> codes 0..7 and 8..15 as bf16x8 (natural
-// order).
+// high bits h16 (code j at bit j) -> bf16 codes in the k order the int3 tile
+// stages its inputs in: lo8 holds codes 0 4 1 5 2 6 3 7 and hi8 codes 8 12 9
+// 13 10 14 11 15 of the quarter.  A dot product does not depend on the order
+// of its terms' positions, only on both operands using the same one; this
+// order saves the four byte permutes that natural order needs.
 __device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t h16, u32x4_t& lo8,
-                                                u32x4_t& hi8) {
+                                                       u32x4_t& hi8) {
     uint32_t sp = (h16 | (h16 << 8)) & 0x00FF00FFu;
     sp = ((sp | (sp << 4)) & 0x0F0F0F0Fu) << 2;  // code 4b+i's high bit at bit 2+i of byte b
     const uint32_t u0 = (L & 0x03030303u) | (sp & 0x04040404u);
     const uint32_t u1 = ((L >> 2) & 0x03030303u) | ((sp >> 1) & 0x04040404u);
     const uint32_t u2 = ((L >> 4) & 0x03030303u) | ((sp >> 2) & 0x04040404u);
     const uint32_t u3 = ((L >> 6) & 0x03030303u) | ((sp >> 3) & 0x04040404u);
-    const uint32_t a0 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // codes 0 1 4 5
-    const uint32_t a1 = __builtin_amdgcn_perm(u1, u0, 0x07030602u);  // codes 8 9 12 13
-    const uint32_t b0 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);  // codes 2 3 6 7
-    const uint32_t b1 = __builtin_amdgcn_perm(u3, u2, 0x07030602u);  // codes 10 11 14 15
-    uint32_t p01, p45, p89, p1213, p23, p67, p1011, p1415;
-    to_bf16_pairs(a0, p01, p45);
-    to_bf16_pairs(a1, p89, p1213);
-    to_bf16_pairs(b0, p23, p67);
-    to_bf16_pairs(b1, p1011, p1415);
-    lo8 = u32x4_t{p01, p23, p45, p67};
-    hi8 = u32x4_t{p89, p1011, p1213, p1415};
+    // byte b of u_i is code 4b+i: pairs (i, 4+i) and (8+i, 12+i)
+    uint32_t p0, p1, p2, p3, q0, q1, q2, q3;
+    to_bf16_pairs(u0, p0, q0);
+    to_bf16_pairs(u1, p1, q1);
+    to_bf16_pairs(u2, p2, q2);
+    to_bf16_pairs(u3, p3, q3);
+    lo8 = u32x4_t{p0, p1, p2, p3};
+    hi8 = u32x4_t{q0, q1, q2, q3};
 }
 
 // v/16 of the two's-complement nibble in the low four bits of byte B of t.
@@ -256,6 +256,22 @@ __device__ __forceinline__ void grouped_tile(
                 float x[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) x[q] = k0 + q < I ? c.x[t][q] : 0.0f;
+                if constexpr (BITS == 3) {
+                    // aligned 8-input block = this thread's 4 and its
+                    // neighbour's; position 2i holds input i, 2i+1 input 4+i
+                    float pn[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        pn[q] = __int_as_float(__builtin_amdgcn_update_dpp(
+                            0, __float_as_int(x[q]), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+                    const bool odd = tid & 1;
+                    const float y0 = odd ? pn[2] : x[0], y1 = odd ? x[2] : pn[0];
+                    const float y2 = odd ? pn[3] : x[1], y3 = odd ? x[3] : pn[1];
+                    x[0] = y0;
+                    x[1] = y1;
+                    x[2] = y2;
+                    x[3] = y3;
+                }
                 uint32_t w[3][2];
                 split3(x, w);
 #pragma unroll
@@ -297,7 +313,9 @@ __device__ __forceinline__ void grouped_tile(
             if (c0 + kCG < G) load_chunk(c0 + kCG, nt, cur);
             const uint8_t* wrow = wl + (16 * wave + l16) * kWRow;
             const uint8_t* prow = pl + l16 * kPRow + 32 * j4;
-            for (int g = 0; g < gn; ++g) {
+#pragma unroll
+            for (int g = 0; g < kCG; ++g) {
+                if (g >= gn) break;  // uniform
                 u32x4_t a0, a1;
                 if constexpr (BITS == 3) {
                     const uint32_t lo =
