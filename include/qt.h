@@ -312,8 +312,8 @@ qt_status qt_gptq_factor(const float* H, int64_t I, double damp, float* U,
  * sequence stated above (a sweep with I <= 128 is bit-exact against it); the
  * propagation between blocks sums in f32, so codes near a rounding boundary
  * may differ from another implementation's.  workspace:
- * qt_gptq_workspace_bytes(O, I) bytes (the current weights and the block
- * errors, (O*I + 128*O) * 4).
+ * qt_gptq_workspace_bytes(O, I) bytes (the current weights and the scaled
+ * errors of four blocks, about (O*I + 512*O) * 4).
  */
 size_t qt_gptq_workspace_bytes(int64_t O, int64_t I);
 qt_status qt_gptq_i3(const float* W, int64_t O, int64_t I, const float* U,
