@@ -58,67 +58,123 @@ __global__ __launch_bounds__(256) void reverse_kernel(const float* __restrict__ 
     }
 }
 
-// Unblocked Cholesky of the kb x kb diagonal block at (k0, k0), in LDS.
-__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ B, int64_t n,
-                                                         int64_t k0, int kb,
-                                                         int32_t* __restrict__ info) {
-    __shared__ double T[kNB][kNB + 1];
-    const int tid = threadIdx.x;
-    for (int p = tid; p < kb * kb; p += 256) {
-        const int i = p / kb, j = p % kb;
-        T[i][j] = j <= i ? B[(k0 + i) * n + k0 + j] : 0.0;
+// Unblocked Cholesky of the kb x kb diagonal block at (k0, k0) by one wave:
+// lane i holds row i in registers (zeros above the diagonal); at column c
+// every lane reads the pivot from lane c, scales its entry, and the column
+// goes through LDS to every lane's update of the later columns.  Lanes update
+// their entries right of their own diagonal too (never stored; finite, since
+// a non-positive pivot is replaced by 1), so the loop has no lane branches.
+__global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ B, int64_t n,
+                                                        int64_t k0, int kb,
+                                                        int32_t* __restrict__ info) {
+    __shared__ double col[kNB];
+    const int i = threadIdx.x;
+    const double* row = B + (k0 + min(i, kb - 1)) * n + k0;
+    double x[kNB];
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) {
+        const double v = row[min(j, kb - 1)];  // inside the block
+        x[j] = (i < kb && j < kb && j <= i) ? v : 0.0;
     }
-    __syncthreads();
-    for (int c = 0; c < kb; ++c) {
-        if (tid == 0) {
-            double d = T[c][c];
-            if (!(d > 0.0)) {
-                if (*info == 0) *info = (int32_t)(k0 + c + 1);
-                d = 1.0;
-            }
-            T[c][c] = sqrt(d);
+    // columns past kb (the last, narrower block) are zero rows and columns:
+    // a unit pivot there changes nothing that is stored
+#pragma unroll
+    for (int c = 0; c < kNB; ++c) {
+        const int lo = __builtin_amdgcn_readlane((int)(__double_as_longlong(x[c]) & 0xFFFFFFFFll), c);
+        const int hi = __builtin_amdgcn_readlane((int)(__double_as_longlong(x[c]) >> 32), c);
+        double d = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+        if (c >= kb) {  // uniform
+            d = 1.0;
+        } else if (!(d > 0.0)) {  // uniform
+            if (i == 0 && *info == 0) *info = (int32_t)(k0 + c + 1);
+            d = 1.0;
         }
-        __syncthreads();
-        for (int i = c + 1 + tid; i < kb; i += 256) T[i][c] = T[i][c] / T[c][c];
-        __syncthreads();
-        const int m = kb - 1 - c;  // trailing size
-        for (int p = tid; p < m * m; p += 256) {
-            const int i = c + 1 + p / m, j = c + 1 + p % m;
-            if (j <= i) T[i][j] -= T[i][c] * T[j][c];
-        }
-        __syncthreads();
+        const double sc = sqrt(d);
+        x[c] = i == c ? sc : (i > c ? x[c] / sc : x[c]);
+        col[i] = x[c];
+        __syncthreads();  // one wave: orders the column's store before its reads
+#pragma unroll
+        for (int j = c + 1; j < kNB; ++j) x[j] -= x[c] * col[j];
+        // the updates happen in this column (left to the scheduler they sink
+        // to their use and keep every column value alive until then)
+#pragma unroll
+        for (int j = c + 1; j < kNB; ++j) asm volatile("" : "+v"(x[j]));
+        __syncthreads();  // the column is read before the next one is stored
     }
-    for (int p = tid; p < kb * kb; p += 256) {
-        const int i = p / kb, j = p % kb;
-        if (j <= i) B[(k0 + i) * n + k0 + j] = T[i][j];
+    if (i < kb) {
+        double* out = B + (k0 + i) * n + k0;
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+            if (j < kb && j <= i) out[j] = x[j];
     }
 }
 
-// Rows below the diagonal block: x C_kk^T = b, one thread per row (64 values
-// in registers, forward substitution over the columns).
+// DPP quad move of an f64 value (two 32-bit moves), CTRL a quad_perm: 0xB1
+// gives lane l the value of lane l ^ 1, 0x4E of lane l ^ 2, 0x55 * S of lane S.
+template <int CTRL>
+__device__ __forceinline__ double quad_dpp(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xFFFFFFFFll), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double quad_bcast(double v, int S) {  // S folds to a constant
+    switch (S) {
+        case 0: return quad_dpp<0x00>(v);
+        case 1: return quad_dpp<0x55>(v);
+        case 2: return quad_dpp<0xAA>(v);
+        default: return quad_dpp<0xFF>(v);
+    }
+}
+
+// Rows below the diagonal block: x C_kk^T = b by forward substitution over
+// the columns, four lanes per row (a DPP quad): lane t keeps the entries
+// 4k + t of the row (the right-hand side b, and the solution x, zero until
+// solved), sums its terms of each column, the quad adds its four partial
+// sums in a fixed order and every lane forms the column's x.  Terms at or
+// right of the column multiply the triangle's zeros or an unsolved zero, so
+// no lane branches.  The diagonal's reciprocals are formed once per block
+// (LDS holds -L below the diagonal, so the sums need no negation); 16 rows
+// per block.
 __global__ __launch_bounds__(64) void trsm_panel_kernel(double* __restrict__ B, int64_t n,
                                                         int64_t k0) {
     __shared__ double L[kNB][kNB + 1];
+    __shared__ double rdiag[kNB];
     for (int p = threadIdx.x; p < kNB * kNB; p += 64) {
         const int i = p / kNB, j = p % kNB;
-        L[i][j] = j <= i ? B[(k0 + i) * n + k0 + j] : 0.0;
+        const double v = B[(k0 + i) * n + k0 + j];
+        if (j < i) L[i][j] = -v;
+        else if (j == i) rdiag[i] = 1.0 / v;
+        if (j >= i) L[i][j] = 0.0;
     }
     __syncthreads();
-    const int64_t r = k0 + kNB + (int64_t)blockIdx.x * 64 + threadIdx.x;
-    if (r >= n) return;
-    double x[kNB];
-    double* row = B + r * n + k0;
+    constexpr int kQK = kNB / 4;
+    const int t = threadIdx.x & 3;
+    const int64_t r = k0 + kNB + (int64_t)blockIdx.x * 16 + (threadIdx.x >> 2);
+    const bool live = r < n;  // rows past n run on row n - 1 and store nothing
+    double* row = B + (live ? r : n - 1) * n + k0;
+    double bx[kQK], xs[kQK];
 #pragma unroll
-    for (int c = 0; c < kNB; ++c) x[c] = row[c];
-#pragma unroll
-    for (int c = 0; c < kNB; ++c) {
-        double s = x[c];
-#pragma unroll
-        for (int m = 0; m < c; ++m) s -= x[m] * L[c][m];
-        x[c] = s / L[c][c];
+    for (int k = 0; k < kQK; ++k) {
+        bx[k] = row[4 * k + t];
+        xs[k] = 0.0;
     }
 #pragma unroll
-    for (int c = 0; c < kNB; ++c) row[c] = x[c];
+    for (int c = 0; c < kNB; ++c) {
+        double part = 0.0;
+#pragma unroll
+        for (int k = 0; k <= c / 4; ++k) part = __builtin_fma(xs[k], L[c][4 * k + t], part);
+        // quad sum in a fixed order: (p0 + p1) + (p2 + p3) in every lane
+        part += quad_dpp<0xB1>(part);
+        part += quad_dpp<0x4E>(part);
+        const double xc = (quad_bcast(bx[c / 4], c % 4) + part) * rdiag[c];
+        xs[c / 4] = t == c % 4 ? xc : xs[c / 4];
+    }
+    if (live) {
+#pragma unroll
+        for (int k = 0; k < kQK; ++k) row[4 * k + t] = xs[k];
+    }
 }
 
 // ---------------------------------------------------------------- f64 tiles
@@ -373,10 +429,10 @@ hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, 
         const int64_t K1 = std::min<int64_t>(K0 + kOuter, n);
         for (int64_t k0 = K0; k0 < K1; k0 += kNB) {
             const int kb = (int)std::min<int64_t>(kNB, n - k0);
-            hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, B, n, k0, kb, info);
+            hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(64), 0, s, B, n, k0, kb, info);
             const int64_t rest = n - k0 - kb;
             if (rest > 0) {  // kb == 64 here: only the last panel can be narrower
-                hipLaunchKernelGGL(trsm_panel_kernel, dim3((unsigned)((rest + 63) / 64)),
+                hipLaunchKernelGGL(trsm_panel_kernel, dim3((unsigned)((rest + 15) / 16)),
                                    dim3(64), 0, s, B, n, k0);
                 update(k0, k0 + kb, k0 + kb, K1);  // the rest of this outer panel
             }
