@@ -30,13 +30,18 @@
 // int3 in the order 0 4 1 5 2 6 3 7 within each eight, which the table
 // unpacking produces without regrouping, and the inputs are staged in the same
 // order).  The B operand columns are (token t, piece p) = 3t+p for up to 5
-// tokens per pass over the weights.  Weights, scales and inputs advance in chunks of 16
-// groups: the next chunk is loaded into registers (16-byte loads of each
-// row's contiguous bytes) while the current one is multiplied out of LDS.
+// tokens per pass over the weights.  Weights, scales and inputs advance in
+// chunks of groups (8 here, 16 in the expert layer): the next chunk is loaded
+// into registers (16-byte loads of each row's contiguous bytes) while the
+// current one is multiplied out of LDS.
 #include "grouped_tile.h"
 
 namespace qt {
 namespace {
+
+// Eight groups per chunk: half the LDS and staging registers of sixteen, so
+// three blocks share a CU and hide each other's load latency.
+constexpr int kGroupedCG = 8;
 
 template <int BITS, bool W16, bool XV>
 __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
@@ -44,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void gemv_grouped_mfma_kernel(
     int32_t G, const float* __restrict__ X, int64_t n_x_rows,
     const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t P,
     float* __restrict__ Y) {
-    __shared__ TileLds<Geo<BITS>::kWRow> lds;
+    __shared__ TileLds<Geo<BITS, kGroupedCG>::kWRow, kGroupedCG> lds;
     grouped_tile<BITS, W16, XV>(lds, blockIdx.y, blockIdx.x, packed, scales, O, I, G, X, n_x_rows,
                                 pair_row, off, P, Y);
 }

@@ -13,18 +13,26 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kRows = 64;             // output rows per block
 constexpr int kThreads = 256;         // 4 waves
-constexpr int kCG = 16;               // groups per chunk
 constexpr int kTok = 5;               // tokens per pass (3 B columns each)
-constexpr int kPRow = kCG * kGroup * 2 + 16;   // LDS bytes per piece column
+
+// Chunk geometry: CG groups per chunk (8 or 16), LDS bytes per piece column,
+// scales staged per thread.
+template <int CG>
+struct Chunking {
+    static constexpr int kCG = CG;
+    static constexpr int kPRow = CG * kGroup * 2 + 16;
+    static constexpr int kSPer = kRows * CG / kThreads;
+    static_assert(CG == 8 || CG == 16, "8 or 16 groups per chunk");
+};
 
 // Weight staging geometry of a format: bytes per group, LDS bytes per weight
 // row (+16: conflict-free reads), 16-byte pieces per thread per chunk.
-template <int BITS>
+template <int BITS, int CG>
 struct Geo {
     static constexpr int kGB = BITS == 3 ? kGroupBytes : kGroupBytesI4;
-    static constexpr int kWRow = kCG * kGB + 16;
-    static constexpr int kWPieces = kRows * kCG * kGB / 16;  // 1536 or 2048
-    static constexpr int kWPer = kWPieces / kThreads;        // 6 or 8
+    static constexpr int kWRow = CG * kGB + 16;
+    static constexpr int kWPieces = kRows * CG * kGB / 16;  // 768..2048
+    static constexpr int kWPer = kWPieces / kThreads;       // 3..8
     static_assert(kWPieces % kThreads == 0, "weight chunk split");
 };
 
@@ -125,12 +133,12 @@ __device__ __forceinline__ float from_lane_plus(float a) {
 }
 
 // LDS of one tile; WROW: weight bytes per row (the larger format's for a
-// kernel that runs both).
-template <int WROW>
+// kernel that runs both), CG groups per chunk.
+template <int WROW, int CG>
 struct TileLds {
     __attribute__((aligned(16))) uint8_t wl[kRows * WROW];   // weight bytes
-    __attribute__((aligned(16))) float sl[kCG][kRows];       // scales [group][row]
-    __attribute__((aligned(16))) uint8_t pl[16 * kPRow];     // pieces [col][k]
+    __attribute__((aligned(16))) float sl[CG][kRows];        // scales [group][row]
+    __attribute__((aligned(16))) uint8_t pl[16 * Chunking<CG>::kPRow];  // pieces [col][k]
     int32_t trow[kTok];
     int32_t tout[kTok];
 };
@@ -142,16 +150,19 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // with G even); else 8-byte pieces.  XV: inputs allow 16-byte loads
 // (I % 4 == 0, X 16-byte aligned).  Starts with a barrier, so items can
 // follow one another in a block.
-template <int BITS, bool W16, bool XV, int WROW>
+template <int BITS, bool W16, bool XV, int WROW, int CG>
 __device__ __forceinline__ void grouped_tile(
-    TileLds<WROW>& L, int e, int64_t rb, const uint8_t* __restrict__ packed,
+    TileLds<WROW, CG>& L, int e, int64_t rb, const uint8_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t O, int32_t I, int32_t G,
     const float* __restrict__ X, int64_t n_x_rows,
     const int32_t* __restrict__ pair_row, const int32_t* __restrict__ off, int32_t P,
     float* __restrict__ Y) {
-    constexpr int kGB = Geo<BITS>::kGB;
-    constexpr int kWRow = Geo<BITS>::kWRow;
-    constexpr int kWPer = Geo<BITS>::kWPer;
+    constexpr int kGB = Geo<BITS, CG>::kGB;
+    constexpr int kWRow = Geo<BITS, CG>::kWRow;
+    constexpr int kWPer = Geo<BITS, CG>::kWPer;
+    constexpr int kCG = CG;
+    constexpr int kPRow = Chunking<CG>::kPRow;
+    constexpr int kSPer = Chunking<CG>::kSPer;
     static_assert(kWRow <= WROW, "tile LDS too small for the format");
     uint8_t* wl = L.wl;
     auto& sl = L.sl;
@@ -193,12 +204,13 @@ __device__ __forceinline__ void grouped_tile(
         wpart[i] = part;
     }
     // scales: 4 per thread, [row][16 groups] -> sl[group][row]
-    const int srow = tid >> 2, sg = (tid & 3) * 4;
+    const int srow = tid / (kCG / kSPer), sg = (tid % (kCG / kSPer)) * kSPer;
+    const bool xq = 4 * tid < kCG * kGroup;  // this thread stages 4 inputs
     const float* ssrc = sk + min<int64_t>(r0 + srow, O - 1) * G;
 
     struct Chunk {
         u32x4_t w[kWPer];
-        float s[4];
+        float s[kSPer];
         float x[kTok][4];
     };
     auto load_chunk = [&](int32_t c0, int nt, Chunk& c) {
@@ -222,7 +234,7 @@ __device__ __forceinline__ void grouped_tile(
             }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) c.s[q] = ssrc[min(c0 + sg + q, G - 1)];
+        for (int q = 0; q < kSPer; ++q) c.s[q] = ssrc[min(c0 + sg + q, G - 1)];
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
             if (t >= nt) break;  // uniform
@@ -248,11 +260,11 @@ __device__ __forceinline__ void grouped_tile(
         for (int i = 0; i < kWPer; ++i)
             *reinterpret_cast<u32x4_t*>(wl + wdst[i]) = c.w[i];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sl[sg + q][srow] = sg + q < gn ? c.s[q] : 0.0f;
+        for (int q = 0; q < kSPer; ++q) sl[sg + q][srow] = sg + q < gn ? c.s[q] : 0.0f;
         const int32_t k0 = c0 * kGroup + 4 * tid;
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            if (t < nt) {  // uniform; columns of absent tokens stay zero
+            if (t < nt && xq) {  // t < nt uniform; columns of absent tokens stay zero
                 float x[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) x[q] = k0 + q < I ? c.x[t][q] : 0.0f;

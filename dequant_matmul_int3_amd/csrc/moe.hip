@@ -166,8 +166,12 @@ __device__ void route(const MoeArgs& a, uint8_t* scratch /* >= 20 KB of LDS */) 
     }
 }
 
+// Sixteen groups per chunk: the layer's kernel holds two blocks per CU either
+// way (its registers), so fewer chunk barriers win.
+constexpr int kLayerCG = 16;
+
 template <int BITS, int WROW>
-__device__ __forceinline__ void tile_bits(TileLds<WROW>& L, int e, int64_t rb,
+__device__ __forceinline__ void tile_bits(TileLds<WROW, kLayerCG>& L, int e, int64_t rb,
                                           const uint8_t* packed, const float* scales, int64_t O,
                                           int32_t I, const float* X, int64_t nx,
                                           const int32_t* prow, const int32_t* offs, int32_t P,
@@ -179,8 +183,9 @@ __device__ __forceinline__ void tile_bits(TileLds<WROW>& L, int e, int64_t rb,
 // GB, UB, DB: the formats (3 or 4 bits) of gate, up and down.
 template <int GB, int UB, int DB>
 __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
-    constexpr int kW = (GB == 4 || UB == 4 || DB == 4) ? Geo<4>::kWRow : Geo<3>::kWRow;
-    __shared__ TileLds<kW> lds;
+    constexpr int kW = (GB == 4 || UB == 4 || DB == 4) ? Geo<4, kLayerCG>::kWRow
+                                                       : Geo<3, kLayerCG>::kWRow;
+    __shared__ TileLds<kW, kLayerCG> lds;
     static_assert(sizeof(lds.wl) >= 20 * 1024, "the routing borrows 20 KB of the weight LDS");
     cg::grid_group grid = cg::this_grid();
     const int P = a.T * a.k;
