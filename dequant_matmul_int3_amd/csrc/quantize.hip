@@ -39,123 +39,66 @@ __device__ __forceinline__ float code_of(float w, float s) {
     return fminf(fmaxf(q, Range<BITS>::kLo), Range<BITS>::kHi);
 }
 
-// One halving step of the slot errors: lane l (l < m) of a 16-lane row adds
-// the partial sum of lane l + m (row_shl:m moves lane l+m's value to lane l).
-template <int M>
-__device__ __forceinline__ float add_from_lane_plus(float a) {
-    const int v = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x100 + M, 0xF, 0xF, true);
-    return a + __builtin_bit_cast(float, v);
-}
-
-// Codes of a candidate without a division on the common path.  With r =
-// rcp(s) (v_rcp_f32: within 1 ulp of 1/s) and y = fl(w * r), y and the
-// correctly rounded fl(w/s) differ by at most 2^-22 * |w/s|.  The host's
-// per-candidate margin leaves twice that bound (for the largest |w/s| the
-// group can hold) between y and every half-integer, so wherever
-// |y - rint(y)| < margin, fl(w/s) rounds to the same integer as y.  Lanes
-// outside the margin, and groups whose scales leave [2^-100, 2^100], take the
-// correctly rounded division instead.
-template <bool WEIGHTED, int BITS>
-__device__ __forceinline__ float candidate_error(const float (&wv)[4], const float (&dv)[4],
-                                                 float s, float margin, bool s_ok) {
-    const float r = __builtin_amdgcn_rcpf(s);
-    float q[4];
-    bool near = false;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float y = wv[e] * r;
-        q[e] = __builtin_rintf(y);
-        near |= !(fabsf(y - q[e]) < margin);
-    }
-    if (near || !s_ok) {  // rare: decide with the division
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = s == 0.0f ? 0.0f : __builtin_rintf(wv[e] / s);
-    }
-    float e4[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float qc = __builtin_amdgcn_fmed3f(q[e], Range<BITS>::kLo, Range<BITS>::kHi);
-        const float t = s * qc;
-        const float rr = wv[e] - t;
-        const float r2 = rr * rr;
-        e4[e] = WEIGHTED ? dv[e] * r2 : r2;  // padding slots: rr = 0 (and dv = 0)
-    }
-    // m = 32: slots j and j+32 are e4[0] + e4[2] and e4[1] + e4[3];
-    // m = 16: slot l gets slot l+16.
-    const float a32_lo = e4[0] + e4[2];
-    const float a32_hi = e4[1] + e4[3];
-    float a = a32_lo + a32_hi;
-    // m = 8, 4, 2, 1: slot l (l < m) gets slot l + m, held by lane l + m
-    a = add_from_lane_plus<8>(a);
-    a = add_from_lane_plus<4>(a);
-    a = add_from_lane_plus<2>(a);
-    a = add_from_lane_plus<1>(a);
-    return a;
-}
-
-// Lane l of a quarter wave holds slots l, l+16, l+32, l+48 of its group, so
-// the first two halving steps (m = 32, 16) are lane-local and the remaining
-// four (m = 8, 4, 2, 1) read the partner lane l + m through DPP.
-template <bool WEIGHTED, int BITS>
-__global__ __launch_bounds__(kQuantBlock) void quantize_g64_kernel(
-    const float* __restrict__ W, int64_t n_groups, int32_t I, int32_t G,
-    const float* __restrict__ d, int32_t ncand, GridTable tab,
-    float* __restrict__ scales, int8_t* __restrict__ codes,
-    uint8_t* __restrict__ grid_idx) {
+// A single candidate (the plain group quantizer, s = base * f0): no
+// objective to evaluate, so the group's 16 lanes take 4 consecutive inputs
+// each (16-byte loads), share the absmax through DPP steps inside their
+// 16-lane row (the maximum does not depend on the order) and store their four
+// codes as one word.  VEC: W rows allow 16-byte loads and code rows 4-byte
+// stores (I % 4 == 0, W 16-byte and codes 4-byte aligned).
+template <int BITS, bool VEC>
+__global__ __launch_bounds__(kQuantBlock) void quantize_rtn_kernel(
+    const float* __restrict__ W, int64_t n_groups, int32_t I, int32_t G, float f0,
+    float* __restrict__ scales, int8_t* __restrict__ codes, uint8_t* __restrict__ grid_idx) {
     const int l = threadIdx.x & (kLanesPerGroup - 1);
     const int64_t grp = (int64_t)blockIdx.x * (kQuantBlock / kLanesPerGroup) +
                         (threadIdx.x / kLanesPerGroup);
-    // grp is uniform over the 16 lanes of a group (one DPP row), so a whole
-    // row leaves together and the cross-lane reads below see only live lanes
-    // of the same group.
-    if (grp >= n_groups) return;
+    if (grp >= n_groups) return;  // a whole 16-lane row leaves together
     const int64_t o = grp / G;
     const int32_t g = (int32_t)(grp - o * G);
     const int32_t c0 = g * kGroup;
     const int32_t n = min(kGroup, I - c0);
     const float* w = W + o * (int64_t)I + c0;
-
-    float wv[4], dv[4];
-    float amax = 0.0f;
+    float wv[4];
+    if (VEC && n == kGroup) {
+        const float4 v = *reinterpret_cast<const float4*>(w + 4 * l);
+        wv[0] = v.x;
+        wv[1] = v.y;
+        wv[2] = v.z;
+        wv[3] = v.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int j = l + 16 * e;
-        const bool ok = j < n;
-        wv[e] = ok ? w[j] : 0.0f;
-        dv[e] = ok && WEIGHTED ? d[c0 + j] : 0.0f;
-        amax = fmaxf(amax, fabsf(wv[e]));
-    }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kLanesPerGroup));
-    const float base = amax * Range<BITS>::kBase;
-    // base normal: then 2^(b-1) * base == amax exactly and every |w| <=
-    // 2^(b-1) * base; s = fl(base * f) is monotone in f, so the range check
-    // of the smallest and largest factor covers every candidate
-    const bool group_ok = base >= 0x1p-125f && base * tab.fmin >= 0x1p-100f &&
-                          base * tab.fmax <= 0x1p100f;
-
-    float best_e = 0.0f;
-    int best_k = 0;
-#pragma unroll 2
-    for (int k = 0; k < ncand; ++k) {
-        const float s = base * tab.f[k];
-        const float a = candidate_error<WEIGHTED, BITS>(wv, dv, s, tab.margin[k], group_ok);
-        if (k == 0 || a < best_e) {  // strict: the lowest k wins ties
-            best_e = a;
-            best_k = k;
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * l + e;
+            wv[e] = j < n ? w[j] : 0.0f;
         }
     }
-    // lane 0 of the quarter wave holds the halving sum and the choice
-    best_k = __shfl(best_k, 0, kLanesPerGroup);
-    const float s = base * tab.f[best_k];
+    float amax = fmaxf(fmaxf(fabsf(wv[0]), fabsf(wv[1])), fmaxf(fabsf(wv[2]), fabsf(wv[3])));
+    // quad_perm [1,0,3,2], [2,3,0,1], then row_ror 4 and 8: every lane of the
+    // row ends with the row's maximum
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1,
+                                                                  0xF, 0xF, false)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E,
+                                                                  0xF, 0xF, false)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x124,
+                                                                  0xF, 0xF, false)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x128,
+                                                                  0xF, 0xF, false)));
+    const float s = amax * Range<BITS>::kBase * f0;
+    uint32_t word = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int j = l + 16 * e;
-        if (j < n) codes[o * (int64_t)I + c0 + j] = (int8_t)(int)code_of<BITS>(wv[e], s);
+    for (int e = 0; e < 4; ++e)
+        word |= ((uint32_t)(int)code_of<BITS>(wv[e], s) & 0xFFu) << (8 * e);
+    int8_t* cd = codes + o * (int64_t)I + c0 + 4 * l;
+    if (VEC && n == kGroup) {
+        *reinterpret_cast<uint32_t*>(cd) = word;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * l + e < n) cd[e] = (int8_t)(word >> (8 * e));
     }
     if (l == 0) {
         scales[grp] = s;
-        if (grid_idx) grid_idx[grp] = (uint8_t)best_k;
+        if (grid_idx) grid_idx[grp] = 0;
     }
 }
 
@@ -173,7 +116,13 @@ enum QuotientMode { kReciprocal, kDivision };
 // Halving sum of the 64 slot errors of one candidate with scale s.  In
 // kReciprocal mode the codes come from y = fl(w * r), r = rcp(s), and *dev
 // receives the largest |y - rint(y)| for the exactness check; kDivision uses
-// the correctly rounded quotient (0 when s == 0).
+// the correctly rounded quotient (0 when s == 0).  Why the check suffices:
+// r = v_rcp_f32(s) is within 1 ulp of 1/s, so y and the correctly rounded
+// fl(w/s) differ by at most 2^-22 |w/s|; the per-candidate margin leaves
+// twice that bound (for the largest |w/s| the group can hold) between y and
+// every half-integer, so wherever |y - rint(y)| < margin, fl(w/s) rounds to
+// the same integer as y.  Groups outside the margin, or whose scales leave
+// [2^-100, 2^100], are decided with the division.
 template <bool WEIGHTED, int MODE, int BITS>
 __device__ __forceinline__ float group_error(const float (&w)[kGroup], const float (&dj)[kGroup],
                                              float s, float r, float* dev) {
@@ -510,15 +459,20 @@ hipError_t quantize_bits(const float* W, int64_t O, int64_t I, const float* d, i
     const int64_t n_groups = O * G;
     const int64_t per_block = kQuantBlock / kLanesPerGroup;
     const int64_t blocks = (n_groups + per_block - 1) / per_block;
-    if (d)
-        hipLaunchKernelGGL((quantize_g64_kernel<true, BITS>), dim3((unsigned)blocks),
-                           dim3(kQuantBlock), 0, s, W, n_groups, (int32_t)I, (int32_t)G, d, ncand,
-                           tab, scales, codes, grid_idx);
-    else
-        hipLaunchKernelGGL((quantize_g64_kernel<false, BITS>), dim3((unsigned)blocks),
-                           dim3(kQuantBlock), 0, s, W, n_groups, (int32_t)I, (int32_t)G, d, ncand,
-                           tab, scales, codes, grid_idx);
-    return hipGetLastError();
+    if (ncand == 1) {  // the plain quantizer: d does not change the choice
+        const bool vec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(codes) & 3) == 0);
+        if (vec)
+            hipLaunchKernelGGL((quantize_rtn_kernel<BITS, true>), dim3((unsigned)blocks),
+                               dim3(kQuantBlock), 0, s, W, n_groups, (int32_t)I, (int32_t)G,
+                               tab.f[0], scales, codes, grid_idx);
+        else
+            hipLaunchKernelGGL((quantize_rtn_kernel<BITS, false>), dim3((unsigned)blocks),
+                               dim3(kQuantBlock), 0, s, W, n_groups, (int32_t)I, (int32_t)G,
+                               tab.f[0], scales, codes, grid_idx);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;  // ncand >= 1
 }
 
 }  // namespace
