@@ -163,6 +163,10 @@ __device__ __forceinline__ void grouped_tile(
     constexpr int kCG = CG;
     constexpr int kPRow = Chunking<CG>::kPRow;
     constexpr int kSPer = Chunking<CG>::kSPer;
+    // Weights are read once: non-temporal loads keep them out of the caches,
+    // but only where a row's chunk is whole 128-byte lines; otherwise the line
+    // that two consecutive chunks share would be fetched twice.
+    constexpr bool kStream = (kCG * kGB) % 128 == 0;
     static_assert(kWRow <= WROW, "tile LDS too small for the format");
     uint8_t* wl = L.wl;
     auto& sl = L.sl;
@@ -223,13 +227,16 @@ __device__ __forceinline__ void grouped_tile(
             const uint8_t* rc = wrow0[i] + (int64_t)c0 * kGB;
             if constexpr (W16) {
                 const uint8_t* src = b0 < gn * kGB ? rc + b0 : wrow0[i];
-                c.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+                const u32x4_t* sp = reinterpret_cast<const u32x4_t*>(src);
+                c.w[i] = kStream ? __builtin_nontemporal_load(sp) : *sp;
             } else {
                 static_assert(BITS == 3, "int4 groups are always 16-byte aligned");
                 const uint8_t* sa = b0 < gn * kGB ? rc + b0 : wrow0[i];
                 const uint8_t* sb = b0 + 8 < gn * kGB ? rc + b0 + 8 : wrow0[i];
-                const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sa));
-                const u32x2_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sb));
+                const u32x2_t* pa = reinterpret_cast<const u32x2_t*>(sa);
+                const u32x2_t* pb = reinterpret_cast<const u32x2_t*>(sb);
+                const u32x2_t a = kStream ? __builtin_nontemporal_load(pa) : *pa;
+                const u32x2_t b = kStream ? __builtin_nontemporal_load(pb) : *pb;
                 c.w[i] = u32x4_t{a.x, a.y, b.x, b.y};
             }
         }
