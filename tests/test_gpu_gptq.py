@@ -70,6 +70,23 @@ def test_gptq_factor(I, damp):
     assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
 
 
+@pytest.mark.parametrize("I", [1100, 1089])
+def test_gptq_factor_several_outer_panels(I):
+    # more than two 512-column outer panels (rank-512 trailing updates, the
+    # in-panel rank-64 updates, a narrower last 64-column step)
+    X = correlated_x(2 * I, I, I + 5)
+    H = (X.astype(np.float64).T @ X.astype(np.float64)).astype(np.float32)
+    say(f"gptq_factor outer panels I={I}")
+    Ud, info = qt.qt_gptq_factor(dev(H), 0.01)
+    U, info = host(Ud), host(info)
+    assert info[0] == 0
+    Uref = oracle.gptq_factor(H.astype(np.float64), 0.01)
+    err = np.abs(U.astype(np.float64) - Uref).max() / np.abs(Uref).max()
+    say(f"  max err / max |U| {err:.3e}")
+    assert err <= 1e-6
+    assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
+
+
 def test_gptq_factor_reports_an_indefinite_matrix():
     # [[1, 2], [2, 1]] reversed is itself: the first pivot is 1, the second
     # 1 - 2*2/1 = -3, so the factorization fails at column 2
@@ -110,7 +127,7 @@ def _replay_valid(W, U, s, c, tol=1e-3):
     assert np.all(y[cf == 3] >= 2.5 - tol) and np.all(y[cf == -4] <= -3.5 + tol)
 
 
-@pytest.mark.parametrize("O,I", [(64, 256), (40, 333), (100, 1000), (3, 129)])
+@pytest.mark.parametrize("O,I", [(64, 256), (40, 333), (100, 1000), (3, 129), (70, 1300)])
 def test_gptq_sweep_follows_the_algorithm(O, I):
     H, U = _factor32(I, 21 + I)
     W = workloads.generic_weights(O, I, seed=3 * I)
