@@ -207,7 +207,7 @@ __device__ __forceinline__ void grouped_tile(
         wdst[i] = row * kWRow + 16 * part;
         wpart[i] = part;
     }
-    // scales: 4 per thread, [row][16 groups] -> sl[group][row]
+    // scales: kSPer per thread, [row][CG groups] -> sl[group][row]
     const int srow = tid / (kCG / kSPer), sg = (tid % (kCG / kSPer)) * kSPer;
     const bool xq = 4 * tid < kCG * kGroup;  // this thread stages 4 inputs
     const float* ssrc = sk + min<int64_t>(r0 + srow, O - 1) * G;
