@@ -8,14 +8,16 @@
 // block of the grid is resident; no block leaves before the last barrier):
 //  0. block 0 routes: per token the k largest logits (equal logits: lower
 //     expert first), combine weights a softmax over them; the (expert,
-//     token) pairs sorted by expert, then token.
+//     token) pairs sorted by expert, then token; the expert work order.
 //  1. items (expert, 64-row block of gate and up): the grouped matrix-core
 //     tile for gate, then for up, then h = silu(g) * u for those rows of
 //     every pair of the expert.
 //  2. items (expert, 64-row block of down): the same tile on h.
 //  3. out[t] = sum_j w_tj y_{pair(t, j)} in j order.
-// Items are dealt round-robin over the blocks; experts without pairs cost a
-// read of two offsets.
+// Blocks take the items of a phase from a shared counter as they finish, in
+// the routing's expert order (the most pairs first, so the longest items
+// start early); experts without pairs have no items.  Each item writes its
+// own outputs, so the results do not depend on which block ran it.
 #include <hip/hip_cooperative_groups.h>
 
 #include "grouped_tile.h"
@@ -47,6 +49,8 @@ struct MoeArgs {
     int32_t* slot;   // [T k] pair index of (t, j)
     int32_t* prow;   // [P] token of pair p
     int32_t* offs;   // [E + 1]
+    int32_t* order;  // [E] experts with pairs, most pairs first (ties: lower index)
+    int32_t* ctr;    // [4] next gate/up item, next down item, experts with pairs
     float* Yg;       // [P x F]
     float* Yu;       // [P x F]
     float* H;        // [P x F] silu(g) * u
@@ -164,14 +168,51 @@ __device__ void route(const MoeArgs& a, uint8_t* scratch /* >= 20 KB of LDS */) 
         a.prow[pos] = t;
         a.slot[q] = pos;
     }
+    // the work order of the expert phases: experts with pairs, the most
+    // first (their items take longest), ties by index; the work counters
+    // start at zero
+    int* cnt = part;  // [E] pair counts (the scan is done with part)
+    for (int e = tid; e < E; e += kThreads) cnt[e] = a.offs[e + 1] - a.offs[e];
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads) {
+        const int c = cnt[e];
+        if (c > 0) {
+            int rank = 0;
+            for (int e2 = 0; e2 < E; ++e2) {
+                const int c2 = cnt[e2];
+                rank += (c2 > c) || (c2 == c && e2 < e);
+            }
+            a.order[rank] = e;
+        }
+    }
+    if (tid == 0) {
+        int ne = 0;
+        for (int e = 0; e < E; ++e) ne += cnt[e] > 0;
+        a.ctr[0] = 0;
+        a.ctr[1] = 0;
+        a.ctr[2] = ne;
+    }
+}
+
+// The next item of a phase for this block, from the phase's shared counter
+// (blocks take items as they finish, so uneven items leave no long tail).
+__device__ __forceinline__ int64_t next_item(int32_t* ctr) {
+    __shared__ int32_t s_item;
+    if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
+    __syncthreads();
+    const int64_t it = s_item;
+    __syncthreads();  // everyone has read it before the next call overwrites it
+    return it;
 }
 
 // Sixteen groups per chunk: the layer's kernel holds two blocks per CU either
-// way (its registers), so fewer chunk barriers win.
+// way (its registers), so fewer chunk barriers win (eight-group chunks for
+// the down tiles, a second tile instantiation in the kernel, raised its
+// registers to one block per CU for some formats).
 constexpr int kLayerCG = 16;
 
-template <int BITS, int WROW>
-__device__ __forceinline__ void tile_bits(TileLds<WROW, kLayerCG>& L, int e, int64_t rb,
+template <int BITS, int WROW, int CG>
+__device__ __forceinline__ void tile_bits(TileLds<WROW, CG>& L, int e, int64_t rb,
                                           const uint8_t* packed, const float* scales, int64_t O,
                                           int32_t I, const float* X, int64_t nx,
                                           const int32_t* prow, const int32_t* offs, int32_t P,
@@ -194,9 +235,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     grid.sync();
 
     const int64_t nf = (a.F + kRows - 1) / kRows, nd = (a.D + kRows - 1) / kRows;
-    const int64_t items1 = a.E * nf;
-    for (int64_t it = blockIdx.x; it < items1; it += gridDim.x) {
-        const int e = (int)(it / nf);
+    const int64_t ne = a.ctr[2];
+    const int64_t items1 = ne * nf;
+    for (;;) {
+        const int64_t it = next_item(&a.ctr[0]);
+        if (it >= items1) break;  // uniform
+        const int e = a.order[it / nf];
         const int64_t rb = it % nf;
         tile_bits<GB>(lds, e, rb, a.gp, a.gs, a.F, a.D, a.X, a.T, a.prow, a.offs, P, a.Yg);
         tile_bits<UB>(lds, e, rb, a.up, a.us, a.F, a.D, a.X, a.T, a.prow, a.offs, P, a.Yu);
@@ -212,9 +256,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     }
     grid.sync();
 
-    const int64_t items2 = a.E * nd;
-    for (int64_t it = blockIdx.x; it < items2; it += gridDim.x) {
-        const int e = (int)(it / nd);
+    const int64_t items2 = ne * nd;
+    for (;;) {
+        const int64_t it = next_item(&a.ctr[1]);
+        if (it >= items2) break;  // uniform
+        const int e = a.order[it / nd];
         const int64_t rb = it % nd;
         tile_bits<DB>(lds, e, rb, a.dp, a.ds, a.D, a.F, a.H, P, nullptr, a.offs, P, a.Yd);
     }
@@ -236,7 +282,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 size_t moe_layer_workspace(int64_t T, int64_t k, int64_t E, int64_t D, int64_t F) {
     const int64_t P = T * k;
     auto up16 = [](int64_t b) { return (b + 15) / 16 * 16; };
-    return (size_t)(4 * up16(P * 4) + up16((E + 1) * 4) + up16(3 * P * F * 4) + up16(P * D * 4));
+    return (size_t)(4 * up16(P * 4) + up16((E + 1) * 4) + up16(E * 4) + up16(4 * 4) +
+                    up16(3 * P * F * 4) + up16(P * D * 4));
 }
 
 hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
@@ -276,6 +323,10 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
     w += up16(P * 4);
     a.offs = reinterpret_cast<int32_t*>(w);
     w += up16((E + 1) * 4);
+    a.order = reinterpret_cast<int32_t*>(w);
+    w += up16(E * 4);
+    a.ctr = reinterpret_cast<int32_t*>(w);
+    w += up16(4 * 4);
     a.Yg = reinterpret_cast<float*>(w);
     a.Yu = a.Yg + P * F;
     a.H = a.Yu + P * F;
