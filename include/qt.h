@@ -351,8 +351,9 @@ qt_status qt_gptq_proxy(const float* W, const uint8_t* packed, const float* scal
  *   (bits 3: 24-byte int3-g64 groups, 4: 32-byte grouped int4) with scales
  *   [E][rows x cols/64]; out [T x D] f32 (16-byte aligned).
  *   D and F multiples of 128; 1 <= k <= min(32, E); E <= 512.
- *   workspace: qt_moe_layer_workspace_bytes(T, k, E, D, F) bytes (routing
- *   tables and the f32 products, (T k)(2F + D) * 4 plus small tables).
+ *   workspace: qt_moe_layer_workspace_bytes(T, k, E, D, F) bytes (the f32
+ *   products g, u, h and the down outputs, (T k)(3F + D) * 4, plus small
+ *   tables: routing, expert work order, work counters).
  * The launch keeps every block of its grid resident until its last barrier;
  * results are deterministic.
  */
