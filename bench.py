@@ -319,7 +319,7 @@ def moe_layer_leg(torch, qt, workloads, dev, legs):
         legs[name] = {"ms": round(ms, 4), "experts_hit": hit, "bits": [gb, ub, db],
                       "GB_s": round(mb / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
                       "frac": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                      "bytes_per_step": int(mb), "launches": 1}
+                      "bytes_per_step": int(mb), "launches": 2}
         log(f"leg {name}: {legs[name]}")
     del store, out, ws
 

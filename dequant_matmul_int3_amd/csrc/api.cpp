@@ -363,8 +363,7 @@ qt_status qt_moe_layer(const float* X, int64_t T, int64_t D, int64_t F, const fl
         return QT_ERR_NULL;
     if (T < 1 || D < 128 || F < 128 || D % 128 || F % 128 || D > QT_MAX_I || F > QT_MAX_I)
         return QT_ERR_SHAPE;
-    if (E < 1 || E > 512 || k < 1 || k > 32 || k > E) return QT_ERR_SHAPE;
-    if (T * k > 0x7fffffffLL) return QT_ERR_SHAPE;
+    if (E < 1 || E > 512 || k < 1 || k > 32 || k > E || T > (1 << 22)) return QT_ERR_SHAPE;
     const int32_t bits[3] = {gate_bits, up_bits, down_bits};
     for (int b : bits)
         if (b != 3 && b != 4) return QT_ERR_ARG;

@@ -1,23 +1,29 @@
-// A mixture-of-experts expert layer in one persistent launch: routing, the
-// gate and up projections, SwiGLU, the down projection and the combine of
-// every token's experts (the pull request page's MoE decode setting: every
-// routed expert's weights read once per step; its per-projection ablation
-// names gate_proj, up_proj and down_proj, each at int3-g64 or grouped int4).
+// A mixture-of-experts expert layer in two launches: a one-block routing
+// kernel, then a persistent kernel for the gate and up projections, SwiGLU,
+// the down projection and the combine of every token's experts (the pull
+// request page's MoE decode setting: every routed expert's weights read once
+// per step; its per-projection ablation names gate_proj, up_proj and
+// down_proj, each at int3-g64 or grouped int4).
 //
-// Phases, separated by grid-wide barriers (a cooperative launch, so every
-// block of the grid is resident; no block leaves before the last barrier):
-//  0. block 0 routes: per token the k largest logits (equal logits: lower
-//     expert first), combine weights a softmax over them; the (expert,
-//     token) pairs sorted by expert, then token; the expert work order.
+//  0. routing (its own launch, one block): per token the k largest logits
+//     (equal logits: lower expert first), combine weights a softmax over
+//     them; the (expert, token) pairs sorted by expert, then token; the
+//     expert work order; the phase counters of the layer kernel zeroed.
+// Then phases separated by grid-wide barriers (a cooperative launch, so
+// every block of the grid is resident; no block leaves before the last
+// barrier):
 //  1. items (expert, 64-row block of gate and up): the grouped matrix-core
 //     tile for gate, then for up, then h = silu(g) * u for those rows of
 //     every pair of the expert.
 //  2. items (expert, 64-row block of down): the same tile on h.
 //  3. out[t] = sum_j w_tj y_{pair(t, j)} in j order.
-// Blocks take the items of a phase from a shared counter as they finish, in
-// the routing's expert order (the most pairs first, so the longest items
-// start early); experts without pairs have no items.  Each item writes its
-// own outputs, so the results do not depend on which block ran it.
+// A block's first item of a phase is its block index; later ones come from
+// the phase's shared counter as blocks finish, in the routing's expert order
+// (the most pairs first, so the longest items start early); experts without
+// pairs have no items.  Each item writes its own outputs, so the results do
+// not depend on which block ran it.  (Routing inside the persistent kernel
+// cost a grid barrier that every block reached at once, which measured
+// tens of microseconds.)
 #include <hip/hip_cooperative_groups.h>
 
 #include "grouped_tile.h"
@@ -28,8 +34,7 @@ namespace {
 namespace cg = cooperative_groups;
 
 constexpr int kMaxTopK = 32;
-constexpr int kMaxExperts = 512;  // routing keeps a token's logits in registers (32 per lane)
-constexpr int kRouteLdsPairs = (20 * 1024 - 16 * 32 * 4 - 2 * 256 * 4) / 4;  // selections in LDS
+constexpr int kMaxExperts = 512;  // routing keeps a token's keys in registers (32 per lane)
 
 struct MoeArgs {
     const float* X;  // [T x D]
@@ -57,140 +62,188 @@ struct MoeArgs {
     float* Yd;       // [P x D]
 };
 
-// Phase 0, one block: a wave per token picks its k experts one at a time
-// (each pick the largest logit after the previous one in the order
-// (-logit, expert): the lanes scan the logits, a butterfly keeps the larger,
-// on equal logits the lower expert); then counts per expert (order-free
-// atomics), offsets, and each pair's slot = its expert's offset + the number
-// of earlier tokens that chose the same expert.
+// Phase 0, one block of NT threads: 16 lanes per token, NT / 16 tokens per
+// pass (NT falls as the experts per lane, and so the registers, grow).  Each pick is the largest key below the previous pick
+// (keys order (logit, expert): larger logit first, then lower expert), a
+// lane's maximum over its experts, then over the 16 lanes.  Each pair's
+// slot is its expert's offset plus the number of earlier tokens that chose
+// that expert: per pass a bit per (expert, token of the pass) in LDS, the
+// bits below a token counted, plus the expert's total over earlier passes
+// (a token picks an expert at most once, so this is deterministic).
+constexpr int kRouteMaxTokens = 64;  // tokens per pass at most: two mask words per expert
+constexpr int kRouteLdsPairs = 4096;  // packed pairs kept in LDS up to this
+
 // value of lane (l - N) mod 16 of this lane's 16-lane row
 template <int N>
 __device__ __forceinline__ int row_ror(int v) {
     return __builtin_amdgcn_mov_dpp(v, 0x120 + N, 0xF, 0xF, false);
 }
 
-__device__ void route(const MoeArgs& a, uint8_t* scratch /* >= 20 KB of LDS */) {
+// Routing keys: a total order on (logit, expert) as one 64-bit integer,
+// larger logit first, then lower expert index: the logit's bits made
+// monotone (-0 folded to +0 first, so equal logits compare equal) above
+// 0xFFFF - e.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+    const uint32_t u = __float_as_uint(v + 0.0f);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)(0xFFFF - e);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) {
+    return 0xFFFF - (int)(key & 0xFFFFu);
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+    const uint32_t o = (uint32_t)(key >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x > y ? x : y; }
+template <int N>
+__device__ __forceinline__ uint64_t ror_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)row_ror<N>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)row_ror<N>((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// M: experts per lane of a token's 16-lane row (E <= 16 M); NT threads.
+template <int M, int NT>
+__global__ __launch_bounds__(NT) void moe_route_kernel(MoeArgs a) {
+    constexpr int kTok = NT / 16;          // tokens per pass
+    constexpr int kMW = (kTok + 31) / 32;  // mask words per expert
+    static_assert(kTok <= kRouteMaxTokens && kTok % 16 == 0, "tokens per pass");
+    __shared__ int csel[kTok * kMaxTopK];    // this pass's picks
+    __shared__ float cval[kTok * kMaxTopK];  // and their logits
+    __shared__ uint32_t mask[kMaxExperts * kMW];     // bit (e, token of the pass)
+    __shared__ int cnt[kMaxExperts];                 // pairs per expert so far (0 past E)
+    __shared__ int loffs[kMaxExperts + 1];
+    __shared__ int lpk[kRouteLdsPairs];              // packed pairs if they fit
+    __shared__ int s_ne;
     const int tid = threadIdx.x;
-    const int sub = tid & 15;              // lane within the token's 16-lane row
-    const int row = tid >> 4;              // 16 tokens in flight per block
-    const int E = a.E, k = a.k, Pn = a.T * a.k;
-    float* svals = reinterpret_cast<float*>(scratch);           // [16][kMaxTopK]
-    int* part = reinterpret_cast<int*>(scratch + 16 * kMaxTopK * 4);  // [2][kThreads] scan
-    int* lsel = part + 2 * kThreads;                             // [Pn] if it fits
-    const bool sel_in_lds = Pn <= kRouteLdsPairs;
-    for (int e = tid; e <= E; e += kThreads) a.offs[e] = 0;
-    for (int t0 = 0; t0 < a.T; t0 += kThreads / 16) {
-        const int t = t0 + row;
-        const bool live = t < a.T;  // uniform over the 16-lane row
-        const float* L = a.logits + (int64_t)(live ? t : 0) * E;
-        float lv[kMaxExperts / 16];  // logits sub + 16 m, read once
+    const int sub = tid & 15;  // lane within the token's 16-lane row
+    const int row = tid >> 4;  // token of the pass
+    const int E = a.E, k = a.k, T = a.T, Pn = T * k;
+    const int E4 = (E + 3) / 4 * 4;
+    int* pk = Pn <= kRouteLdsPairs ? lpk : a.sel;  // rank << 9 | expert of pair (t, j)
+    for (int e = tid; e < E4; e += NT) cnt[e] = 0;
+    // this pass's logits (rows past T read row T - 1, experts past E read
+    // expert E - 1; both are masked below), the next pass's issued before
+    // this pass's picks
+    float v[M];
+    {
+        const float* L = a.logits + (int64_t)min(row, T - 1) * E;
 #pragma unroll
-        for (int m = 0; m < kMaxExperts / 16; ++m) {
-            const int e = sub + 16 * m;
-            lv[m] = e < E ? L[e] : 0.0f;
-        }
-        float pv = 0.0f;
-        int pi = -1;
-        for (int j = 0; j < k; ++j) {
-            float bv = 0.0f;
-            int bi = -1;
-#pragma unroll
-            for (int m = 0; m < kMaxExperts / 16; ++m) {
-                const int e = sub + 16 * m;
-                const float v = lv[m];
-                const bool after = pi < 0 || v < pv || (v == pv && e > pi);
-                if (e < E && after && (bi < 0 || v > bv)) {  // ascending e: ties keep the lower
-                    bv = v;
-                    bi = e;
-                }
-            }
-            // all 16 lanes of the row end with the row's best (rotations by
-            // 8, 4, 2, 1 combine every lane's candidate)
-#define QT_ROUTE_STEP(N)                                                              \
-    {                                                                                 \
-        const float ov = __int_as_float(row_ror<N>(__float_as_int(bv)));              \
-        const int oi = row_ror<N>(bi);                                                \
-        if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {                 \
-            bv = ov;                                                                  \
-            bi = oi;                                                                  \
-        }                                                                             \
+        for (int m = 0; m < M; ++m) v[m] = L[min(sub + 16 * m, E - 1)];
     }
-            QT_ROUTE_STEP(8)
-            QT_ROUTE_STEP(4)
-            QT_ROUTE_STEP(2)
-            QT_ROUTE_STEP(1)
-#undef QT_ROUTE_STEP
-            pv = bv;
-            pi = bi;
-            if (live && sub == 0) {
-                a.sel[t * k + j] = bi;
-                if (sel_in_lds) lsel[t * k + j] = bi;
-                svals[row * kMaxTopK + j] = bv;
+    for (int t0 = 0; t0 < T; t0 += kTok) {
+        const int t = t0 + row;
+        const bool live = t < T;  // uniform over the 16-lane row
+        uint64_t key[M];  // 0 past E: below every real key
+#pragma unroll
+        for (int m = 0; m < M; ++m) key[m] = sub + 16 * m < E ? route_key(v[m], sub + 16 * m) : 0ull;
+        if (t0 + kTok < T) {
+            const float* L = a.logits + (int64_t)min(t + kTok, T - 1) * E;
+#pragma unroll
+            for (int m = 0; m < M; ++m) v[m] = L[min(sub + 16 * m, E - 1)];
+        }
+        for (int w = tid; w < kMW * E; w += NT) mask[w] = 0;
+        uint64_t prev = ~0ull;
+        for (int j = 0; j < k; ++j) {
+            // the largest key below the previous pick, over the lane, then
+            // over the 16-lane row (rotations by 8, 4, 2, 1: every lane
+            // ends with the row's maximum)
+            uint64_t best = 0;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint64_t c = key[m] < prev ? key[m] : 0ull;
+                best = c > best ? c : best;
+            }
+            best = max_u64(best, ror_u64<8>(best));
+            best = max_u64(best, ror_u64<4>(best));
+            best = max_u64(best, ror_u64<2>(best));
+            best = max_u64(best, ror_u64<1>(best));
+            prev = best;
+            if (sub == 0) {
+                csel[row * kMaxTopK + j] = key_expert(best);
+                cval[row * kMaxTopK + j] = key_logit(best);
             }
         }
         if (live && sub == 0) {  // combine weights: softmax over the k picks
-            const float* sv = svals + row * kMaxTopK;
+            const float* sv = cval + row * kMaxTopK;
             float sum = 0.0f;
             for (int j = 0; j < k; ++j) sum += expf(sv[j] - sv[0]);
             for (int j = 0; j < k; ++j) a.wgt[t * k + j] = expf(sv[j] - sv[0]) / sum;
         }
-    }
-    __syncthreads();
-    const int* sel = sel_in_lds ? lsel : a.sel;
-    for (int q = tid; q < Pn; q += kThreads) atomicAdd(&a.offs[sel[q] + 1], 1);
-    __syncthreads();
-    // offsets: each thread totals a contiguous run of experts, the totals
-    // are scanned in LDS (log steps), then each run is rewritten from its base
-    const int run = (E + kThreads - 1) / kThreads;
-    const int e0 = tid * run, e1 = min(E, e0 + run);
-    int tot = 0;
-    for (int e = e0; e < e1; ++e) tot += a.offs[e + 1];
-    part[tid] = tot;
-    __syncthreads();
-    int cur = 0;
-    for (int d = 1; d < kThreads; d <<= 1) {
-        const int v = part[cur * kThreads + tid] + (tid >= d ? part[cur * kThreads + tid - d] : 0);
-        part[(cur ^ 1) * kThreads + tid] = v;
-        cur ^= 1;
+        __syncthreads();
+        const int np = min(kTok, T - t0) * k;  // pairs of this pass
+        for (int q = tid; q < np; q += NT) {
+            const int r = q / k, e = csel[r * kMaxTopK + q % k];
+            atomicOr(&mask[kMW * e + (r >> 5)], 1u << (r & 31));
+        }
+        __syncthreads();
+        for (int q = tid; q < np; q += NT) {
+            const int r = q / k, e = csel[r * kMaxTopK + q % k];
+            const uint32_t* me = mask + kMW * e;
+            int below = __popc(me[r >> 5] & ((1u << (r & 31)) - 1u));
+            if (kMW == 2 && r >= 32) below += __popc(me[0]);
+            pk[t0 * k + q] = ((cnt[e] + below) << 9) | e;
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += NT) {
+            int c = __popc(mask[kMW * e]);
+            if (kMW == 2) c += __popc(mask[kMW * e + 1]);
+            cnt[e] += c;
+        }
         __syncthreads();
     }
-    int base = tid > 0 ? part[cur * kThreads + tid - 1] : 0;
-    for (int e = e0; e < e1; ++e) {
-        base += a.offs[e + 1];
-        a.offs[e + 1] = base;
+    // offsets: one wave scans the counts (a lane sums a run of up to 8
+    // experts, the lanes' totals are scanned across the wave)
+    if (tid < 64) {
+        const int run = (E + 63) / 64;
+        const int e0 = tid * run, e1 = min(E, e0 + run);
+        int tot = 0;
+        for (int e = e0; e < e1; ++e) tot += cnt[e];
+        int inc = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(inc, d, 64);
+            if (tid >= d) inc += y;
+        }
+        int base = inc - tot;
+        for (int e = e0; e < e1; ++e) {
+            loffs[e] = base;
+            base += cnt[e];
+        }
+        if (tid == 63) loffs[E] = inc;
+        if (tid == 0) s_ne = 0;
     }
     __syncthreads();
-    for (int q = tid; q < Pn; q += kThreads) {
-        const int e = sel[q], t = q / k;
-        int rank = 0;
-        for (int q2 = 0; q2 < t * k; ++q2) rank += sel[q2] == e;  // a token picks e at most once
-        const int pos = a.offs[e] + rank;
-        a.prow[pos] = t;
+    for (int e = tid; e <= E; e += NT) a.offs[e] = loffs[e];
+    for (int q = tid; q < Pn; q += NT) {
+        const int pv = pk[q];
+        const int pos = loffs[pv & 511] + (pv >> 9);
+        a.prow[pos] = q / k;
         a.slot[q] = pos;
     }
     // the work order of the expert phases: experts with pairs, the most
-    // first (their items take longest), ties by index; the work counters
-    // start at zero
-    int* cnt = part;  // [E] pair counts (the scan is done with part)
-    for (int e = tid; e < E; e += kThreads) cnt[e] = a.offs[e + 1] - a.offs[e];
-    __syncthreads();
-    for (int e = tid; e < E; e += kThreads) {
+    // first (their items take longest), ties by index
+    for (int e = tid; e < E; e += NT) {
         const int c = cnt[e];
         if (c > 0) {
             int rank = 0;
-            for (int e2 = 0; e2 < E; ++e2) {
-                const int c2 = cnt[e2];
-                rank += (c2 > c) || (c2 == c && e2 < e);
+            for (int e2 = 0; e2 < E4; e2 += 4) {  // four counts per LDS read
+                const int4 c4 = *reinterpret_cast<const int4*>(cnt + e2);
+                rank += (c4.x > c) || (c4.x == c && e2 < e);
+                rank += (c4.y > c) || (c4.y == c && e2 + 1 < e);
+                rank += (c4.z > c) || (c4.z == c && e2 + 2 < e);
+                rank += (c4.w > c) || (c4.w == c && e2 + 3 < e);
             }
             a.order[rank] = e;
+            atomicAdd(&s_ne, 1);
         }
     }
-    if (tid == 0) {
-        int ne = 0;
-        for (int e = 0; e < E; ++e) ne += cnt[e] > 0;
+    __syncthreads();
+    if (tid == 0) {  // the layer kernel's phase counters
         a.ctr[0] = 0;
         a.ctr[1] = 0;
-        a.ctr[2] = ne;
+        a.ctr[2] = s_ne;
     }
 }
 
@@ -227,18 +280,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     constexpr int kW = (GB == 4 || UB == 4 || DB == 4) ? Geo<4, kLayerCG>::kWRow
                                                        : Geo<3, kLayerCG>::kWRow;
     __shared__ TileLds<kW, kLayerCG> lds;
-    static_assert(sizeof(lds.wl) >= 20 * 1024, "the routing borrows 20 KB of the weight LDS");
     cg::grid_group grid = cg::this_grid();
     const int P = a.T * a.k;
-    // the routing borrows the tile's weight LDS (no tile has run yet)
-    if (blockIdx.x == 0) route(a, lds.wl);
-    grid.sync();
 
     const int64_t nf = (a.F + kRows - 1) / kRows, nd = (a.D + kRows - 1) / kRows;
     const int64_t ne = a.ctr[2];
     const int64_t items1 = ne * nf;
-    for (;;) {
-        const int64_t it = next_item(&a.ctr[0]);
+    for (int64_t it = blockIdx.x;; it = gridDim.x + next_item(&a.ctr[0])) {
         if (it >= items1) break;  // uniform
         const int e = a.order[it / nf];
         const int64_t rb = it % nf;
@@ -257,8 +305,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     grid.sync();
 
     const int64_t items2 = ne * nd;
-    for (;;) {
-        const int64_t it = next_item(&a.ctr[1]);
+    for (int64_t it = blockIdx.x;; it = gridDim.x + next_item(&a.ctr[1])) {
         if (it >= items2) break;  // uniform
         const int e = a.order[it / nd];
         const int64_t rb = it % nd;
@@ -291,7 +338,7 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
                             const float* gs, int gbits, const uint8_t* up, const float* us,
                             int ubits, const uint8_t* dp, const float* ds, int dbits, float* out,
                             void* workspace, hipStream_t s) {
-    if (k > kMaxTopK || E > kMaxExperts) return hipErrorInvalidValue;
+    if (k > kMaxTopK || E > kMaxExperts || T > (1 << 22)) return hipErrorInvalidValue;
     const int64_t P = T * k;
     auto up16 = [](int64_t b) { return (b + 15) / 16 * 16; };
     uint8_t* w = static_cast<uint8_t*>(workspace);
@@ -352,6 +399,14 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernels[code], kThreads, 0);
     if (e != hipSuccess) return e;
     if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+    if (E <= 128)
+        moe_route_kernel<8, 1024><<<1, 1024, 0, s>>>(a);
+    else if (E <= 256)
+        moe_route_kernel<16, 512><<<1, 512, 0, s>>>(a);
+    else
+        moe_route_kernel<32, 256><<<1, 256, 0, s>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     void* args[] = {&a};
     return hipLaunchCooperativeKernel(kernels[code], dim3((unsigned)(per_cu * cus)), dim3(kThreads),
                                       args, 0, s);

@@ -69,7 +69,7 @@ hipError_t launch_gptq_proxy(const float* W, const uint8_t* packed, const float*
                              int64_t O, int64_t I, const float* H, double* terms,
                              void* workspace, hipStream_t s);
 
-// MoE expert layer (moe.hip): one cooperative launch.
+// MoE expert layer (moe.hip): a one-block routing launch, then one cooperative launch.
 size_t moe_layer_workspace(int64_t T, int64_t k, int64_t E, int64_t D, int64_t F);
 hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
                             const float* logits, int32_t E, int32_t k, const uint8_t* gp,

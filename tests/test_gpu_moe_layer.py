@@ -1,6 +1,7 @@
-"""The MoE expert layer (one cooperative launch: routing, gate/up, SwiGLU,
-down, combine) against the oracle's f64 layer: every output within 1e-5 of
-the error budget the oracle derives from the grouped multiply's tolerance."""
+"""The MoE expert layer (a routing launch, then one cooperative launch for
+gate/up, SwiGLU, down, combine) against the oracle's f64 layer: every output
+within 1e-5 of the error budget the oracle derives from the grouped
+multiply's tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -67,6 +68,23 @@ def test_moe_layer_shapes(E, F, D, T, k):
     X = workloads.generic_matrix(T, D, seed=T)
     logits = workloads.rng_for("generic", 901, T, E).random((T, E)).astype(np.float32)
     out1 = check(X, logits, k, gate, up, down, "shape")
+    out2 = run_gpu(X, logits, k, gate, up, down)
+    assert np.array_equal(fbits(out1), fbits(out2)), "not deterministic"
+
+
+@pytest.mark.parametrize("E,T,k", [(200, 70, 3),    # 17-32 experts per 16 lanes, 32 tokens a pass
+                                   (300, 40, 2),    # 33-64 experts per 16 lanes, 16 tokens a pass
+                                   (512, 17, 32),   # the largest E and k
+                                   (8, 700, 8),     # 5600 pairs: the pair table past its LDS size
+                                   (128, 129, 8)])  # two passes of 64 tokens and one token more
+def test_moe_layer_routing_sizes(E, T, k):
+    # every routing variant over several passes of tokens; ranks of a token
+    # among the earlier tokens of its expert cross pass boundaries
+    F, D = 128, 128
+    gate, up, down = experts(E, F, D, E + T, (3, 3, 3))
+    X = workloads.generic_matrix(T, D, seed=T + 1)
+    logits = workloads.rng_for("generic", 902, T, E).random((T, E)).astype(np.float32)
+    out1 = check(X, logits, k, gate, up, down, "routing sizes")
     out2 = run_gpu(X, logits, k, gate, up, down)
     assert np.array_equal(fbits(out1), fbits(out2)), "not deterministic"
 
