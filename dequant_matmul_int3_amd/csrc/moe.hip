@@ -247,16 +247,26 @@ __global__ __launch_bounds__(NT) void moe_route_kernel(MoeArgs a) {
     }
 }
 
-// The next item of a phase for this block, from the phase's shared counter
-// (blocks take items as they finish, so uneven items leave no long tail).
-__device__ __forceinline__ int64_t next_item(int32_t* ctr) {
-    __shared__ int32_t s_item;
-    if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
-    __syncthreads();
-    const int64_t it = s_item;
-    __syncthreads();  // everyone has read it before the next call overwrites it
-    return it;
-}
+// Work items of a phase come from the phase's shared counter as blocks
+// finish (uneven items leave no long tail).  The counter is read one step
+// ahead: ask() issues the atomic in thread 0 and keeps the result in a
+// register, take() hands it to the block, so the atomic's latency overlaps
+// the work issued in between.
+struct ItemCounter {
+    int32_t* ctr;
+    int32_t pending;  // thread 0 only
+    __device__ __forceinline__ void ask() {
+        if (threadIdx.x == 0) pending = atomicAdd(ctr, 1);
+    }
+    __device__ __forceinline__ int64_t take() {
+        __shared__ int32_t s_item;
+        if (threadIdx.x == 0) s_item = pending;
+        __syncthreads();
+        const int64_t it = s_item;
+        __syncthreads();  // everyone has read it before the next take()
+        return it;
+    }
+};
 
 // Sixteen groups per chunk: the layer's kernel holds two blocks per CU either
 // way (its registers), so fewer chunk barriers win (eight-group chunks for
@@ -274,42 +284,66 @@ __device__ __forceinline__ void tile_bits(TileLds<WROW, CG>& L, int e, int64_t r
     grouped_tile<BITS, true, true>(L, e, rb, packed, scales, O, I, G, X, nx, prow, offs, P, Y);
 }
 
+// Routing tables the items look up, copied to LDS at the start (a global
+// read each time put its latency on every item's critical path): the expert
+// order, the offsets and, up to this many pairs, the pairs' token rows.
+constexpr int kLayerLdsPairs = 1024;
+
 // GB, UB, DB: the formats (3 or 4 bits) of gate, up and down.
 template <int GB, int UB, int DB>
-__global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void moe_layer_kernel(MoeArgs a) {
     constexpr int kW = (GB == 4 || UB == 4 || DB == 4) ? Geo<4, kLayerCG>::kWRow
                                                        : Geo<3, kLayerCG>::kWRow;
     __shared__ TileLds<kW, kLayerCG> lds;
+    __shared__ int32_t s_order[kMaxExperts];
+    __shared__ int32_t s_offs[kMaxExperts + 1];
+    __shared__ int32_t s_prow[kLayerLdsPairs];
     cg::grid_group grid = cg::this_grid();
     const int P = a.T * a.k;
+    const int tid = threadIdx.x;
 
     const int64_t nf = (a.F + kRows - 1) / kRows, nd = (a.D + kRows - 1) / kRows;
     const int64_t ne = a.ctr[2];
+    ItemCounter c1{&a.ctr[0], 0};
+    for (int i = tid; i < ne; i += kThreads) s_order[i] = a.order[i];
+    for (int i = tid; i <= a.E; i += kThreads) s_offs[i] = a.offs[i];
+    const bool prow_lds = P <= kLayerLdsPairs;
+    if (prow_lds)
+        for (int i = tid; i < P; i += kThreads) s_prow[i] = a.prow[i];
+    const int32_t* prow = prow_lds ? s_prow : a.prow;
+    __syncthreads();
+
     const int64_t items1 = ne * nf;
-    for (int64_t it = blockIdx.x;; it = gridDim.x + next_item(&a.ctr[0])) {
-        if (it >= items1) break;  // uniform
-        const int e = a.order[it / nf];
+    for (int64_t it = blockIdx.x; it < items1;) {
+        const int e = s_order[it / nf];
         const int64_t rb = it % nf;
-        tile_bits<GB>(lds, e, rb, a.gp, a.gs, a.F, a.D, a.X, a.T, a.prow, a.offs, P, a.Yg);
-        tile_bits<UB>(lds, e, rb, a.up, a.us, a.F, a.D, a.X, a.T, a.prow, a.offs, P, a.Yu);
+        tile_bits<GB>(lds, e, rb, a.gp, a.gs, a.F, a.D, a.X, a.T, prow, s_offs, P, a.Yg);
+        tile_bits<UB>(lds, e, rb, a.up, a.us, a.F, a.D, a.X, a.T, prow, s_offs, P, a.Yu);
         // h for this block's rows of every pair of the expert (the tiles'
-        // stores above come from this block: a barrier makes them visible)
-        const int p0 = a.offs[e], p1 = a.offs[e + 1];
+        // stores above come from this block: a barrier makes them visible);
+        // the next item is asked for first (items here are long: asking
+        // earlier could leave a block holding one while others idle); every
+        // answer is taken below, so no item is skipped
+        c1.ask();
+        const int p0 = s_offs[e], p1 = s_offs[e + 1];
         __syncthreads();
         const int64_t r0 = rb * kRows;
-        for (int q = threadIdx.x; q < (p1 - p0) * kRows; q += kThreads) {
+        for (int q = tid; q < (p1 - p0) * kRows; q += kThreads) {
             const int64_t p = p0 + q / kRows, r = r0 + q % kRows;
             if (r < a.F) a.H[p * a.F + r] = silu(a.Yg[p * a.F + r]) * a.Yu[p * a.F + r];
         }
+        it = gridDim.x + c1.take();
     }
     grid.sync();
 
     const int64_t items2 = ne * nd;
-    for (int64_t it = blockIdx.x;; it = gridDim.x + next_item(&a.ctr[1])) {
-        if (it >= items2) break;  // uniform
-        const int e = a.order[it / nd];
+    ItemCounter c2{&a.ctr[1], 0};
+    for (int64_t it = blockIdx.x; it < items2;) {
+        c2.ask();  // short items: the next one is asked for as this one starts (taken below)
+        const int e = s_order[it / nd];
         const int64_t rb = it % nd;
-        tile_bits<DB>(lds, e, rb, a.dp, a.ds, a.D, a.F, a.H, P, nullptr, a.offs, P, a.Yd);
+        tile_bits<DB>(lds, e, rb, a.dp, a.ds, a.D, a.F, a.H, P, nullptr, s_offs, P, a.Yd);
+        it = gridDim.x + c2.take();
     }
     grid.sync();
 
