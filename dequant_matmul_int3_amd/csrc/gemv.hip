@@ -212,12 +212,12 @@ struct InputStage {
     uint4 raw_[T][QPT];  // loaded bits (f32, or bf16 pairs in x, y)
     bool ok_[T][QPT];
 
-    __device__ __forceinline__ void load(const void* __restrict__ X, const int32_t* rows, int nt,
+    __device__ __forceinline__ void load(const void* __restrict__ X, int64_t row0, int nt,
                                          int64_t I, int64_t g0, int gn) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int64_t row = rows[t < nt ? t : 0];
+            const int64_t row = row0 + (t < nt ? t : 0);
 #pragma unroll
             for (int j = 0; j < QPT; ++j) {
                 const int qd = tid + j * NTHR;
@@ -318,14 +318,12 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     }
 }
 
-// Rows [r0, r0+RB) of one matrix against the tokens listed in tok_rows
-// (input row of each token) / tok_outs (output row of each token, -1 = do not
-// store), T tokens per pass over the weights.
+// Rows [r0, r0+RB) of one matrix against tokens tok0 .. tok0+ntok-1 (the
+// input and output rows), T tokens per pass over the weights.
 template <int LPR, int WAVES, int T, int GC, bool BF16, bool VEC, int BITS>
 __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __restrict__ scales,
                           int64_t O, int64_t I, int64_t G, const void* __restrict__ X,
-                          const int32_t* tok_rows, const int32_t* tok_outs, int ntok,
-                          float* __restrict__ Y, int64_t r0, float* lds) {
+                          int64_t tok0, int ntok, float* __restrict__ Y, int64_t r0, float* lds) {
     constexpr int NTHR = WAVES * 64;
     constexpr int NG = (GC + LPR - 1) / LPR;  // groups per lane per chunk
     static_assert(GC >= LPR, "each lane needs at least one group per chunk");
@@ -345,9 +343,13 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
             const int gn = (int)min<int64_t>(GC, G - g0);
             if (tt > 0 || g0 > 0) __syncthreads();  // earlier readers are done with LDS
             InputStage<T, GC, NTHR, BF16, VEC> stage;
-            stage.load(X, tok_rows + tt, nt, I, g0, gn);
+            stage.load(X, tok0 + tt, nt, I, g0, gn);
             // weight loads, branch-free: idle lanes load group 0 of the block's
-            // first row (always valid) and are not used
+            // first row (always valid) and are not used.  The compiler issues
+            // them after the staging barrier below (their uses sit in the
+            // branch after it); issuing them before it, so that they were in
+            // flight during the staging, measured slower: 5.3 against 4.75 us
+            // per decode launch.
             GroupBits<BITS> gb[NG];
             float sc[NG];
 #pragma unroll
@@ -400,8 +402,7 @@ __device__ void gemv_rows(const uint8_t* __restrict__ packed, const float* __res
         if (row_ok && q == 0) {
 #pragma unroll
             for (int t = 0; t < T; ++t)
-                if (t < nt && tok_outs[tt + t] >= 0)
-                    Y[(int64_t)tok_outs[tt + t] * O + r] = rowacc[t];
+                if (t < nt) Y[(tok0 + tt + t) * O + r] = rowacc[t];
         }
     }
 }
@@ -419,11 +420,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_batch_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int64_t I,
     int64_t G, const void* __restrict__ X, int64_t tok0, int ntok, float* __restrict__ Y) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
-    __shared__ int32_t rows[kMaxTok];
-    if (threadIdx.x < kMaxTok) rows[threadIdx.x] = (int32_t)(tok0 + threadIdx.x);
-    __syncthreads();
     constexpr int RB = WAVES * 64 / LPR;
-    gemv_rows<LPR, WAVES, T, GC, BF16, VEC, BITS>(packed, scales, O, I, G, X, rows, rows, ntok, Y,
+    gemv_rows<LPR, WAVES, T, GC, BF16, VEC, BITS>(packed, scales, O, I, G, X, tok0, ntok, Y,
                                               (int64_t)blockIdx.x * RB, lds);
 }
 
