@@ -15,6 +15,7 @@
 //   buffer; the triangular factors' zero halves are skipped).
 // A non-positive pivot sets *info to its 1-based column (of the reversed
 // matrix) and is replaced by 1 so that every later step stays finite.
+#include <mutex>
 #include <algorithm>
 
 #include "qt_internal.h"
@@ -58,54 +59,78 @@ __global__ __launch_bounds__(256) void reverse_kernel(const float* __restrict__ 
     }
 }
 
-// Unblocked Cholesky of the kb x kb diagonal block at (k0, k0) by one wave:
-// lane i holds row i in registers (zeros above the diagonal); at column c
-// every lane reads the pivot from lane c, scales its entry, and the column
-// goes through LDS to every lane's update of the later columns.  Lanes update
-// their entries right of their own diagonal too (never stored; finite, since
-// a non-positive pivot is replaced by 1), so the loop has no lane branches.
-__global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ B, int64_t n,
-                                                        int64_t k0, int kb,
-                                                        int32_t* __restrict__ info) {
-    __shared__ double col[kNB];
-    const int i = threadIdx.x;
+// Cholesky of one kNB x kNB diagonal block in place (lower triangle), four
+// waves: lane i holds row i, wave w its columns 16w .. 16w+15 (zeros above
+// the diagonal).  Blocked by 16-column panels: the panel's wave factors it
+// alone (each pivot and column entry read from its lane with readlane),
+// writes it to LDS, and after a barrier the waves right of it subtract the
+// panel's rank-16 product from their columns; every entry's updates still
+// run over the columns in order.  Columns past kb (the last, narrower block)
+// are zero rows and columns: a unit pivot there changes nothing that is
+// stored, and so does a non-positive pivot, which also sets *info.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), lane);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ B, int64_t n,
+                                                         int64_t k0, int kb,
+                                                         int32_t* __restrict__ info) {
+    constexpr int kPW = 16;  // panel width: one wave's columns
+    __shared__ double pan[kNB][kPW + 1];
+    const int i = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int j0 = kPW * w;
     const double* row = B + (k0 + min(i, kb - 1)) * n + k0;
-    double x[kNB];
+    double x[kPW];
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) {
+    for (int jl = 0; jl < kPW; ++jl) {
+        const int j = j0 + jl;
         const double v = row[min(j, kb - 1)];  // inside the block
-        x[j] = (i < kb && j < kb && j <= i) ? v : 0.0;
+        x[jl] = (i < kb && j < kb && j <= i) ? v : 0.0;
     }
-    // columns past kb (the last, narrower block) are zero rows and columns:
-    // a unit pivot there changes nothing that is stored
+    for (int p = 0; p < kNB / kPW; ++p) {
+        if (w == p) {  // uniform over the wave
 #pragma unroll
-    for (int c = 0; c < kNB; ++c) {
-        const int lo = __builtin_amdgcn_readlane((int)(__double_as_longlong(x[c]) & 0xFFFFFFFFll), c);
-        const int hi = __builtin_amdgcn_readlane((int)(__double_as_longlong(x[c]) >> 32), c);
-        double d = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-        if (c >= kb) {  // uniform
-            d = 1.0;
-        } else if (!(d > 0.0)) {  // uniform
-            if (i == 0 && *info == 0) *info = (int32_t)(k0 + c + 1);
-            d = 1.0;
+            for (int cl = 0; cl < kPW; ++cl) {
+                const int c = j0 + cl;
+                double d = readlane_f64(x[cl], c);
+                if (c >= kb) {  // uniform
+                    d = 1.0;
+                } else if (!(d > 0.0)) {  // uniform
+                    if (i == 0 && *info == 0) *info = (int32_t)(k0 + c + 1);
+                    d = 1.0;
+                }
+                const double sc = sqrt(d);
+                x[cl] = i == c ? sc : (i > c ? x[cl] / sc : x[cl]);
+#pragma unroll
+                for (int jl = cl + 1; jl < kPW; ++jl)
+                    x[jl] = __builtin_fma(-x[cl], readlane_f64(x[cl], j0 + jl), x[jl]);
+            }
+#pragma unroll
+            for (int cl = 0; cl < kPW; ++cl) pan[i][cl] = x[cl];
         }
-        const double sc = sqrt(d);
-        x[c] = i == c ? sc : (i > c ? x[c] / sc : x[c]);
-        col[i] = x[c];
-        __syncthreads();  // one wave: orders the column's store before its reads
+        __syncthreads();
+        if (w > p) {
 #pragma unroll
-        for (int j = c + 1; j < kNB; ++j) x[j] -= x[c] * col[j];
-        // the updates happen in this column (left to the scheduler they sink
-        // to their use and keep every column value alive until then)
+            for (int cl = 0; cl < kPW; ++cl) {
+                const double a = pan[i][cl];
 #pragma unroll
-        for (int j = c + 1; j < kNB; ++j) asm volatile("" : "+v"(x[j]));
-        __syncthreads();  // the column is read before the next one is stored
+                for (int jl = 0; jl < kPW; ++jl)
+                    x[jl] = __builtin_fma(-a, pan[j0 + jl][cl], x[jl]);
+            }
+        }
+        __syncthreads();  // the panel is read before the next one is written
     }
     if (i < kb) {
         double* out = B + (k0 + i) * n + k0;
 #pragma unroll
-        for (int j = 0; j < kNB; ++j)
-            if (j < kb && j <= i) out[j] = x[j];
+        for (int jl = 0; jl < kPW; ++jl) {
+            const int j = j0 + jl;
+            if (j < kb && j <= i) out[j] = x[jl];
+        }
     }
 }
 
@@ -141,12 +166,21 @@ __global__ __launch_bounds__(64) void trsm_panel_kernel(double* __restrict__ B, 
                                                         int64_t k0) {
     __shared__ double L[kNB][kNB + 1];
     __shared__ double rdiag[kNB];
-    for (int p = threadIdx.x; p < kNB * kNB; p += 64) {
-        const int i = p / kNB, j = p % kNB;
-        const double v = B[(k0 + i) * n + k0 + j];
-        if (j < i) L[i][j] = -v;
-        else if (j == i) rdiag[i] = 1.0 / v;
-        if (j >= i) L[i][j] = 0.0;
+    {
+        // thread i stages row i of the diagonal block: all of its loads are
+        // issued before the first is used (one latency, not one per entry)
+        const int i = threadIdx.x;
+        const double* src = B + (k0 + i) * n + k0;
+        double v[kNB];
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) v[j] = src[j];
+        double d = 1.0;
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+            L[i][j] = j < i ? -v[j] : 0.0;
+            d = j == i ? v[j] : d;
+        }
+        rdiag[i] = 1.0 / d;
     }
     __syncthreads();
     constexpr int kQK = kNB / 4;
@@ -276,12 +310,13 @@ __device__ __forceinline__ void tile_product(int64_t kbeg, int64_t kend, LP ldp,
 }
 
 // Trailing update B[i][j] -= sum_{kbeg <= c < kend} B[i][c] B[j][c] for
-// r0 <= j <= i < n and j < cend, on 128 x 128 tiles of the lower triangle
-// (tile (ti, tj) starts at row r0 + 128 ti, column r0 + 128 tj).
+// r0 <= j <= i < n and j < cend, on TILE x TILE tiles of the lower triangle
+// (tile (ti, tj) starts at row r0 + TILE ti, column r0 + TILE tj).  Every
+// entry's sum runs over c in the same order whatever the tile size.
+template <int TILE>
 __global__ __launch_bounds__(256) void syrk_update_kernel(double* __restrict__ B, int64_t n,
                                                           int64_t kbeg, int64_t kend, int64_t r0,
                                                           int64_t cend) {
-    constexpr int TILE = 128;
     const int ti = blockIdx.y, tj = blockIdx.x;
     if (tj > ti) return;  // lower tiles only; uniform over the block
     __shared__ __attribute__((aligned(16))) double Ps[TILE][kKP];
@@ -405,6 +440,39 @@ size_t gptq_factor_workspace(int64_t n) {
     return (size_t)(n * n + inv_scratch(n) + 2) * sizeof(double);
 }
 
+// The factor's second stream (lookahead updates), one per device, created
+// on first use at the default priority and kept until the process ends.
+static hipError_t side_stream(hipStream_t* out) {
+    static std::mutex mu;
+    static hipStream_t streams[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[dev]) {
+        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+    }
+    *out = streams[dev];
+    return hipSuccess;
+}
+
+// Ordering events of one factor call (no timing).
+struct Events {
+    hipEvent_t main = nullptr, side = nullptr;
+    hipError_t create() {
+        hipError_t e = hipEventCreateWithFlags(&main, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&side, hipEventDisableTiming);
+        return e;
+    }
+    void destroy() {  // released by the runtime once the work they order is done
+        if (main) (void)hipEventDestroy(main);
+        if (side) (void)hipEventDestroy(side);
+        main = side = nullptr;
+    }
+};
+
 hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, int32_t* info,
                               void* workspace, hipStream_t s) {
     double* B = static_cast<double*>(workspace);
@@ -418,29 +486,70 @@ hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, 
     if (e != hipSuccess) return e;
     // Outer panels of kOuter columns, each factored in kNB-wide steps whose
     // updates stay inside the panel; then one rank-kOuter update of
-    // everything right of and below it.
-    auto update = [&](int64_t kbeg, int64_t kend, int64_t r0, int64_t cend) {
+    // everything right of and below it.  Lookahead: each update is split
+    // into the next step's kNB columns (this stream) and the rest (a second
+    // stream), so the next diagonal factor and panel solve, which need only
+    // those columns, run while the rest is updated.  The next step's update
+    // writes columns the previous rest also writes, so it waits for it.
+    // (a strip of kNB columns takes 64 x 64 tiles: 128-wide ones would be
+    // half empty and twice as few)
+    auto update = [&](hipStream_t st, int64_t kbeg, int64_t kend, int64_t r0, int64_t cend) {
         const int64_t rows = n - r0, cols = cend - r0;
         if (rows <= 0 || cols <= 0) return;
-        const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
-        hipLaunchKernelGGL(syrk_update_kernel, grid, dim3(256), 0, s, B, n, kbeg, kend, r0, cend);
+        if (cols <= kNB) {
+            const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+            hipLaunchKernelGGL((syrk_update_kernel<64>), grid, dim3(256), 0, st, B, n, kbeg, kend,
+                               r0, cend);
+        } else {
+            const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+            hipLaunchKernelGGL((syrk_update_kernel<128>), grid, dim3(256), 0, st, B, n, kbeg, kend,
+                               r0, cend);
+        }
     };
-    for (int64_t K0 = 0; K0 < n; K0 += kOuter) {
+    hipStream_t side = nullptr;
+    e = side_stream(&side);
+    if (e != hipSuccess) return e;
+    Events ev;
+    e = ev.create();
+    if (e != hipSuccess) return e;
+    // the side stream starts after everything already on this stream
+    e = hipEventRecord(ev.main, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev.main, 0);
+    bool side_used = false;
+    // split update of columns [r0, cend): the first kNB on this stream, the
+    // rest on the side stream after this stream's work so far
+    auto split_update = [&](int64_t kbeg, int64_t kend, int64_t r0, int64_t cend) {
+        if (e != hipSuccess) return;
+        if (side_used) e = hipStreamWaitEvent(s, ev.side, 0);  // the previous rest is done
+        if (e != hipSuccess) return;
+        update(s, kbeg, kend, r0, std::min<int64_t>(r0 + kNB, cend));
+        if (r0 + kNB >= cend) return;
+        e = hipEventRecord(ev.main, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side, ev.main, 0);
+        if (e != hipSuccess) return;
+        update(side, kbeg, kend, r0 + kNB, cend);
+        e = hipEventRecord(ev.side, side);
+        side_used = true;
+    };
+    for (int64_t K0 = 0; K0 < n && e == hipSuccess; K0 += kOuter) {
         const int64_t K1 = std::min<int64_t>(K0 + kOuter, n);
-        for (int64_t k0 = K0; k0 < K1; k0 += kNB) {
+        for (int64_t k0 = K0; k0 < K1 && e == hipSuccess; k0 += kNB) {
             const int kb = (int)std::min<int64_t>(kNB, n - k0);
-            hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(64), 0, s, B, n, k0, kb, info);
+            hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, B, n, k0, kb, info);
             const int64_t rest = n - k0 - kb;
             if (rest > 0) {  // kb == 64 here: only the last panel can be narrower
                 hipLaunchKernelGGL(trsm_panel_kernel, dim3((unsigned)((rest + 15) / 16)),
                                    dim3(64), 0, s, B, n, k0);
-                update(k0, k0 + kb, k0 + kb, K1);  // the rest of this outer panel
+                split_update(k0, k0 + kb, k0 + kb, K1);  // the rest of this outer panel
             }
         }
-        update(K0, K1, K1, n);  // everything after it
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (e == hipSuccess) split_update(K0, K1, K1, n);  // everything after it
+        if (e == hipSuccess) e = hipGetLastError();
     }
+    // this stream continues after the side stream's last update
+    if (e == hipSuccess && side_used) e = hipStreamWaitEvent(s, ev.side, 0);
+    ev.destroy();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(trtri_diag_kernel, dim3((unsigned)((n + kNB - 1) / kNB)), dim3(64), 0, s,
                        B, n);
     for (int64_t bs = kNB; bs < n; bs *= 2) {
