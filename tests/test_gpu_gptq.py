@@ -70,10 +70,12 @@ def test_gptq_factor(I, damp):
     assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
 
 
-@pytest.mark.parametrize("I", [1100, 1089])
+@pytest.mark.parametrize("I", [1100, 1089, 2100])
 def test_gptq_factor_several_outer_panels(I):
     # more than two 512-column outer panels (rank-512 trailing updates, the
-    # in-panel rank-64 updates, a narrower last 64-column step)
+    # in-panel rank-64 updates, a narrower last 64-column step); every update
+    # is split between two streams, so 2100 also runs 33 steps of that
+    # ordering
     X = correlated_x(2 * I, I, I + 5)
     H = (X.astype(np.float64).T @ X.astype(np.float64)).astype(np.float32)
     say(f"gptq_factor outer panels I={I}")
