@@ -342,20 +342,32 @@ __global__ __launch_bounds__(256) void pack_i3_kernel(const int8_t* __restrict__
             c[q] = wv;
         }
     }
-    uint32_t lo[4] = {0, 0, 0, 0};
+    // Byte-parallel: word q holds slots 4q..4q+3, which are exactly low byte
+    // q (two bits each) and high bits 4q..4q+3.
+    uint32_t lb[16];  // low byte q in bits 0..7 (higher bits are not used)
     uint32_t hi[2] = {0, 0};
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         // u = (v + 4) mod 8 in every byte: flipping bit 2 of the low three
         // bits of v (no carry crosses a byte)
         const uint32_t u4 = (c[q] & 0x07070707u) ^ 0x04040404u;
+        // low two bits of byte b to bits 2b..2b+1 of byte 0
+        const uint32_t t = u4 & 0x03030303u;
+        const uint32_t x = t | (t >> 6);  // bytes 0 and 2: two slots each
+        lb[q] = x | (x >> 12);
+        // bit 2 of byte b to bit b of a nibble: the product's terms land on
+        // distinct bits (no carries), bits 21..24 hold the four
+        const uint32_t h = (u4 >> 2) & 0x01010101u;
+        const uint32_t nib = ((h * 0x00204081u) >> 21) & 0xFu;
+        hi[q >> 3] |= nib << (4 * (q & 7));
+    }
+    uint32_t lo[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t u = (u4 >> (8 * b)) & 7u;
-            const int j = 4 * q + b;  // slot index in the group
-            lo[j >> 4] |= (u & 3u) << (2 * (j & 15));
-            hi[j >> 5] |= (u >> 2) << (j & 31);
-        }
+    for (int w = 0; w < 4; ++w) {
+        // bytes 0 of lb[4w .. 4w+3] side by side
+        const uint32_t p01 = __builtin_amdgcn_perm(lb[4 * w + 1], lb[4 * w], 0x0C0C0400u);
+        const uint32_t p23 = __builtin_amdgcn_perm(lb[4 * w + 3], lb[4 * w + 2], 0x04000C0Cu);
+        lo[w] = p01 | p23;
     }
     uint2* dst = reinterpret_cast<uint2*>(packed + grp * kGroupBytes);
     dst[0] = make_uint2(lo[0], lo[1]);
