@@ -103,8 +103,12 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ B,
                     if (i == 0 && *info == 0) *info = (int32_t)(k0 + c + 1);
                     d = 1.0;
                 }
-                const double sc = sqrt(d);
-                x[cl] = i == c ? sc : (i > c ? x[cl] / sc : x[cl]);
+                // 1/sqrt(d): the hardware estimate and one Newton step
+                // (doubling its correct bits), then sqrt(d) = d / sqrt(d)
+                const double r0 = __builtin_amdgcn_rsq(d);
+                const double res = __builtin_fma(-d * r0, r0, 1.0);
+                const double rs = __builtin_fma(0.5 * r0, res, r0);
+                x[cl] = i == c ? d * rs : (i > c ? x[cl] * rs : x[cl]);
 #pragma unroll
                 for (int jl = cl + 1; jl < kPW; ++jl)
                     x[jl] = __builtin_fma(-x[cl], readlane_f64(x[cl], j0 + jl), x[jl]);
