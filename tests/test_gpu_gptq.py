@@ -89,6 +89,34 @@ def test_gptq_factor_several_outer_panels(I):
     assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
 
 
+def test_gptq_factor_calls_on_two_streams():
+    # two factor calls on two streams, issued without synchronising between
+    # them (their lookahead updates share the library's second stream of the
+    # device): each gives the same bits as when it runs alone
+    I = 700
+    Hs = []
+    for seed in (41, 42):
+        X = correlated_x(2 * I, I, seed)
+        Hs.append((X.astype(np.float64).T @ X.astype(np.float64)).astype(np.float32))
+    say("gptq_factor two streams I=700")
+    solo = [host(qt.qt_gptq_factor(dev(H), 0.01)[0]) for H in Hs]
+    Hd = [dev(H) for H in Hs]
+    nb = qt.qt_gptq_factor_workspace_bytes(I)
+    ws = [torch.empty(nb, dtype=torch.uint8, device=Hd[0].device) for _ in Hs]
+    Us = [torch.empty((I, I), dtype=torch.float32, device=Hd[0].device) for _ in Hs]
+    infos = [torch.zeros(1, dtype=torch.int32, device=Hd[0].device) for _ in Hs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for q in range(2):
+            qt.qt_gptq_factor(Hd[q], 0.01, U=Us[q], info=infos[q], workspace=ws[q],
+                              stream=streams[q])
+        torch.cuda.synchronize()
+        for q in range(2):
+            assert host(infos[q])[0] == 0
+            assert np.array_equal(bits(host(Us[q])), bits(solo[q])), f"call {q} differs"
+
+
 def test_gptq_factor_reports_an_indefinite_matrix():
     # [[1, 2], [2, 1]] reversed is itself: the first pivot is 1, the second
     # 1 - 2*2/1 = -3, so the factorization fails at column 2
