@@ -15,7 +15,6 @@
 //   buffer; the triangular factors' zero halves are skipped).
 // A non-positive pivot sets *info to its 1-based column (of the reversed
 // matrix) and is replaced by 1 so that every later step stays finite.
-#include <mutex>
 #include <algorithm>
 
 #include "qt_internal.h"
@@ -444,39 +443,6 @@ size_t gptq_factor_workspace(int64_t n) {
     return (size_t)(n * n + inv_scratch(n) + 2) * sizeof(double);
 }
 
-// The factor's second stream (lookahead updates), one per device, created
-// on first use at the default priority and kept until the process ends.
-static hipError_t side_stream(hipStream_t* out) {
-    static std::mutex mu;
-    static hipStream_t streams[64] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!streams[dev]) {
-        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
-        if (e != hipSuccess) return e;
-    }
-    *out = streams[dev];
-    return hipSuccess;
-}
-
-// Ordering events of one factor call (no timing).
-struct Events {
-    hipEvent_t main = nullptr, side = nullptr;
-    hipError_t create() {
-        hipError_t e = hipEventCreateWithFlags(&main, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&side, hipEventDisableTiming);
-        return e;
-    }
-    void destroy() {  // released by the runtime once the work they order is done
-        if (main) (void)hipEventDestroy(main);
-        if (side) (void)hipEventDestroy(side);
-        main = side = nullptr;
-    }
-};
-
 hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, int32_t* info,
                               void* workspace, hipStream_t s) {
     double* B = static_cast<double*>(workspace);
@@ -490,70 +456,37 @@ hipError_t launch_gptq_factor(const float* H, int64_t n, double damp, float* U, 
     if (e != hipSuccess) return e;
     // Outer panels of kOuter columns, each factored in kNB-wide steps whose
     // updates stay inside the panel; then one rank-kOuter update of
-    // everything right of and below it.  Lookahead: each update is split
-    // into the next step's kNB columns (this stream) and the rest (a second
-    // stream), so the next diagonal factor and panel solve, which need only
-    // those columns, run while the rest is updated.  The next step's update
-    // writes columns the previous rest also writes, so it waits for it.
-    // (a strip of kNB columns takes 64 x 64 tiles: 128-wide ones would be
-    // half empty and twice as few)
-    auto update = [&](hipStream_t st, int64_t kbeg, int64_t kend, int64_t r0, int64_t cend) {
+    // everything right of and below it.  A strip of kNB columns takes
+    // 64 x 64 tiles (128-wide ones would be half empty and twice as few).
+    auto update = [&](int64_t kbeg, int64_t kend, int64_t r0, int64_t cend) {
         const int64_t rows = n - r0, cols = cend - r0;
         if (rows <= 0 || cols <= 0) return;
         if (cols <= kNB) {
             const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
-            hipLaunchKernelGGL((syrk_update_kernel<64>), grid, dim3(256), 0, st, B, n, kbeg, kend,
+            hipLaunchKernelGGL((syrk_update_kernel<64>), grid, dim3(256), 0, s, B, n, kbeg, kend,
                                r0, cend);
         } else {
             const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
-            hipLaunchKernelGGL((syrk_update_kernel<128>), grid, dim3(256), 0, st, B, n, kbeg, kend,
+            hipLaunchKernelGGL((syrk_update_kernel<128>), grid, dim3(256), 0, s, B, n, kbeg, kend,
                                r0, cend);
         }
     };
-    hipStream_t side = nullptr;
-    e = side_stream(&side);
-    if (e != hipSuccess) return e;
-    Events ev;
-    e = ev.create();
-    if (e != hipSuccess) return e;
-    // the side stream starts after everything already on this stream
-    e = hipEventRecord(ev.main, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev.main, 0);
-    bool side_used = false;
-    // split update of columns [r0, cend): the first kNB on this stream, the
-    // rest on the side stream after this stream's work so far
-    auto split_update = [&](int64_t kbeg, int64_t kend, int64_t r0, int64_t cend) {
-        if (e != hipSuccess) return;
-        if (side_used) e = hipStreamWaitEvent(s, ev.side, 0);  // the previous rest is done
-        if (e != hipSuccess) return;
-        update(s, kbeg, kend, r0, std::min<int64_t>(r0 + kNB, cend));
-        if (r0 + kNB >= cend) return;
-        e = hipEventRecord(ev.main, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(side, ev.main, 0);
-        if (e != hipSuccess) return;
-        update(side, kbeg, kend, r0 + kNB, cend);
-        e = hipEventRecord(ev.side, side);
-        side_used = true;
-    };
-    for (int64_t K0 = 0; K0 < n && e == hipSuccess; K0 += kOuter) {
+    for (int64_t K0 = 0; K0 < n; K0 += kOuter) {
         const int64_t K1 = std::min<int64_t>(K0 + kOuter, n);
-        for (int64_t k0 = K0; k0 < K1 && e == hipSuccess; k0 += kNB) {
+        for (int64_t k0 = K0; k0 < K1; k0 += kNB) {
             const int kb = (int)std::min<int64_t>(kNB, n - k0);
             hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, B, n, k0, kb, info);
             const int64_t rest = n - k0 - kb;
             if (rest > 0) {  // kb == 64 here: only the last panel can be narrower
                 hipLaunchKernelGGL(trsm_panel_kernel, dim3((unsigned)((rest + 15) / 16)),
                                    dim3(64), 0, s, B, n, k0);
-                split_update(k0, k0 + kb, k0 + kb, K1);  // the rest of this outer panel
+                update(k0, k0 + kb, k0 + kb, K1);  // the rest of this outer panel
             }
         }
-        if (e == hipSuccess) split_update(K0, K1, K1, n);  // everything after it
-        if (e == hipSuccess) e = hipGetLastError();
+        update(K0, K1, K1, n);  // everything after it
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    // this stream continues after the side stream's last update
-    if (e == hipSuccess && side_used) e = hipStreamWaitEvent(s, ev.side, 0);
-    ev.destroy();
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(trtri_diag_kernel, dim3((unsigned)((n + kNB - 1) / kNB)), dim3(64), 0, s,
                        B, n);
     for (int64_t bs = kNB; bs < n; bs *= 2) {

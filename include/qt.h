@@ -19,9 +19,7 @@
  *   - Pointers are DEVICE pointers unless stated otherwise; all tensors are
  *     contiguous and row-major; the caller owns every buffer.  The library
  *     never allocates or frees device memory and keeps no mutable global
- *     state, so calls are reentrant.  One exception: qt_gptq_factor keeps a
- *     second stream per device (created on first use at the default
- *     priority, thread-safe, kept until the process ends) for its lookahead.
+ *     state, so calls are reentrant.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns before the work completes; results are
  *     valid once the caller has synchronised that stream.
@@ -300,11 +298,7 @@ qt_status qt_hessian_full(const void* X, qt_dtype xt, int64_t T, int64_t I, floa
  * index of the first non-positive pivot of the reversed matrix (the result is
  * then not a factor of A).  damp >= 0 (0.01 is the usual choice).
  * workspace: qt_gptq_factor_workspace_bytes(I) bytes (about 8 I^2).
- * I <= 65535.  Part of the work runs on the library's second stream of the
- * device, ordered against `stream` by events (created and released per
- * call): `stream` waits for it before the call's last kernels, so the
- * usual rule holds (results valid once `stream` is synchronised).  Calls on
- * different streams stay correct; their side work shares the second stream.
+ * I <= 65535.
  */
 size_t qt_gptq_factor_workspace_bytes(int64_t I);
 qt_status qt_gptq_factor(const float* H, int64_t I, double damp, float* U,

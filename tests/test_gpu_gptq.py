@@ -73,9 +73,7 @@ def test_gptq_factor(I, damp):
 @pytest.mark.parametrize("I", [1100, 1089, 2100])
 def test_gptq_factor_several_outer_panels(I):
     # more than two 512-column outer panels (rank-512 trailing updates, the
-    # in-panel rank-64 updates, a narrower last 64-column step); every update
-    # is split between two streams, so 2100 also runs 33 steps of that
-    # ordering
+    # in-panel rank-64 updates, a narrower last 64-column step)
     X = correlated_x(2 * I, I, I + 5)
     H = (X.astype(np.float64).T @ X.astype(np.float64)).astype(np.float32)
     say(f"gptq_factor outer panels I={I}")
@@ -91,8 +89,8 @@ def test_gptq_factor_several_outer_panels(I):
 
 def test_gptq_factor_calls_on_two_streams():
     # two factor calls on two streams, issued without synchronising between
-    # them (their lookahead updates share the library's second stream of the
-    # device): each gives the same bits as when it runs alone
+    # them, each on its own workspace: each gives the same bits as when it
+    # runs alone
     I = 700
     Hs = []
     for seed in (41, 42):
