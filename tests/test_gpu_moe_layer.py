@@ -89,6 +89,17 @@ def test_moe_layer_routing_sizes(E, T, k):
     assert np.array_equal(fbits(out1), fbits(out2)), "not deterministic"
 
 
+@pytest.mark.parametrize("E,T,k", [(1, 3, 1),      # one expert: every pair on it
+                                   (4, 70, 4),     # k = E: every token picks every expert
+                                   (2, 64, 1)])    # exactly one pass of 64 tokens
+def test_moe_layer_routing_degenerate(E, T, k):
+    F, D = 128, 128
+    gate, up, down = experts(E, F, D, 300 + E + T, (3, 3, 3))
+    X = workloads.generic_matrix(T, D, seed=T + 7)
+    logits = workloads.rng_for("generic", 903, T, E).random((T, E)).astype(np.float32)
+    check(X, logits, k, gate, up, down, "degenerate routing")
+
+
 def test_moe_layer_routing_ties_and_idle_experts():
     # tied logits pick the lower expert first; experts nobody picks are idle
     E, F, D, T, k = 8, 128, 128, 4, 3
