@@ -33,6 +33,16 @@
 //    four waves per SIMD overlap their loads with the other waves' arithmetic;
 //    larger tiles use 8 waves of 64 lanes per row.  The inputs of a chunk of
 //    GC groups of all T tokens are staged at once.
+//  * One f32 token (the decode case) has a kernel of its own: the input
+//    vector is copied into LDS once per block by LDS-direct loads
+//    (global_load_lds, 16 bytes per lane, no register round trip), and only
+//    then are the weight loads issued, so that each wave starts its
+//    arithmetic as soon as its own weights arrive.  Issuing the weight loads
+//    first was measured slower in every form tried: the input copy then
+//    finishes only after the weights, and no wave computes while others
+//    still wait.  Blocks loop over 8-row tiles (the next tile's weights in
+//    flight while the current one is multiplied), so one launch streams any
+//    number of rows with the input staged once per block.
 #include <algorithm>
 
 #include "qt_internal.h"
@@ -446,6 +456,149 @@ static hipError_t run_batch(const uint8_t* packed, const float* scales, int64_t 
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------- decode kernel
+// One f32 input vector, lane q of a row taking groups q, q + 128, ... (at
+// most kDecMaxG groups, all staged at once).  LDS layout of x: 16-byte piece p
+// (columns 4p .. 4p+3) at byte (p / 64) * kDecChunk + (p % 64) * 16, i.e. four
+// groups per 1024-byte run, each run padded by 16 bytes.
+constexpr int kDecRows = 8;       // rows per tile
+constexpr int kDecMaxG = 256;     // groups per row the decode kernel stages
+constexpr int kDecChunk = 1040;   // LDS bytes per 64 pieces (4 groups)
+
+__device__ __forceinline__ const float* dec_group(const float* xs, int64_t g) {
+    return reinterpret_cast<const float*>(reinterpret_cast<const char*>(xs) + (g >> 2) * kDecChunk +
+                                          (g & 3) * 256);
+}
+
+// NG: groups per lane (G <= 128 NG).  LOOP: blocks take several 8-row tiles
+// (the next tile's weights in flight while the current one is multiplied);
+// otherwise each block multiplies one tile.
+template <int BITS, int NG, bool LOOP>
+__global__ __launch_bounds__(1024) void gemv_decode_kernel(
+    const uint8_t* __restrict__ packed, const float* __restrict__ scales, int O, int I,
+    int G, const float* __restrict__ x, float* __restrict__ y, int ntiles) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    typedef __attribute__((address_space(1))) void glob_void;
+    extern __shared__ __attribute__((aligned(16))) float xs[];
+    __shared__ float part[2][16];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int q = tid & 127;
+    const int rl = tid >> 7;
+
+    // ---- x into LDS: wave w copies runs w, w + 16, ...; pieces past I are
+    // zeroed (I % 4 == 0, so a piece lies wholly inside or outside x)
+    const int nruns = (G + 3) / 4;
+    for (int c = w; c < nruns; c += 16) {
+        const int pc = c * 64 + lane;  // piece: columns 4 pc .. 4 pc + 3
+        char* base = reinterpret_cast<char*>(xs) + c * kDecChunk;  // wave-uniform
+        if (4 * pc < I)
+            __builtin_amdgcn_global_load_lds((const glob_void*)(x + 4 * pc), (lds_void*)base, 16, 0,
+                                             0);
+        else if (pc < 16 * G)
+            *reinterpret_cast<float4*>(base + 16 * lane) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+
+    const float* xg[NG][1];
+#pragma unroll
+    for (int m = 0; m < NG; ++m) xg[m][0] = dec_group(xs, q + 128 * m < G ? q + 128 * m : 0);
+    // several tiles, one group per lane: its 64 inputs are read into registers
+    // once and serve every tile of the block (read after the first tile's
+    // weight loads are issued, so the LDS reads do not wait for the weights)
+    float xr[NG == 1 ? kGroup : 1];
+    const float* xrp[1] = {xr};
+    auto read_x = [&]() {
+        if constexpr (NG == 1) {
+#pragma unroll
+            for (int k = 0; k < kGroup / 4; ++k) {
+                const float4 v = reinterpret_cast<const float4*>(xg[0][0])[k];
+                xr[4 * k] = v.x;
+                xr[4 * k + 1] = v.y;
+                xr[4 * k + 2] = v.z;
+                xr[4 * k + 3] = v.w;
+            }
+        }
+    };
+
+    // ---- lanes past G and rows past O load nothing and skip the arithmetic
+    auto load_tile = [&](int tile, GroupBits<BITS> (&gb)[NG], float (&sc)[NG]) {
+        const int r = tile * kDecRows + rl;
+#pragma unroll
+        for (int m = 0; m < NG; ++m) {
+            const int g = q + 128 * m;
+            if (r < O && g < G) {
+                const int64_t gi = (int64_t)r * G + g;
+                gb[m] = load_group<BITS>(packed + gi * GroupBits<BITS>::kBytes);
+                sc[m] = scales[gi];
+            }
+        }
+    };
+    auto mul_tile = [&](int tile, int it, const GroupBits<BITS> (&gb)[NG], const float (&sc)[NG]) {
+        const int r = tile * kDecRows + rl;
+        float rowacc[1] = {0.0f};
+        if constexpr (NG == 1 && LOOP) {
+            if (r < O && q < G) group_dot<1, 1, BITS>(gb[0], sc[0], xrp, rowacc);
+        } else {
+#pragma unroll
+            for (int m = 0; m < NG; ++m)
+                if (r < O && q + 128 * m < G) group_dot<1, 1, BITS>(gb[m], sc[m], xg[m], rowacc);
+        }
+        const float acc = lane_group_sum<64>(rowacc[0]);
+        // the two waves of a row in a fixed order; part is double-buffered by
+        // tile parity, so one barrier per tile suffices
+        if (lane == 0) part[it & 1][w] = acc;
+        __syncthreads();
+        if (q == 0 && r < O) y[r] = part[it & 1][w] + part[it & 1][w + 1];
+    };
+    GroupBits<BITS> cur[NG];
+    float cs[NG];
+    if constexpr (!LOOP) {
+        // one tile: the inputs are read from LDS inside the arithmetic (the
+        // compiler issues those reads ahead of the weights' arrival)
+        load_tile(blockIdx.x, cur, cs);
+        mul_tile(blockIdx.x, 0, cur, cs);
+    } else {
+        GroupBits<BITS> nxt[NG];
+        float ns[NG];
+        int tile = blockIdx.x;
+        load_tile(tile, cur, cs);
+        read_x();
+        for (int it = 0; tile < ntiles; tile += gridDim.x, ++it) {
+            if (tile + (int)gridDim.x < ntiles) load_tile(tile + gridDim.x, nxt, ns);
+            mul_tile(tile, it, cur, cs);
+#pragma unroll
+            for (int m = 0; m < NG; ++m) {
+                cur[m] = nxt[m];
+                cs[m] = ns[m];
+            }
+        }
+    }
+}
+
+template <int BITS>
+static hipError_t run_decode(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
+                             const float* x, float* y, hipStream_t s) {
+    const int G = (int)((I + kGroup - 1) / kGroup);
+    const int ntiles = (int)((O + kDecRows - 1) / kDecRows);
+    // up to two blocks per CU on a 256-CU device; more tiles loop
+    const int blocks = std::min(ntiles, 512);
+    const size_t lds = (size_t)((G + 3) / 4) * kDecChunk;
+    const dim3 grid((unsigned)blocks), block(1024);
+#define QT_DEC(NG, LOOP)                                                                   \
+    hipLaunchKernelGGL((gemv_decode_kernel<BITS, NG, LOOP>), grid, block, lds, s, packed, \
+                       scales, (int)O, (int)I, G, x, y, ntiles)
+    if (G <= 128) {
+        if (ntiles <= blocks) QT_DEC(1, false);
+        else QT_DEC(1, true);
+    } else {
+        if (ntiles <= blocks) QT_DEC(2, false);
+        else QT_DEC(2, true);
+    }
+#undef QT_DEC
+    return hipGetLastError();
+}
+
 template <bool BF16, bool VEC, int BITS>
 static hipError_t batch_dispatch(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
                                  const void* X, int64_t ntok, float* Y, hipStream_t s) {
@@ -462,6 +615,9 @@ static hipError_t gemv_bits(const uint8_t* packed, const float* scales, int64_t 
     // 16-byte (f32) or 8-byte (bf16) input loads need aligned rows
     const uintptr_t al = bf16 ? 8 : 16;
     const bool vec = (I % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & (al - 1)) == 0);
+    // the decode kernel indexes rows and columns in 32 bits
+    if (!bf16 && vec && ntok == 1 && (I + kGroup - 1) / kGroup <= kDecMaxG && O <= (1 << 28))
+        return run_decode<BITS>(packed, scales, O, I, static_cast<const float*>(X), Y, s);
     if (bf16)
         return vec ? batch_dispatch<true, true, BITS>(packed, scales, O, I, X, ntok, Y, s)
                    : batch_dispatch<true, false, BITS>(packed, scales, O, I, X, ntok, Y, s);

@@ -178,13 +178,6 @@ def unpack_i3(packed, O: int, I: int):
     return out
 
 
-def dequant_f64(packed, scales, O: int, I: int):
-    packed, scales = _c(packed, np.uint8), _c(scales, np.float32)
-    out = np.empty((O, I), np.float64)
-    lib().qto_dequant_f64(_p(packed), _p(scales), O, I, _p(out))
-    return out
-
-
 def matvec_f64(packed, scales, O: int, I: int, x):
     """-> (y[O] f64, absy[O] f64)."""
     packed, scales, x = _c(packed, np.uint8), _c(scales, np.float32), _c(x, np.float32)
@@ -297,8 +290,14 @@ def proxy_terms(W, codes, scales, H):
 #     expert index first), combine weights a softmax over those k logits;
 #   - out_t = sum_j w_tj y_{e_tj}(x_t).
 def dequant_f64(packed, scales, O: int, I: int, bits: int = 3):
-    """The weights a packed matrix denotes, s * v, in f64 [O, I]."""
-    codes = unpack_i3(packed, O, I) if bits == 3 else unpack_i4(packed, O, I)
+    """The weights a packed matrix denotes, s * v, in f64 [O, I] (int3-g64 by
+    the C routine, grouped int4 from its unpacked codes)."""
+    if bits == 3:
+        packed, scales = _c(packed, np.uint8), _c(scales, np.float32)
+        out = np.empty((O, I), np.float64)
+        lib().qto_dequant_f64(_p(packed), _p(scales), O, I, _p(out))
+        return out
+    codes = unpack_i4(packed, O, I)
     s = np.repeat(np.asarray(scales, np.float64).reshape(O, -1), 64, axis=1)[:, :I]
     return s * codes.astype(np.float64)
 
@@ -350,4 +349,36 @@ def moe_layer_f64(X, logits, k: int, gate, up, down):
             dh = 1.1 * ag * np.abs(u) + np.abs(silu_f64(g)) * au  # |silu'| <= 1.1
             out[t] += w[t, j] * y
             bound[t] += w[t, j] * (np.abs(Wd) @ dh + np.abs(Wd) @ np.abs(h) + np.abs(y))
+    return out, bound
+
+
+def moe_layer_f64_tokens(X, logits, k: int, expert, tokens):
+    """moe_layer_f64 for the rows `tokens` only, without holding whole
+    dequantized matrices: expert(e) -> (gate, up, down), each (packed [bytes],
+    scales [O, G], bits) of one expert.  The gate and up products of a token
+    are the f64 matvecs (which also give sum |w x|); the down matrix of one
+    expert at a time is dequantized in f64.  -> (out [n, D], bound [n, D])."""
+    X = np.asarray(X, np.float32)
+    tokens = [int(t) for t in tokens]
+    experts, w = moe_route(logits, k)
+    D = X.shape[1]
+    out = np.zeros((len(tokens), D))
+    bound = np.zeros((len(tokens), D))
+
+    def mv(m, O, I, x):
+        return (matvec_f64 if m[2] == 3 else matvec_i4_f64)(m[0], m[1], O, I, x)
+
+    for i, t in enumerate(tokens):
+        x = X[t]
+        for j in range(k):
+            gate, up, down = expert(int(experts[t, j]))
+            F = np.asarray(gate[1]).shape[0]
+            g, ag = mv(gate, F, D, x)
+            u, au = mv(up, F, D, x)
+            h = silu_f64(g) * u
+            Wd = dequant_f64(down[0], down[1], D, F, down[2])
+            y = Wd @ h
+            dh = 1.1 * ag * np.abs(u) + np.abs(silu_f64(g)) * au  # |silu'| <= 1.1
+            out[i] += w[t, j] * y
+            bound[i] += w[t, j] * (np.abs(Wd) @ dh + np.abs(Wd) @ np.abs(h) + np.abs(y))
     return out, bound

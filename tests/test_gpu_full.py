@@ -1,10 +1,20 @@
 """Parity at the full workload sizes, in the launch configurations bench.py
-times, on sampled outputs the oracle computes one by one.
+times.
+
+Bit-exact over the whole of each configuration: every prefill slab's scales
+and packed bytes, every MoE expert's up and down matrices, every row of the
+weighted and the signed scale search (scales, codes, grid indices).  The f32
+products are compared on outputs the oracle computes one by one (all 256
+(token, expert) pairs of the MoE step for up and down, 16 outputs of every
+prefill slab).  The oracle runs on a pool of host threads: each call is a C
+function reached through ctypes, which releases the interpreter lock.
 
 Decode (W[2048x7168] and the 7200 tail variant) is compared in full in
-test_gpu_parity.py; here: the prefill GEMM, the 128-expert MoE grouped GEMV
-and the weighted scale search with its Hessian diagonal.
+test_gpu_parity.py.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -19,92 +29,119 @@ pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-5
 TOL_MFMA = 2e-3
+THREADS = min(16, os.cpu_count() or 1)
 
 
-def test_prefill_gemm_full_size_sampled():
+def oracle_quant_pack(W):
+    so, co, _ = oracle.quantize_g64(W)
+    return so, oracle.pack_i3(co)
+
+
+def test_prefill_gemm_full_size():
     O, I = workloads.PREFILL_SHAPE
     G = qt.qt_groups(I)
-    say(f"prefill: quantize+pack W[{O}x{I}] in 1024-row slabs on the GPU")
+    nslab = O // 1024
+    say(f"prefill: quantize+pack W[{O}x{I}] in {nslab} slabs of 1024 rows on the GPU")
     pk = torch.empty(qt.qt_packed_bytes(O, I), dtype=torch.uint8, device="cuda:0")
     sc = torch.empty((O, G), dtype=torch.float32, device="cuda:0")
     codes_dev = torch.empty((O, I), dtype=torch.int8, device="cuda:0")
-    for s in range(O // 1024):
-        w = dev(workloads.prefill_w([s]))
-        qt.qt_quantize_g64(w, scales=sc[s * 1024:(s + 1) * 1024],
+    slabs = []
+    for s in range(nslab):
+        w = workloads.prefill_w([s])
+        slabs.append(w)
+        qt.qt_quantize_g64(dev(w), scales=sc[s * 1024:(s + 1) * 1024],
                            codes=codes_dev[s * 1024:(s + 1) * 1024], want_grid_idx=False)
     qt.qt_pack_i3(codes_dev, pk)
+    del codes_dev
     Xb = workloads.prefill_x()
     B = Xb.shape[0]
     say(f"prefill: GEMM B={B}")
     Y = host(qt.qt_matmul_i3(pk, sc, O, I, dev_bf16(Xb)))
     Xf = workloads.bf16_bits_to_f32(Xb)
+    pk_h, sc_h = host(pk).reshape(O, G * 24), host(sc)
+    say(f"prefill: oracle quantize+pack of all {nslab} slabs on {THREADS} threads")
+    with ThreadPoolExecutor(THREADS) as ex:
+        ref = list(ex.map(oracle_quant_pack, slabs))
+    del slabs
+    for s, (so, po) in enumerate(ref):
+        rows = slice(s * 1024, (s + 1) * 1024)
+        assert np.array_equal(bits(sc_h[rows]), bits(so)), f"scales differ in slab {s}"
+        assert np.array_equal(pk_h[rows].reshape(-1), po), f"packed bytes differ in slab {s}"
+    # 16 sampled outputs of every slab against the f64 oracle
     rng = workloads.rng_for("generic", 9001)
-    slabs = rng.choice(O // 1024, size=3, replace=False)
-    pk_h, sc_h = host(pk), host(sc)
-    worst = 0.0
-    for s in slabs:
-        Wslab = workloads.prefill_w([int(s)])
-        so, co, _ = oracle.quantize_g64(Wslab)
-        rows = np.arange(s * 1024, (s + 1) * 1024)
-        assert np.array_equal(bits(sc_h[rows]), bits(so)), "scales differ"
-        po = oracle.pack_i3(co)
-        assert np.array_equal(pk_h.reshape(O, G * 24)[rows].reshape(-1), po), "packed differ"
-        # sampled outputs of this slab
-        t_idx = rng.integers(0, B, size=96)
-        o_loc = rng.integers(0, 1024, size=96)
+
+    def slab_err(s):
+        so, po = ref[s]
+        t_idx = rng_t[s]
+        o_loc = rng_o[s]
         yr, ar = oracle.matmul_f64_sampled(po, so, 1024, I, Xf, t_idx, o_loc)
-        err = componentwise_err(Y[t_idx, s * 1024 + o_loc], yr, ar)
-        worst = max(worst, err)
-    say(f"  sampled componentwise err {worst:.3e}")
+        return componentwise_err(Y[t_idx, s * 1024 + o_loc], yr, ar)
+
+    rng_t = [rng.integers(0, B, size=16) for _ in range(nslab)]
+    rng_o = [rng.integers(0, 1024, size=16) for _ in range(nslab)]
+    with ThreadPoolExecutor(THREADS) as ex:
+        worst = max(ex.map(slab_err, range(nslab)))
+    say(f"  all {nslab} slabs bit-exact; {16 * nslab} sampled outputs, componentwise err "
+        f"{worst:.3e}")
     assert worst <= TOL_MFMA
 
 
-def test_moe_grouped_full_size_sampled():
+def test_moe_grouped_full_size():
     E = workloads.MOE_EXPERTS
     (Ou, Iu), (Od, Id) = workloads.MOE_UP_SHAPE, workloads.MOE_DOWN_SHAPE
     Gu, Gd = qt.qt_groups(Iu), qt.qt_groups(Id)
     d0 = "cuda:0"
+    Xm, top = workloads.moe_tokens()
+    tok, exp, offs = workloads.route_pairs(top, E)
+    P = tok.size
+    hit = set(int(e) for e in np.unique(exp))
     pu = torch.empty((E, qt.qt_packed_bytes(Ou, Iu)), dtype=torch.uint8, device=d0)
     su = torch.empty((E, Ou, Gu), dtype=torch.float32, device=d0)
     pdn = torch.empty((E, qt.qt_packed_bytes(Od, Id)), dtype=torch.uint8, device=d0)
     sdn = torch.empty((E, Od, Gd), dtype=torch.float32, device=d0)
-    for which, pk, sc in (("up", pu, su), ("down", pdn, sdn)):
-        say(f"moe: quantize+pack 128 {which} matrices on the GPU")
-        for e0 in range(0, E, 16):
-            mats = workloads.moe_experts_parallel(which, range(e0, e0 + 16), workers=16)
-            for j, m in enumerate(mats):
-                s_, c_, _ = qt.qt_quantize_g64(dev(m), want_grid_idx=False)
-                sc[e0 + j].copy_(s_)
-                qt.qt_pack_i3(c_, pk[e0 + j])
-            torch.cuda.synchronize()
-    Xm, top = workloads.moe_tokens()
-    tok, exp, offs = workloads.route_pairs(top, E)
-    P = tok.size
-    say(f"moe: grouped up P={P}, experts hit {int(np.count_nonzero(np.diff(offs)))}")
-    h = qt.qt_matvec_i3_grouped(pu, su, E, Ou, Iu, dev(Xm), dev(offs), P, pair_row=dev(tok))
+    ref = {"up": {}, "down": {}}  # the oracle's bytes of the experts that pairs hit
+    with ThreadPoolExecutor(THREADS) as ex:
+        for which, pk, sc in (("up", pu, su), ("down", pdn, sdn)):
+            say(f"moe: quantize+pack 128 {which} matrices on the GPU and in the oracle")
+            for e0 in range(0, E, 16):
+                mats = workloads.moe_experts_parallel(which, range(e0, e0 + 16), workers=16)
+                for j, m in enumerate(mats):
+                    s_, c_, _ = qt.qt_quantize_g64(dev(m), want_grid_idx=False)
+                    sc[e0 + j].copy_(s_)
+                    qt.qt_pack_i3(c_, pk[e0 + j])
+                refs = list(ex.map(oracle_quant_pack, mats))
+                del mats
+                for j, (so, po) in enumerate(refs):
+                    e = e0 + j
+                    assert np.array_equal(bits(host(sc[e])), bits(so)), f"{which} scales differ, expert {e}"
+                    assert np.array_equal(host(pk[e]), po), f"{which} packed bytes differ, expert {e}"
+                    if e in hit:
+                        ref[which][e] = (so, po)
+    say(f"moe: all 128 experts bit-exact (up and down); grouped up P={P}, "
+        f"experts hit {len(hit)}")
+    h = host(qt.qt_matvec_i3_grouped(pu, su, E, Ou, Iu, dev(Xm), dev(offs), P, pair_row=dev(tok)))
     H = workloads.generic_matrix(P, Id, seed=4321)
     say("moe: grouped down on an independent input")
-    yd = qt.qt_matvec_i3_grouped(pdn, sdn, E, Od, Id, dev(H), dev(offs), P)
-    h, yd = host(h), host(yd)
-    rng = workloads.rng_for("generic", 9002)
-    sample = rng.choice(P, size=16, replace=False)
-    worst_u = worst_d = 0.0
-    for p in sample:
+    yd = host(qt.qt_matvec_i3_grouped(pdn, sdn, E, Od, Id, dev(H), dev(offs), P))
+
+    def pair_err(p):
         e, t = int(exp[p]), int(tok[p])
-        so, co, _ = oracle.quantize_g64(workloads.moe_expert(e, "up"))
-        po = oracle.pack_i3(co)
-        assert np.array_equal(host(pu[e]), po) and np.array_equal(bits(host(su[e])), bits(so))
+        so, po = ref["up"][e]
         yr, ar = oracle.matvec_f64(po, so, Ou, Iu, Xm[t])
-        worst_u = max(worst_u, componentwise_err(h[p], yr, ar))
-        so, co, _ = oracle.quantize_g64(workloads.moe_expert(e, "down"))
-        po = oracle.pack_i3(co)
+        eu = componentwise_err(h[p], yr, ar)
+        so, po = ref["down"][e]
         yr, ar = oracle.matvec_f64(po, so, Od, Id, H[p])
-        worst_d = max(worst_d, componentwise_err(yd[p], yr, ar))
-    say(f"  sampled componentwise err up {worst_u:.3e} down {worst_d:.3e}")
+        return eu, componentwise_err(yd[p], yr, ar)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        errs = list(ex.map(pair_err, range(P)))
+    worst_u = max(e[0] for e in errs)
+    worst_d = max(e[1] for e in errs)
+    say(f"  all {P} pairs: componentwise err up {worst_u:.3e} down {worst_d:.3e}")
     assert worst_u <= TOL_F32 and worst_d <= TOL_F32
 
 
-def test_search_and_hessian_full_size_sampled():
+def test_search_and_hessian_full_size():
     O, I = workloads.SEARCH_SHAPE
     say(f"search: X[{workloads.SEARCH_TOKENS}x{I}] Hessian diagonal")
     X = workloads.search_x()
@@ -122,19 +159,34 @@ def test_search_and_hessian_full_size_sampled():
     W = workloads.search_w()
     s, c, k = qt.qt_quantize_g64(dev(W), dev(d), 64, 0.5, 1.0)
     s, c, k = host(s), host(c), host(k)
-    rng = workloads.rng_for("generic", 9003)
-    rows = np.sort(rng.choice(O, size=12, replace=False))
-    so, co, ko = oracle.quantize_g64(W[rows], d, 64, 0.5, 1.0)
-    assert np.array_equal(bits(s[rows]), bits(so)), "scales differ"
-    assert np.array_equal(c[rows], co), "codes differ"
-    assert np.array_equal(k[rows], ko), "grid indices differ"
-    say(f"  {rows.size} sampled rows bit-exact; grid index histogram head "
+    slabs = [slice(r, min(r + 64, O)) for r in range(0, O, 64)]
+    say(f"search: oracle over all {O} rows on {THREADS} threads")
+
+    def check(rows):
+        so, co, ko = oracle.quantize_g64(W[rows], d, 64, 0.5, 1.0)
+        return (np.array_equal(bits(s[rows]), bits(so)), np.array_equal(c[rows], co),
+                np.array_equal(k[rows], ko))
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        res = list(ex.map(check, slabs))
+    for i, (a, b, g) in enumerate(res):
+        assert a, f"scales differ in rows {slabs[i]}"
+        assert b, f"codes differ in rows {slabs[i]}"
+        assert g, f"grid indices differ in rows {slabs[i]}"
+    say(f"  all {O} rows bit-exact; grid index histogram head "
         f"{np.bincount(k.reshape(-1), minlength=64)[:4]}")
+    del c
     say(f"search: W[{O}x{I}] two-stage signed 64/32 weighted search on the GPU")
     s2, c2 = qt.qt_quantize_g64_signed(dev(W), dev(d), 64, 32, 0.5, 1.0)
     s2, c2 = host(s2), host(c2)
-    rows = np.sort(rng.choice(O, size=6, replace=False))
-    so2, co2 = oracle.quantize_g64_signed(W[rows], d, 64, 32, 0.5, 1.0)
-    assert np.array_equal(bits(s2[rows]), bits(so2)), "signed scales differ"
-    assert np.array_equal(c2[rows], co2), "signed codes differ"
-    say(f"  {rows.size} sampled rows bit-exact; negative scales {np.mean(s2 < 0):.3f}")
+
+    def check2(rows):
+        so2, co2 = oracle.quantize_g64_signed(W[rows], d, 64, 32, 0.5, 1.0)
+        return np.array_equal(bits(s2[rows]), bits(so2)), np.array_equal(c2[rows], co2)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        res = list(ex.map(check2, slabs))
+    for i, (a, b) in enumerate(res):
+        assert a, f"signed scales differ in rows {slabs[i]}"
+        assert b, f"signed codes differ in rows {slabs[i]}"
+    say(f"  all {O} rows bit-exact; negative scales {np.mean(s2 < 0):.3f}")

@@ -64,9 +64,25 @@ def test_gptq_factor(I, damp):
     U, info = host(Ud), host(info)
     assert info[0] == 0
     Uref = oracle.gptq_factor(H.astype(np.float64), damp)
-    err = np.abs(U.astype(np.float64) - Uref).max() / np.abs(Uref).max()
-    say(f"  max err / max |U| {err:.3e}")
-    assert err <= 1e-6
+    check_factor_elementwise(U, Uref)
+
+
+def check_factor_elementwise(U, Uref):
+    """Every element of the f32 factor against the f64 oracle: within one
+    f32 rounding of its own magnitude (2^-24 |U_ij|) plus an f64-level term of
+    the factor's scale, n 2^-52 kappa max|U| with kappa the condition number
+    of the damped matrix, taken here as 1e6 (the tests' damped Hessians are
+    far better conditioned)."""
+    n = U.shape[0]
+    Uf = U.astype(np.float64)
+    diff = np.abs(Uf - Uref)
+    big = np.abs(Uref).max()
+    bound = 2.0 ** -24 * np.abs(Uref) + n * 2.0 ** -52 * 1e6 * big
+    rounded = np.mean(Uf == Uref.astype(np.float32).astype(np.float64))
+    ratio = float(np.max(diff / bound))
+    say(f"  elementwise: max err / bound {ratio:.3f}, exactly the rounded f64 value "
+        f"{100 * rounded:.2f}%, normwise {diff.max() / big:.2e}")
+    assert ratio <= 1.0
     assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
 
 
@@ -81,10 +97,7 @@ def test_gptq_factor_several_outer_panels(I):
     U, info = host(Ud), host(info)
     assert info[0] == 0
     Uref = oracle.gptq_factor(H.astype(np.float64), 0.01)
-    err = np.abs(U.astype(np.float64) - Uref).max() / np.abs(Uref).max()
-    say(f"  max err / max |U| {err:.3e}")
-    assert err <= 1e-6
-    assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
+    check_factor_elementwise(U, Uref)
 
 
 def test_gptq_factor_calls_on_two_streams():
@@ -143,16 +156,37 @@ def test_gptq_sweep_one_block_is_bit_exact(O, I):
     assert np.array_equal(c, co), "codes differ"
 
 
-def _replay_valid(W, U, s, c, tol=1e-3):
+# Slack of the replay check.  The GPU sweep runs in f32 and propagates each
+# finished 128-column block with an f32 matrix product; the oracle's replay
+# follows the GPU's codes in f64.  The two differ by the f32 rounding of the
+# propagated values, which grows with the number of columns propagated
+# (measured: scale differences up to 3.5e-6 relative at I = 1300, every code
+# margin exact).  The check allows 2e-5 on scales and 1e-5 of a quantization
+# step on codes (was 1e-3 on both).
+SCALE_RTOL = 2e-5
+CODE_SLACK = 1e-5
+
+
+def _replay_valid(W, U, s, c):
     wt, base = oracle.gptq_replay(W, U, s, c)
     I = W.shape[1]
-    assert np.allclose(s, base, rtol=1e-3, atol=1e-30), "scales are not the group bases"
+    pos = base > 0
+    srel = float(np.max(np.abs(s[pos] - base[pos]) / base[pos])) if np.any(pos) else 0.0
     sf = np.repeat(s.astype(np.float64), 64, axis=1)[:, :I]
     y = np.where(sf > 0, wt / np.where(sf > 0, sf, 1), 0)
     cf = c.astype(np.float64)
     inner = (cf > -4) & (cf < 3)
-    assert np.all(np.abs(y - cf)[inner] <= 0.5 + tol)
-    assert np.all(y[cf == 3] >= 2.5 - tol) and np.all(y[cf == -4] <= -3.5 + tol)
+    excess = 0.0
+    if np.any(inner):
+        excess = max(excess, float(np.max(np.abs(y - cf)[inner])) - 0.5)
+    if np.any(cf == 3):
+        excess = max(excess, 2.5 - float(np.min(y[cf == 3])))
+    if np.any(cf == -4):
+        excess = max(excess, float(np.max(y[cf == -4])) + 3.5)
+    say(f"  replay: scale rel diff {srel:.2e}, code margin excess {excess:.2e}")
+    assert np.all(s[~pos] == 0), "a zero group has a nonzero scale"
+    assert srel <= SCALE_RTOL, "scales are not the group bases"
+    assert excess <= CODE_SLACK, "a code does not round its replayed value"
 
 
 @pytest.mark.parametrize("O,I", [(64, 256), (40, 333), (100, 1000), (3, 129), (70, 1300)])

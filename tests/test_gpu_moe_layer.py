@@ -111,3 +111,62 @@ def test_moe_layer_routing_ties_and_idle_experts():
     logits[2] = np.arange(E, dtype=np.float32)[::-1]
     logits[3, 7] = 2.0
     check(X, logits, k, gate, up, down, "ties")
+
+
+def test_moe_layer_full_size_sampled():
+    # the benched shape: 128 experts of gate/up [2048x7168] and down
+    # [7168x2048], int3-g64 everywhere, 32 tokens, top-8 of uniform logits.
+    # Every expert's bytes and scales are checked against the oracle's; six
+    # tokens' outputs against the oracle's f64 layer within the error budget.
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    E, T, k = workloads.MOE_EXPERTS, workloads.MOE_TOKENS, workloads.MOE_TOPK
+    F, D = workloads.MOE_UP_SHAPE
+    threads = min(16, os.cpu_count() or 1)
+    X, _ = workloads.moe_tokens()
+    logits = workloads.moe_logits().astype(np.float32)
+    rng = workloads.rng_for("generic", 9004)
+    tokens = sorted(int(t) for t in rng.choice(T, size=6, replace=False))
+    used = set(int(e) for e in oracle.moe_route(logits, k)[0][tokens].reshape(-1))
+    shapes = {"gate": (F, D), "up": (F, D), "down": (D, F)}
+    dev_mats, keep = {}, {e: {} for e in used}
+
+    def oq(m):
+        s, c, _ = oracle.quantize_g64(m)
+        return s, oracle.pack_i3(c)
+
+    with ThreadPoolExecutor(threads) as ex:
+        for proj in ("gate", "up", "down"):
+            O, I = shapes[proj]
+            pk = torch.empty((E, qt.qt_packed_bytes(O, I)), dtype=torch.uint8, device="cuda:0")
+            sc = torch.empty((E, O, qt.qt_groups(I)), dtype=torch.float32, device="cuda:0")
+            say(f"moe layer full size: quantize+pack 128 {proj} matrices (GPU and oracle)")
+            for e0 in range(0, E, 16):
+                mats = workloads.moe_experts_parallel(proj, range(e0, e0 + 16), workers=16)
+                for j, m in enumerate(mats):
+                    s_, c_, _ = qt.qt_quantize_g64(dev(m), want_grid_idx=False)
+                    sc[e0 + j].copy_(s_)
+                    qt.qt_pack_i3(c_, pk[e0 + j])
+                refs = list(ex.map(oq, mats))
+                del mats
+                for j, (so, po) in enumerate(refs):
+                    e = e0 + j
+                    assert np.array_equal(fbits(host(sc[e])), fbits(so)), f"{proj} scales, expert {e}"
+                    assert np.array_equal(host(pk[e]), po), f"{proj} bytes, expert {e}"
+                    if e in used:
+                        keep[e][proj] = (po, so, 3)
+            dev_mats[proj] = (pk, sc, 3)
+    say(f"moe layer full size: E={E} T={T} k={k}, sampled tokens {tokens}")
+    out = host(qt.qt_moe_layer(dev(X), dev(logits), k, dev_mats["gate"], dev_mats["up"],
+                               dev_mats["down"]))
+    out2 = host(qt.qt_moe_layer(dev(X), dev(logits), k, dev_mats["gate"], dev_mats["up"],
+                                dev_mats["down"]))
+    assert np.array_equal(fbits(out), fbits(out2)), "not deterministic"
+
+    def expert(e):
+        return keep[e]["gate"], keep[e]["up"], keep[e]["down"]
+
+    ref, bound = oracle.moe_layer_f64_tokens(X, logits, k, expert, tokens)
+    err = np.max(np.abs(out[tokens] - ref) / bound)
+    say(f"  max error / budget {err:.3e} over {len(tokens)} tokens x {D} outputs")
+    assert err <= TOL

@@ -103,6 +103,25 @@ def test_search_bit_exact(n_grid, lo, hi, weighted):
     check_quantize(W, d, n_grid, lo, hi)
 
 
+def test_search_summation_order_group():
+    # the group of tests/golden/search_order.txt, on which a left-to-right sum
+    # of the objective picks another scale than the halving order; placed in
+    # several rows and in both the first and a later group of a row
+    from tests.test_oracle import read_search_order_fixture
+    w, d, n, lo, hi, k, scale, codes = read_search_order_fixture()
+    W = np.zeros((8, 192), np.float32)
+    dd = np.ones(192, np.float32)
+    for o in range(8):
+        g = o % 3
+        W[o, 64 * g:64 * g + 64] = w
+    for g in range(3):
+        dd[64 * g:64 * g + 64] = d
+    so, co, _, _ = check_quantize(W, dd, n, lo, hi)
+    for o in range(8):
+        g = o % 3
+        assert so[o, g] == scale and np.array_equal(co[o, 64 * g:64 * g + 64], codes)
+
+
 def check_signed(W, d, n1, n2, lo=0.5, hi=1.0):
     O, I = W.shape
     say(f"signed search O={O} I={I} n1={n1} n2={n2} weighted={d is not None}")

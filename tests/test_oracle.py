@@ -232,6 +232,42 @@ def test_search_worked_example_s():
                                      * np.linspace(0.5, 1.0, 64).astype(np.float32)[k[0, 0]])
 
 
+def read_search_order_fixture():
+    """The group of tests/golden/search_order.txt -> (w[64], d[64], n, lo, hi,
+    expected k, expected scale, expected codes[64])."""
+    w = np.zeros(64, np.float32)
+    d = np.ones(64, np.float32)
+    codes = np.zeros(64, np.int8)
+    for line in open(os.path.join(GOLDEN, "search_order.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        f = [t.strip() for t in line.split("|")]
+        if f[0] == "grid":
+            n, lo, hi = int(f[1]), float(f[2]), float(f[3])
+        elif f[0] == "slot":
+            w[int(f[1])] = np.float32(float(f[2]))
+            d[int(f[1])] = np.float32(float(f[3]))
+        elif f[0] == "expect":
+            k, scale = int(f[1]), np.float32(float(f[2]))
+            for item in f[3].split(","):
+                j, v = item.split(":")
+                codes[int(j)] = int(v)
+    return w, d, n, lo, hi, k, scale, codes
+
+
+def test_search_summation_order_worked_example():
+    # pins the halving order of the objective's sum (a left-to-right sum picks
+    # the other candidate on this group; derivation in the fixture)
+    w, d, n, lo, hi, k, scale, codes = read_search_order_fixture()
+    s, c, kk, errs = oracle.quantize_g64(w[None, :], d=d, n_grid=n, lo=lo, hi=hi,
+                                         return_errs=True)
+    assert errs[0, 0, 0] == np.float32(1.0 + 2.0 ** -23)
+    assert errs[0, 0, 1] == np.float32(1.0)
+    assert int(kk[0, 0]) == k and s[0, 0] == scale
+    assert np.array_equal(c[0], codes)
+
+
 # ---------------------------------------------------------------- signed two-stage search
 def _err_f64(w, d, s):
     """The objective for one scale in f64 (codes as the method decides them:
@@ -812,3 +848,28 @@ def test_dequant_f64_matches_matvec():
     y4, _ = oracle.matvec_i4_f64(p4, s4, 9, 200, x)
     assert np.allclose(oracle.dequant_f64(p4, s4, 9, 200, 4) @ x.astype(np.float64), y4,
                        rtol=1e-12)
+
+
+def test_moe_layer_token_rows_match_the_whole_layer():
+    # the memory-light form used at full size agrees with the whole-layer
+    # oracle (itself pinned by the closed forms above) on every row
+    E, F, D, T, k = 5, 64, 192, 6, 3
+    mats = []
+    for n, (O, I) in enumerate(((F, D), (F, D), (D, F))):
+        ps, ss = [], []
+        for e in range(E):
+            s, c, _ = oracle.quantize_g64(workloads.generic_weights(O, I, seed=7000 + 10 * n + e))
+            ps.append(oracle.pack_i3(c))
+            ss.append(s)
+        mats.append((np.stack(ps), np.stack(ss), 3))
+    X = workloads.generic_matrix(T, D, seed=71)
+    logits = workloads.rng_for("generic", 72, T, E).random((T, E)).astype(np.float32)
+    ref, bound = oracle.moe_layer_f64(X, logits, k, *mats)
+
+    def expert(e):
+        return tuple((m[0][e], m[1][e], m[2]) for m in mats)
+
+    rows = [4, 0, 5]
+    out, b2 = oracle.moe_layer_f64_tokens(X, logits, k, expert, rows)
+    assert np.allclose(out, ref[rows], rtol=1e-12, atol=1e-300)
+    assert np.allclose(b2, bound[rows], rtol=1e-12, atol=1e-300)
