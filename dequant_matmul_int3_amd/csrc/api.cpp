@@ -73,6 +73,7 @@ const char* qt_status_str(qt_status s) {
         case QT_ERR_ALIAS: return "an output overlaps an input";
         case QT_ERR_LAUNCH: return "kernel launch failed";
         case QT_ERR_WORKSPACE: return "workspace missing or too small";
+        case QT_ERR_SCRATCH: return "problem larger than the built-in scratch";
     }
     return "unknown status";
 }
@@ -107,6 +108,30 @@ qt_status qt_hessian_diag(const void* X, qt_dtype xt, int64_t T, int64_t I, floa
     return launched(qt::launch_hessian_diag(X, xt == QT_BF16, T, I, d, accumulate,
                                             static_cast<float*>(workspace), as_stream(stream)));
 }
+
+qt_status qt_hessian_diag_noalloc(const void* X, qt_dtype xt, int64_t T, int64_t I, float* d,
+                                  int accumulate, void* stream) {
+    if (!X || !d) return QT_ERR_NULL;
+    if (xt != QT_F32 && xt != QT_BF16) return QT_ERR_DTYPE;
+    if (T < 1 || I < 1 || I > QT_MAX_I) return QT_ERR_SHAPE;
+    const int64_t esz = xt == QT_F32 ? 4 : 2;
+    const int64_t xbytes = mul3(T, I, esz);
+    if (xbytes < 0) return QT_ERR_SHAPE;
+    if (accumulate != 0 && accumulate != 1) return QT_ERR_ARG;
+    if (!aligned(X, (uintptr_t)esz) || !aligned(d, 4)) return QT_ERR_ALIGN;
+    const size_t need = qt_hessian_workspace_bytes(T, I);
+    if (need > qt::kHessianScratchBytes) return QT_ERR_SCRATCH;
+    if (overlap(d, I * 4, X, xbytes)) return QT_ERR_ALIAS;
+    float* ws = nullptr;
+    if (need > 0) {
+        ws = static_cast<float*>(qt::hessian_scratch_ptr());
+        if (!ws) return QT_ERR_LAUNCH;
+    }
+    return launched(qt::launch_hessian_diag(X, xt == QT_BF16, T, I, d, accumulate, ws,
+                                            as_stream(stream)));
+}
+
+size_t qt_hessian_scratch_bytes(void) { return qt::kHessianScratchBytes; }
 
 namespace {
 

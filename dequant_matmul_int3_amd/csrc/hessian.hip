@@ -9,8 +9,15 @@
 // Stage 2 adds the slab partials along a fixed tree.  No atomics: the result
 // is independent of scheduling.
 #include <algorithm>
+#include <atomic>
 
 #include "qt_internal.h"
+
+// Scratch of the allocation-free entry point (slab partials): a file-scope
+// device array, so that callers that cannot allocate still get a fixed-order
+// reduction.  Each device holds its own copy until the process ends; calls
+// on one device share it.
+static __device__ __align__(256) float scratch[qt::kHessianScratchBytes / sizeof(float)];
 
 namespace qt {
 namespace {
@@ -152,6 +159,22 @@ hipError_t launch_hessian_diag(const void* X, bool bf16, int64_t T, int64_t I, f
     }
     if (aligned && I % 4 == 0) return run<4, false>(X, T, I, d, accumulate, workspace, slabs, s);
     return run<1, false>(X, T, I, d, accumulate, workspace, slabs, s);
+}
+
+// Device address of `scratch` on the current device, taken once per device
+// (the array's name in host code is only a stand-in, not a device address).
+// NULL if the runtime cannot give it.
+void* hessian_scratch_ptr() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    addr[dev].store(q, std::memory_order_release);  // two racing threads store the same address
+    return q;
 }
 
 }  // namespace qt

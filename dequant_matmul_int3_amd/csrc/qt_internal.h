@@ -78,6 +78,10 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
                             void* workspace, hipStream_t s);
 
 int hessian_slabs(int64_t T, int64_t I);
+// Bytes of the built-in scratch of qt_hessian_diag_noalloc, and its device
+// address on the current device (NULL on failure).
+constexpr size_t kHessianScratchBytes = size_t(16) << 20;
+void* hessian_scratch_ptr();
 hipError_t launch_hessian_diag(const void* X, bool bf16, int64_t T, int64_t I, float* d,
                                int accumulate, float* workspace, hipStream_t s);
 

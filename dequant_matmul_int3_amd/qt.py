@@ -26,6 +26,9 @@ _SIGS = {
     "qt_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
     "qt_hessian_diag": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_void_p,
                                   C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qt_hessian_diag_noalloc": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64,
+                                          C.c_void_p, C.c_int, C.c_void_p]),
+    "qt_hessian_scratch_bytes": (C.c_size_t, []),
     "qt_quantize_g64": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
                                   C.c_float, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p]),
@@ -154,6 +157,22 @@ def qt_hessian_diag(X, d=None, accumulate: bool = False, workspace=None, stream=
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qt_hessian_diag(_ptr(X), xt, T, I, _ptr(d), int(accumulate), _ptr(workspace),
                                  ws_bytes, _stream(stream, dev)), "qt_hessian_diag")
+    return d
+
+
+def qt_hessian_scratch_bytes() -> int:
+    return int(lib().qt_hessian_scratch_bytes())
+
+
+def qt_hessian_diag_noalloc(X, d=None, accumulate: bool = False, stream=None):
+    """qt_hessian_diag with the library's built-in scratch (no workspace)."""
+    T, I = X.shape
+    if d is None:
+        d = torch.zeros(I, dtype=torch.float32, device=X.device)
+    dev = _dev(X, d)
+    xt = QT_BF16 if X.dtype == torch.bfloat16 else QT_F32 if X.dtype == torch.float32 else -1
+    _check(lib().qt_hessian_diag_noalloc(_ptr(X), xt, T, I, _ptr(d), int(accumulate),
+                                         _stream(stream, dev)), "qt_hessian_diag_noalloc")
     return d
 
 

@@ -18,8 +18,10 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless stated otherwise; all tensors are
  *     contiguous and row-major; the caller owns every buffer.  The library
- *     never allocates or frees device memory and keeps no mutable global
- *     state, so calls are reentrant.
+ *     never allocates or frees device memory.  It keeps no mutable global
+ *     state, so calls are reentrant, with one exception stated at its
+ *     declaration: qt_hessian_diag_noalloc, whose scratch is a device array
+ *     shared by its calls on a device.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns before the work completes; results are
  *     valid once the caller has synchronised that stream.
@@ -52,7 +54,8 @@ typedef enum {
     QT_ERR_ARG = 5,       /* another argument is out of range                */
     QT_ERR_ALIAS = 6,     /* an output overlaps an input                     */
     QT_ERR_LAUNCH = 7,    /* the kernel launch failed                        */
-    QT_ERR_WORKSPACE = 8  /* workspace missing or too small                  */
+    QT_ERR_WORKSPACE = 8, /* workspace missing or too small                  */
+    QT_ERR_SCRATCH = 9    /* larger than the built-in scratch (_noalloc)     */
 } qt_status;
 
 typedef enum { QT_F32 = 0, QT_BF16 = 1 } qt_dtype;
@@ -86,6 +89,26 @@ size_t qt_hessian_workspace_bytes(int64_t T, int64_t I);
 qt_status qt_hessian_diag(const void* X, qt_dtype xt, int64_t T, int64_t I,
                           float* d, int accumulate, void* workspace,
                           size_t ws_bytes, void* stream);
+
+/*
+ * qt_hessian_diag for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments minus the workspace, same kernels and summation order, so
+ * the result is bit-identical to qt_hessian_diag's.  The slab partials live
+ * in a file-scope device array of qt_hessian_scratch_bytes() bytes (16 MiB)
+ * that each device holds until the process ends; its device address is
+ * taken once per device, with that device current, on the first call there
+ * (`stream` must belong to the current device).  Nothing is allocated or
+ * freed by any call.  Problems whose qt_hessian_workspace_bytes(T, I)
+ * exceeds that size return QT_ERR_SCRATCH with nothing enqueued (at the
+ * largest slab count, 128, that is I > 32768).  Every call on a device uses
+ * the same array: calls that overlap in time on one device (other streams,
+ * other threads) race on it and must be ordered by the caller.  The array
+ * needs no clearing: every partial is written before it is read.
+ */
+size_t qt_hessian_scratch_bytes(void);
+qt_status qt_hessian_diag_noalloc(const void* X, qt_dtype xt, int64_t T, int64_t I,
+                                  float* d, int accumulate, void* stream);
 
 /*
  * Per-group scale choice and code emission (pull request page, "Why this

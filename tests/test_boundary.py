@@ -215,3 +215,19 @@ P1, S1, P2, S2, P3, S3 = (0x7F4000000000, 0x7F5000000000, 0x7F6000000000, 0x7F70
                           0x7F8000000000, 0x7F9000000000)
 D_OUT = 0x7FA000000000
 WS = 0x7FB000000000
+
+
+def test_hessian_noalloc_rejects():
+    f = L.qt_hessian_diag_noalloc
+    QT_ERR_SCRATCH = 9
+    assert qt.qt_hessian_scratch_bytes() == 16 << 20
+    assert f(None, 0, 100, 64, B, 0, None) == QT_ERR_NULL
+    assert f(A, 2, 100, 64, B, 0, None) == QT_ERR_DTYPE
+    assert f(A, 0, 0, 64, B, 0, None) == QT_ERR_SHAPE
+    assert f(A, 0, 100, 64, B, 2, None) == QT_ERR_ARG
+    assert f(A + 2, 0, 100, 64, B, 0, None) == QT_ERR_ALIGN
+    assert f(A, 0, 100, 64, A + 4, 0, None) == QT_ERR_ALIAS
+    # 128 slabs x 32769 columns x 4 bytes is past the 16 MiB scratch; 32768 fits
+    assert qt.qt_hessian_workspace_bytes(128 * 128, 32768) == 16 << 20
+    assert f(A, 0, 128 * 128, 32769, B, 0, None) == QT_ERR_SCRATCH
+    assert "scratch" in qt.qt_status_str(QT_ERR_SCRATCH)
