@@ -36,38 +36,40 @@ struct Geo {
     static_assert(kWPieces % kThreads == 0, "weight chunk split");
 };
 
-// bf16 bit patterns of v = u - 4 for four codes u (one per byte), as the pairs
-// [c0 | c1 << 16] and [c2 | c3 << 16].  bf16(v) for v = -4..3 is c080 c040 c000
-// bf80 0000 3f80 4000 4040: one table gives the high bytes, one the low bytes.
-__device__ __forceinline__ void to_bf16_pairs(uint32_t W4, uint32_t& d0, uint32_t& d1) {
-    const uint32_t hi = __builtin_amdgcn_perm(0x40403F00u, 0xBFC0C0C0u, W4);
-    const uint32_t lo = __builtin_amdgcn_perm(0x40008000u, 0x80004080u, W4);
-    d0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-    d1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-}
-
-// One 16-code quarter: low-plane word L (code 4b+i at bits 8b+2i) and its 16
-// high bits h16 (code j at bit j) -> bf16 codes in the k order the int3 tile
-// stages its inputs in: lo8 holds codes 0 4 1 5 2 6 3 7 and hi8 codes 8 12 9
-// 13 10 14 11 15 of the quarter.  A dot product does not depend on the order
-// of its terms' positions, only on both operands using the same one; this
-// order saves the four byte permutes that natural order needs.
-__device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t h16, u32x4_t& lo8,
-                                                       u32x4_t& hi8) {
-    uint32_t sp = (h16 | (h16 << 8)) & 0x00FF00FFu;
-    sp = ((sp | (sp << 4)) & 0x0F0F0F0Fu) << 2;  // code 4b+i's high bit at bit 2+i of byte b
-    const uint32_t u0 = (L & 0x03030303u) | (sp & 0x04040404u);
-    const uint32_t u1 = ((L >> 2) & 0x03030303u) | ((sp >> 1) & 0x04040404u);
-    const uint32_t u2 = ((L >> 4) & 0x03030303u) | ((sp >> 2) & 0x04040404u);
-    const uint32_t u3 = ((L >> 6) & 0x03030303u) | ((sp >> 3) & 0x04040404u);
-    // byte b of u_i is code 4b+i: pairs (i, 4+i) and (8+i, 12+i)
-    uint32_t p0, p1, p2, p3, q0, q1, q2, q3;
-    to_bf16_pairs(u0, p0, q0);
-    to_bf16_pairs(u1, p1, q1);
-    to_bf16_pairs(u2, p2, q2);
-    to_bf16_pairs(u3, p3, q3);
-    lo8 = u32x4_t{p0, p1, p2, p3};
-    hi8 = u32x4_t{q0, q1, q2, q3};
+// One 16-code quarter: low-plane word L (code 4b+i at bits 8b+2i) and the
+// 32-bit high-plane word hw holding its 16 high bits (bytes 0-1 or 2-3, as
+// hsel selects: code j at bit j) -> its codes v as bf16, in the k order the
+// int3 tile stages its inputs in: lo8 holds codes 0 4 1 5 2 6 3 7 and hi8
+// codes 8 12 9 13 10 14 11 15 of the quarter (a dot product does not depend
+// on the order of its terms, only on both operands using the same one).
+//   * one byte permute puts the quarter's two high bytes in bytes 0 and 2,
+//     and one shift-or spreads nibble b to byte b: bit i of byte b is then
+//     the high bit of code 4b+i;
+//   * u_i = ((L >> 2i) & 3) | (high bit << 2) per byte is u = v + 4 of code
+//     4b+i in byte b;
+//   * a byte-permute table maps each u to the FP8 (E4M3) encoding of v/256:
+//     sign and magnitude, |v| <= 3 as the subnormal 2|v| * 2^-9 and -4 as the
+//     smallest normal 2^-6 (bytes 88 86 84 82 00 02 04 06 for u = 0..7);
+//   * the conversion of two FP8 bytes to bf16 with the scale 2^8 gives
+//     bf16(v) exactly, two codes per instruction.
+__device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t hw, uint32_t hsel,
+                                                u32x4_t& lo8, u32x4_t& hi8) {
+    const uint32_t b = __builtin_amdgcn_perm(0u, hw, hsel);
+    const uint32_t t = (b | (b << 4)) & 0x0F0F0F0Fu;  // bit i of byte b: high bit of 4b+i
+    uint32_t f[4];
+    f[0] = (L & 0x03030303u) | ((t << 2) & 0x04040404u);
+    f[1] = ((L >> 2) & 0x03030303u) | ((t << 1) & 0x04040404u);
+    f[2] = ((L >> 4) & 0x03030303u) | (t & 0x04040404u);
+    f[3] = ((L >> 6) & 0x03030303u) | ((t >> 1) & 0x04040404u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __builtin_amdgcn_perm(0x06040200u, 0x82848688u, f[i]);
+    // byte b of f_i is code 4b+i: pairs (i, 4+i) from bytes 0-1, (8+i, 12+i)
+    // from bytes 2-3
+#define QT_CV(u, HI) \
+    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, 256.0f, HI))
+    lo8 = u32x4_t{QT_CV(f[0], false), QT_CV(f[1], false), QT_CV(f[2], false), QT_CV(f[3], false)};
+    hi8 = u32x4_t{QT_CV(f[0], true), QT_CV(f[1], true), QT_CV(f[2], true), QT_CV(f[3], true)};
+#undef QT_CV
 }
 
 // v/16 of the two's-complement nibble in the low four bits of byte B of t.
@@ -332,6 +334,8 @@ __device__ __forceinline__ void grouped_tile(
             if (c0 + kCG < G) load_chunk(c0 + kCG, nt, cur);
             const uint8_t* wrow = wl + (16 * wave + l16) * kWRow;
             const uint8_t* prow = pl + l16 * kPRow + 32 * j4;
+            // selector of the quarter's two high-plane bytes (int3)
+            const uint32_t hsel = (j4 & 1) ? 0x0c030c02u : 0x0c010c00u;
 #pragma unroll
             for (int g = 0; g < kCG; ++g) {
                 if (g >= gn) break;  // uniform
@@ -341,7 +345,7 @@ __device__ __forceinline__ void grouped_tile(
                         *reinterpret_cast<const uint32_t*>(wrow + g * kGB + 4 * j4);
                     const uint32_t hw = *reinterpret_cast<const uint32_t*>(
                         wrow + g * kGB + 16 + 4 * (j4 >> 1));
-                    dequant_quarter(lo, (hw >> (16 * (j4 & 1))) & 0xFFFFu, a0, a1);
+                    dequant_quarter(lo, hw, hsel, a0, a1);
                 } else {
                     // quarter j4 = codes 16 j4 .. 16 j4 + 15 = bytes 8 j4 .. 8 j4 + 7
                     const u32x2_t q = *reinterpret_cast<const u32x2_t*>(wrow + g * kGB + 8 * j4);
