@@ -6,8 +6,17 @@ Headline (one JSON line on stdout): the decode GEMV, W[2048x7168] int3-g64
 with f32 scales times x[7168] f32, batch 1.  A step is one dequantize-multiply
 of the whole matrix; consecutive steps read 64 distinct copies of the packed
 weights (64 x 6.46 MB = 413 MB, more than the 256 MB Infinity Cache), so every
-step streams its weights from HBM.  value = algorithmic bytes per step
-(packed weights + scales + x + y = 6,459,392 B) x steps / elapsed time.
+step streams its weights from HBM.  The 64 launches are captured in one HIP
+graph; each replay is timed by its own pair of events on the stream the
+kernels run on, and the reported time per launch is the median over the
+replays (p10 and p90 beside it).  value = algorithmic bytes per step (packed
+weights + scales + x + y = 6,459,392 B) / median time per launch.
+
+Beside the headline: the same multiply on the tail variant W[2048x7200] (113
+groups, the last one 32 wide), the same kernel over all 64 copies as one
+matrix in a single launch (O = 131072, 413 MB: the streaming rate without
+launch gaps), and a measured streaming-read peak (a device reduction over
+1 GiB) that the GEMV rates are also quoted against.
 
 The other rows of the hot path are timed as "legs" on their own workloads:
 the Hessian diagonal and the weighted scale search (W[5120x17408],
@@ -15,8 +24,10 @@ X[8192x17408]), plain quantize + pack at the decode shape, the grouped MoE
 GEMV (128 experts, 32 tokens, top-8) and the bf16 MFMA prefill GEMM
 (X[512x7168] x W[18432x7168]); grouped int4: the decode GEMV with int4
 weights and the MoE step with every projection at int4 and with up at int3
-(the per-projection mix).  Every input is seeded synthetic data
-(workloads.py) resident on the GPU before its timed region starts.
+(the per-projection mix); GPTQ and the MoE expert layer.  Every input is
+seeded synthetic data (workloads.py) resident on the GPU before its timed
+region starts.  The CPU oracle is timed beside the legs on bounded samples
+(bench_cpu.py), on one host thread and on N threads.
 """
 import argparse
 import hashlib
@@ -32,12 +43,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
-# Vector ALU: the published fp32 vector peak, 157.3 TFLOP/s, counts an FMA as
-# two operations: 78.65 T lane-operations/s.  (Single-issue non-packed f32
-# instructions measure 64 lanes/clock/CU = 39.3 T at 2.4 GHz; round-to-integer
-# issues beside them, so an op count can exceed that figure.)
-VALU_PEAK_TOPS = 157.3 / 2
+# Vector ALU: one non-packed f32 instruction per lane per 4 clocks per SIMD,
+# 64 lanes/clock/CU = 39.3 T lane-operations/s at 2.4 GHz (the published
+# 157.3 TFLOP/s fp32 vector peak counts a packed FMA as four).  Reciprocals
+# and round-to-integer issue on the transcendental unit beside the other
+# vector instructions, so an operation count can exceed this figure; the
+# search legs' roofline fraction is therefore the VALUBusy counter.
+VALU_SINGLE_TOPS = 256 * 64 * 2.4e9 / 1e12
 N_COPIES = 64
+MIN_REPLAYS = 8  # timed graph replays of the headline (>= 512 launches)
 
 
 def parse():
@@ -47,7 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--legs", default="all",
                     help="all, gemv (headline only) or a comma list of: " + ",".join(LEG_NAMES))
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="CPU-oracle time per baseline measurement (1 thread and N threads each)")
     ap.add_argument("--calib", action="store_true",
                     help="also run a 256 MiB device copy (reference for HBM traffic counters)")
     return ap.parse_args()
@@ -77,6 +92,18 @@ def traffic_for(name, bytes_alg):
     return rec.get("hbm_bytes_per_launch")
 
 
+def counters_for(name):
+    """Counter figures of a kernel from profiles/<name>_counters.json, if the
+    kernel source is unchanged since they were taken; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}_counters.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_sha") != sha_of(*rec.get("sources", [])):
+        return None
+    return rec
+
+
 def time_launches(fn, n, torch, warmup=2):
     """Average time per fn() call over n back-to-back calls, from a pair of
     events on the current stream (the stream the kernels run on), after
@@ -96,9 +123,17 @@ def time_launches(fn, n, torch, warmup=2):
 
 
 def graph_ms(fn, n_copies, warmup, steps, torch):
-    """Per-call time of fn(j), j = 0..n_copies-1, captured once in a HIP
-    graph and replayed until `steps` calls are timed (so that host-side call
-    overhead does not pace the GPU)."""
+    """Median per-call time of fn(j), j = 0..n_copies-1, captured once in a
+    HIP graph and replayed (so that host-side call overhead does not pace the
+    GPU); -> (ms per call, calls timed)."""
+    reps = max(MIN_REPLAYS, -(-steps // n_copies))
+    return graph_replays(fn, n_copies, warmup, reps, torch)["median"], reps * n_copies
+
+
+def graph_replays(fn, n_copies, warmup, reps, torch):
+    """Capture fn(0..n_copies-1) in one HIP graph on a side stream and time
+    `reps` replays, each between its own pair of events recorded on that
+    stream; -> {"median", "p10", "p90"} of the per-call time in ms."""
     cs = torch.cuda.Stream()
     with torch.cuda.stream(cs):
         for j in range(n_copies):
@@ -108,26 +143,19 @@ def graph_ms(fn, n_copies, warmup, steps, torch):
     with torch.cuda.graph(graph, stream=cs):
         for j in range(n_copies):
             fn(j)
-    for _ in range(max(1, -(-warmup // n_copies))):
-        graph.replay()
-    torch.cuda.synchronize()
-    reps = max(1, -(-steps // n_copies))
-    return time_launches(lambda i: graph.replay(), reps, torch) / n_copies, reps * n_copies
-
-
-def per_launch_ms(fn, n, torch):
-    """Mean and median of single fn() calls, each bracketed by its own events."""
-    st = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record(st)
-        fn(i)
-        b.record(st)
-    torch.cuda.synchronize()
-    d = np.array([a.elapsed_time(b) for a, b in evs])
-    return float(np.mean(d)), float(np.median(d))
+    with torch.cuda.stream(cs):
+        for _ in range(max(1, -(-warmup // n_copies))):
+            graph.replay()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record(cs)
+        for r in range(reps):
+            graph.replay()
+            evs[r + 1].record(cs)
+        torch.cuda.synchronize()
+    per = np.array([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)]) / n_copies
+    return {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
+            "p90": float(np.percentile(per, 90))}
 
 
 def main():
@@ -166,39 +194,78 @@ def main():
     def gemv(j):
         qt.qt_matvec_i3(packs[j], scs[j], O, I, xd, y)
 
-    # the launch loop is captured in a HIP graph (one launch per weight copy)
-    # so that host-side call overhead does not pace the GPU
-    log(f"decode GEMV: capture {N_COPIES} launches, warmup {args.warmup}, timed {args.steps} steps")
-    cs = torch.cuda.Stream()
-    with torch.cuda.stream(cs):
-        for j in range(N_COPIES):
-            gemv(j)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cs):
-        for j in range(N_COPIES):
-            gemv(j)
-    reps_w = max(1, -(-args.warmup // N_COPIES))
-    reps = max(1, -(-args.steps // N_COPIES))
+    reps = max(MIN_REPLAYS, -(-args.steps // N_COPIES))
+    log(f"decode GEMV: graph of {N_COPIES} launches, {reps} timed replays")
+    tm = graph_replays(gemv, N_COPIES, args.warmup, reps, torch)
     steps = reps * N_COPIES
-    for _ in range(reps_w):
-        graph.replay()
-    torch.cuda.synchronize()
-    ms_step = time_launches(lambda i: graph.replay(), reps, torch) / N_COPIES
+    ms_step = tm["median"]
     value = bytes_step / (ms_step * 1e-3) / 1e9
-    achieved = value
-    # eager single launches bracketed by their own events, for reference
-    kmean, kmed = per_launch_ms(lambda i: gemv(i % N_COPIES), 256, torch)
     tr = traffic_for("gemv_decode", bytes_step)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": tr, "kernel": "gemv_batch_kernel<128,16,1,128,f32,vec>",
-                "launch_us_mean": round(ms_step * 1e3, 3),
-                "eager_event_pair_us_mean": round(kmean * 1e3, 3),
+    roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
+                "traffic": tr, "kernel": "gemv_decode1_kernel<3>",
+                "launch_us_median": round(ms_step * 1e3, 3),
+                "launch_us_p10": round(tm["p10"] * 1e3, 3),
+                "launch_us_p90": round(tm["p90"] * 1e3, 3),
                 "bytes_per_launch": bytes_step}
-    log(f"  {ms_step * 1e3:.2f} us/launch back-to-back (graph) = {value:.0f} GB/s; "
-        f"eager event pair {kmean * 1e3:.2f} us")
-    del packs, scs
+    log(f"  {ms_step * 1e3:.3f} us/launch median (p10 {tm['p10'] * 1e3:.3f}, p90 "
+        f"{tm['p90'] * 1e3:.3f}) = {value:.0f} GB/s")
+
+    # the same kernel over the 64 copies as one matrix, one launch
+    Ostack = O * N_COPIES
+    ystack = torch.empty(Ostack, dtype=torch.float32, device=dev)
+    stack_bytes = packs.numel() + scs.numel() * 4 + I * 4 + Ostack * 4
+    for _ in range(3):
+        qt.qt_matvec_i3(packs.view(-1), scs.view(-1), Ostack, I, xd, ystack)
+    ms = time_launches(lambda i: qt.qt_matvec_i3(packs.view(-1), scs.view(-1), Ostack, I, xd,
+                                                 ystack), 20, torch)
+    gbs = stack_bytes / (ms * 1e-3) / 1e9
+    legs["gemv_stacked_one_launch"] = {
+        "us": round(ms * 1e3, 2), "GB_s": round(gbs, 1), "bound": "hbm",
+        "frac": round(gbs / HBM_PEAK_GBS, 4), "O": Ostack, "I": I,
+        "bytes_per_launch": int(stack_bytes), "traffic": traffic_for("gemv_stacked", stack_bytes)}
+    log(f"leg gemv_stacked_one_launch: {legs['gemv_stacked_one_launch']}")
+    del packs, scs, ystack
+
+    # tail variant: W[2048x7200], 113 groups, the last one 32 wide
+    Wt, xt = workloads.decode(tail=True)
+    Ot, It = Wt.shape
+    Gt = qt.qt_groups(It)
+    st, ct, _ = qt.qt_quantize_g64(torch.from_numpy(Wt).to(dev))
+    pt = qt.qt_pack_i3(ct)
+    xtd = torch.from_numpy(xt).to(dev)
+    packs_t = torch.empty((N_COPIES, pt.numel()), dtype=torch.uint8, device=dev)
+    scs_t = torch.empty((N_COPIES, Ot, Gt), dtype=torch.float32, device=dev)
+    packs_t.copy_(pt.expand(N_COPIES, -1))
+    scs_t.copy_(st.expand(N_COPIES, -1, -1))
+    yt = torch.empty(Ot, dtype=torch.float32, device=dev)
+    bytes_t = pt.numel() + st.numel() * 4 + It * 4 + Ot * 4
+    tmt = graph_replays(lambda j: qt.qt_matvec_i3(packs_t[j], scs_t[j], Ot, It, xtd, yt),
+                        N_COPIES, args.warmup, reps, torch)
+    gbs = bytes_t / (tmt["median"] * 1e-3) / 1e9
+    legs["gemv_decode_tail_7200"] = {
+        "us_median": round(tmt["median"] * 1e3, 3), "us_p10": round(tmt["p10"] * 1e3, 3),
+        "us_p90": round(tmt["p90"] * 1e3, 3), "GB_s": round(gbs, 1), "bound": "hbm",
+        "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": int(bytes_t),
+        "O": Ot, "I": It}
+    log(f"leg gemv_decode_tail_7200: {legs['gemv_decode_tail_7200']}")
+    del packs_t, scs_t
+
+    # measured streaming peak: a 1 GiB device-to-device copy (bytes read plus
+    # bytes written over its time) and a device sum over the same 1 GiB (bytes
+    # read); the larger is the streaming peak the GEMV rates are quoted against
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    big2 = torch.empty_like(big)
+    for _ in range(3):
+        big2.copy_(big)
+        big.sum()
+    ms_c = time_launches(lambda i: big2.copy_(big), 10, torch)
+    ms_s = time_launches(lambda i: big.sum(), 10, torch)
+    copy_gbs = 2 * big.numel() * 4 / (ms_c * 1e-3) / 1e9
+    sum_gbs = big.numel() * 4 / (ms_s * 1e-3) / 1e9
+    stream_peak = max(copy_gbs, sum_gbs)
+    del big, big2
+    log(f"streaming peak: 1 GiB copy {copy_gbs:.0f} GB/s (read + write), sum {sum_gbs:.0f} GB/s")
 
     if args.calib:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings
@@ -217,13 +284,17 @@ def main():
             raise SystemExit(f"unknown legs {sorted(unknown)}; choose from {LEG_NAMES}")
         legs.update(run_legs(torch, qt, workloads, dev, which, args))
 
-    cpu = cpu_baseline(W, x, args.cpu_seconds, bytes_step)
+    cpu = cpu_baselines(args.cpu_seconds, legs, W, x)
 
     line = {
         "metric": "int3-g64 GEMV effective HBM GB/s (% of peak) at I=7168; quantize groups/s",
         "value": round(value, 1),
         "unit": "GB/s",
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "pct_of_stream_peak": round(100 * value / stream_peak, 2),
+        "stream_peak_GB_s": round(stream_peak, 1),
+        "stream_probe_GB_s": {"copy_1GiB_read_plus_write": round(copy_gbs, 1),
+                              "sum_1GiB_read": round(sum_gbs, 1)},
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
@@ -237,6 +308,10 @@ def main():
                                "batch 1, 64 rotating weight copies",
                    "O": O, "I": I, "batch": 1, "rotating_copies": N_COPIES,
                    "bytes_per_step": bytes_step},
+        "timing": {"replays": reps, "launches_per_replay": N_COPIES,
+                   "per_launch_ms_median": round(ms_step, 6),
+                   "per_launch_ms_p10": round(tm["p10"], 6),
+                   "per_launch_ms_p90": round(tm["p90"], 6)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "legs": legs,
@@ -483,22 +558,31 @@ def search_leg(torch, qt, workloads, dev, legs):
     # per group: 64 candidates x 64 slots x 9 operations (divide, round, max,
     # min, multiply, subtract, multiply, multiply, add)
     ops = ngroups * 64 * 64 * 9
-    legs["quantize_search"] = {"ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)),
-                               "bound": "alu", "achieved_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
-                               "peak_Tops": round(VALU_PEAK_TOPS, 2),
-                               "frac": round(ops / (ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
-                               "op_count": "9 per slot per candidate (division as one)"}
+    cnt = counters_for("search")
+    legs["quantize_search"] = {
+        "ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)), "bound": "alu",
+        # the roofline fraction: the share of the kernel's cycles in which the
+        # vector ALUs issue (rocprofv3 VALUBusy of this kernel; None if the
+        # kernel changed since the counters were taken)
+        "frac": None if cnt is None else cnt["valu_busy"],
+        "frac_basis": "VALUBusy counter (cycles the vector ALUs issue / kernel cycles)",
+        "ops_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
+        "op_count": "9 per slot per candidate (division as one)",
+        "ops_over_single_issue_peak": round(ops / (ms * 1e-3) / 1e12 / VALU_SINGLE_TOPS, 4)}
     log(f"leg search: {legs['quantize_search']}")
     # two-stage signed search: 2 x 64 signed candidates, then 32 refinement points
     qt.qt_quantize_g64_signed(Wd, d, 64, 32, 0.5, 1.0, scales=s, codes=c)
     ms = time_launches(lambda i: qt.qt_quantize_g64_signed(Wd, d, 64, 32, 0.5, 1.0, scales=s,
                                                           codes=c), 3, torch)
     ops = ngroups * (2 * 64 + 32) * 64 * 9
-    legs["quantize_search_signed"] = {"ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)),
-                                      "bound": "alu", "achieved_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
-                                      "peak_Tops": round(VALU_PEAK_TOPS, 2),
-                                      "frac": round(ops / (ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
-                                      "candidates": "2 x 64 + 32 per group"}
+    cnt = counters_for("search_signed")
+    legs["quantize_search_signed"] = {
+        "ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)), "bound": "alu",
+        "frac": None if cnt is None else cnt["valu_busy"],
+        "frac_basis": "VALUBusy counter (cycles the vector ALUs issue / kernel cycles)",
+        "ops_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
+        "ops_over_single_issue_peak": round(ops / (ms * 1e-3) / 1e12 / VALU_SINGLE_TOPS, 4),
+        "candidates": "2 x 64 + 32 per group"}
     log(f"leg search signed: {legs['quantize_search_signed']}")
     del Wd, s, c, k, d
 
@@ -598,24 +682,143 @@ def prefill_leg(torch, qt, workloads, dev, legs):
     log(f"leg prefill: {legs['prefill_gemm']}")
 
 
-def cpu_baseline(W, x, seconds, bytes_step):
-    """The CPU oracle's fp64 dequantize-then-multiply of the same decode
-    matrix, repeated for about `seconds` on one host core."""
-    import oracle
+# ---------------------------------------------------------------- CPU oracle baselines
+def host_threads():
+    """Host threads for the CPU baselines: the cores this process may run on,
+    at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
-    O, I = W.shape
-    s, c, _ = oracle.quantize_g64(W)
-    p = oracle.pack_i3(c)
-    n = 0
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_rate(items, seconds, threads):
+    """items: callables, each one oracle call returning the units of work it
+    did.  Runs them round-robin for about `seconds` on `threads` host threads
+    (a ctypes call releases the interpreter lock, so the C oracle runs in
+    parallel) -> (units per second, calls made)."""
+    from concurrent.futures import ThreadPoolExecutor
+    done_units, calls = 0.0, 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        oracle.matvec_f64(p, s, O, I, x)
-        n += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(bytes_step * n / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+    if threads == 1:
+        while True:
+            done_units += items[calls % len(items)]()
+            calls += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            while True:
+                batch = [items[(calls + k) % len(items)] for k in range(threads)]
+                done_units += sum(ex.map(lambda f: f(), batch))
+                calls += threads
+                if time.perf_counter() - t0 >= seconds:
+                    break
+    return done_units / (time.perf_counter() - t0), calls
+
+
+def cpu_baselines(seconds, legs, Wdec, xdec):
+    """The oracle (plain scalar C, built -O2 without fast-math, never tuned for
+    speed) timed on bounded samples of the legs' workloads, on one host thread
+    and on N; each figure is attached to its leg as "cpu_oracle" and the
+    decode matvec is the line's cpu_baseline."""
+    import oracle
+    import workloads
+    n = host_threads()
+    out = {}
+
+    def measure(name, items, unit, sample):
+        r1, c1 = oracle_rate(items, seconds, 1)
+        rn, cn = oracle_rate(items, seconds, n)
+        out[name] = {"unit": unit, "single_thread": round(r1, 4), "threads": n,
+                     "all_threads": round(rn, 4), "sample": sample}
+        log(f"cpu oracle {name}: 1 thread {r1:.4g}, {n} threads {rn:.4g} {unit}")
+
+    O, I = Wdec.shape
+    G = -(-I // 64)
+    rows = 128
+    slabs = []
+    for r0 in range(0, O, rows):
+        so, co, _ = oracle.quantize_g64(Wdec[r0:r0 + rows])
+        slabs.append((so, co, oracle.pack_i3(co), Wdec[r0:r0 + rows]))
+    per_row = G * 28  # packed + scale bytes of a row
+    measure("matvec_decode",
+            [lambda sl=sl: (oracle.matvec_f64(sl[2], sl[0], rows, I, xdec),
+                            rows * per_row + I * 4 + rows * 4)[1] for sl in slabs],
+            "bytes_per_s", f"fp64 dequantize-then-multiply of 128-row slabs of W[{O}x{I}]")
+    measure("quantize_rtn_decode",
+            [lambda sl=sl: (oracle.quantize_g64(sl[3]), rows * G)[1] for sl in slabs],
+            "groups_per_s", f"plain absmax/4 quantize of 128-row slabs of W[{O}x{I}]")
+    measure("pack_decode",
+            [lambda sl=sl: (oracle.pack_i3(sl[1]), rows * I + rows * G * 24)[1] for sl in slabs],
+            "bytes_per_s", f"bit-plane pack of 128-row slabs of the codes of W[{O}x{I}]")
+    # weighted search on rows of the search matrix (importance d drawn lognormal)
+    Os, Is = workloads.SEARCH_SHAPE
+    Gs = -(-Is // 64)
+    Ws = workloads.generic_weights(32, Is, seed=31)
+    d = np.exp(workloads.generic_vector(Is, seed=32)).astype(np.float32)
+    measure("quantize_search",
+            [lambda k=k: (oracle.quantize_g64(Ws[4 * k:4 * k + 4], d, 64, 0.5, 1.0), 4 * Gs)[1]
+             for k in range(8)],
+            "groups_per_s", f"64-point weighted search of 4-row slabs of [x{Is}] rows")
+    measure("quantize_search_signed",
+            [lambda k=k: (oracle.quantize_g64_signed(Ws[2 * k:2 * k + 2], d, 64, 32, 0.5, 1.0),
+                          2 * Gs)[1] for k in range(16)],
+            "groups_per_s", f"two-stage signed 64/32 search of 2-row slabs of [x{Is}] rows")
+    Xh = workloads.generic_matrix(512, Is, seed=33)
+    measure("hessian_diag",
+            [lambda k=k: (oracle.hessian_diag(Xh[64 * k:64 * k + 64]), 64 * Is * 4)[1]
+             for k in range(8)],
+            "bytes_per_s", f"f64 column sums of squares over 64-token slabs of X[.x{Is}]")
+    # grouped MoE: per-pair matvecs of two experts (up and down)
+    mats = []
+    for e in range(2):
+        for which in ("up", "down"):
+            m = workloads.moe_expert(e, which)
+            so, co, _ = oracle.quantize_g64(m)
+            mats.append((oracle.pack_i3(co), so, m.shape[0], m.shape[1]))
+    xs = {k: workloads.generic_vector(k, seed=k) for k in (7168, 2048)}
+    measure("moe_grouped",
+            [lambda mt=mt: (oracle.matvec_f64(mt[0], mt[1], mt[2], mt[3], xs[mt[3]]),
+                            mt[0].size + mt[1].size * 4)[1] for mt in mats],
+            "bytes_per_s", "fp64 (token, expert) matvecs of the up and down matrices of two experts")
+    # prefill: sampled outputs of one 1024-row slab
+    Op, Ip = workloads.PREFILL_SHAPE
+    sp, cp, _ = oracle.quantize_g64(workloads.prefill_w([0]))
+    pp = oracle.pack_i3(cp)
+    Xp = workloads.bf16_bits_to_f32(workloads.prefill_x()[:64])
+    rng = workloads.rng_for("generic", 9100)
+    samples = [(rng.integers(0, 64, size=256), rng.integers(0, 1024, size=256)) for _ in range(8)]
+    measure("prefill_gemm",
+            [lambda sm=sm: (oracle.matmul_f64_sampled(pp, sp, 1024, Ip, Xp, sm[0], sm[1]),
+                            2.0 * Ip * sm[0].size)[1] for sm in samples],
+            "flop_per_s", f"fp64 sampled outputs (256 per call) of a 1024-row slab of W[{Op}x{Ip}]")
+    # attach to the legs that ran
+    for leg, key in (("quantize_rtn_decode", "quantize_rtn_decode"), ("pack_decode", "pack_decode"),
+                     ("quantize_search", "quantize_search"),
+                     ("quantize_search_signed", "quantize_search_signed"),
+                     ("hessian_diag", "hessian_diag"), ("moe_grouped", "moe_grouped"),
+                     ("prefill_gemm", "prefill_gemm")):
+        if leg in legs:
+            legs[leg]["cpu_oracle"] = out[key]
+    m = out["matvec_decode"]
+    return {"value": round(m["all_threads"] / 1e9, 3), "unit": "GB/s", "cores": n,
             "kind": "oracle",
-            "sample": f"{n} fp64 dequantize-then-multiply passes over the decode matrix "
-                      f"W[{O}x{I}] ({dt:.1f} s, single thread)"}
+            "sample": f"fp64 dequantize-then-multiply of 128-row slabs of the decode matrix "
+                      f"W[{O}x{I}] for about {seconds:.1f} s on {n} host threads",
+            "single_thread_GB_s": round(m["single_thread"] / 1e9, 3),
+            "cpu_model": cpu_model(), "legs": out}
 
 
 if __name__ == "__main__":

@@ -503,9 +503,10 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
     const float* xg[NG][1];
 #pragma unroll
     for (int m = 0; m < NG; ++m) xg[m][0] = dec_group(xs, q + 128 * m < G ? q + 128 * m : 0);
-    // several tiles, one group per lane: its 64 inputs are read into registers
-    // once and serve every tile of the block (read after the first tile's
-    // weight loads are issued, so the LDS reads do not wait for the weights)
+    // one group per lane: its 64 inputs are read into registers once and serve
+    // every tile of the block (read after the first tile's weight loads are
+    // issued, so the LDS reads do not wait for the weights; reading them inside
+    // the arithmetic instead measured 0.4 us slower per decode launch)
     float xr[NG == 1 ? kGroup : 1];
     const float* xrp[1] = {xr};
     auto read_x = [&]() {
@@ -537,7 +538,7 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
     auto mul_tile = [&](int tile, int it, const GroupBits<BITS> (&gb)[NG], const float (&sc)[NG]) {
         const int r = tile * kDecRows + rl;
         float rowacc[1] = {0.0f};
-        if constexpr (NG == 1 && LOOP) {
+        if constexpr (NG == 1) {
             if (r < O && q < G) group_dot<1, 1, BITS>(gb[0], sc[0], xrp, rowacc);
         } else {
 #pragma unroll
@@ -554,9 +555,8 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
     GroupBits<BITS> cur[NG];
     float cs[NG];
     if constexpr (!LOOP) {
-        // one tile: the inputs are read from LDS inside the arithmetic (the
-        // compiler issues those reads ahead of the weights' arrival)
         load_tile(blockIdx.x, cur, cs);
+        read_x();
         mul_tile(blockIdx.x, 0, cur, cs);
     } else {
         GroupBits<BITS> nxt[NG];
@@ -576,6 +576,48 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
     }
 }
 
+// One 8-row tile per block, G <= 128: the plainest form of the decode kernel
+// (x copied into LDS, then each lane's weight loads and its group's dot
+// product read straight from LDS), which measured fastest for one tile.
+template <int BITS>
+__global__ __launch_bounds__(1024) void gemv_decode1_kernel(
+    const uint8_t* __restrict__ packed, const float* __restrict__ scales, int O, int I, int G,
+    const float* __restrict__ x, float* __restrict__ y) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    typedef __attribute__((address_space(1))) void glob_void;
+    extern __shared__ __attribute__((aligned(16))) float xs[];
+    __shared__ float part[16];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int q = tid & 127;
+    const int r = blockIdx.x * kDecRows + (tid >> 7);
+    const int nruns = (G + 3) / 4;
+    for (int c = w; c < nruns; c += 16) {
+        const int pc = c * 64 + lane;
+        char* base = reinterpret_cast<char*>(xs) + c * kDecChunk;
+        if (4 * pc < I)
+            __builtin_amdgcn_global_load_lds((const glob_void*)(x + 4 * pc), (lds_void*)base, 16, 0,
+                                             0);
+        else if (pc < 16 * G)
+            *reinterpret_cast<float4*>(base + 16 * lane) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    float acc = 0.0f;
+    if (q < G && r < O) {
+        const int64_t gi = (int64_t)r * G + q;
+        const GroupBits<BITS> gb = load_group<BITS>(packed + gi * GroupBits<BITS>::kBytes);
+        const float sc = scales[gi];
+        const float* xg[1] = {dec_group(xs, q)};
+        float ra[1] = {0.0f};
+        group_dot<1, 1, BITS>(gb, sc, xg, ra);
+        acc = ra[0];
+    }
+    acc = lane_group_sum<64>(acc);
+    if (lane == 0) part[w] = acc;
+    __syncthreads();
+    if (q == 0 && r < O) y[r] = part[w] + part[w + 1];
+}
+
 template <int BITS>
 static hipError_t run_decode(const uint8_t* packed, const float* scales, int64_t O, int64_t I,
                              const float* x, float* y, hipStream_t s) {
@@ -589,8 +631,11 @@ static hipError_t run_decode(const uint8_t* packed, const float* scales, int64_t
     hipLaunchKernelGGL((gemv_decode_kernel<BITS, NG, LOOP>), grid, block, lds, s, packed, \
                        scales, (int)O, (int)I, G, x, y, ntiles)
     if (G <= 128) {
-        if (ntiles <= blocks) QT_DEC(1, false);
-        else QT_DEC(1, true);
+        if (ntiles <= blocks)
+            hipLaunchKernelGGL((gemv_decode1_kernel<BITS>), grid, block, lds, s, packed, scales,
+                               (int)O, (int)I, G, x, y);
+        else
+            QT_DEC(1, true);
     } else {
         if (ntiles <= blocks) QT_DEC(2, false);
         else QT_DEC(2, true);
