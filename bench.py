@@ -43,13 +43,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
-# Vector ALU: one non-packed f32 instruction per lane per 4 clocks per SIMD,
-# 64 lanes/clock/CU = 39.3 T lane-operations/s at 2.4 GHz (the published
-# 157.3 TFLOP/s fp32 vector peak counts a packed FMA as four).  Reciprocals
-# and round-to-integer issue on the transcendental unit beside the other
-# vector instructions, so an operation count can exceed this figure; the
-# search legs' roofline fraction is therefore the VALUBusy counter.
-VALU_SINGLE_TOPS = 256 * 64 * 2.4e9 / 1e12
+# Vector ALU issue peak: 128 lanes per clock per CU at 2.4 GHz = 78.64 T
+# lane-instructions/s (the published 157.3 TFLOP/s fp32 vector peak with an
+# FMA as two flops).  The search legs' roofline fraction is the kernel's
+# executed vector instructions (SQ_INSTS_VALU of a counter pass, times 64
+# lanes) per second of its live time against this peak.
+VALU_ISSUE_PEAK = 256 * 128 * 2.4e9
 N_COPIES = 64
 MIN_REPLAYS = 8  # timed graph replays of the headline (>= 512 launches)
 
@@ -102,6 +101,18 @@ def counters_for(name):
     if rec.get("source_sha") != sha_of(*rec.get("sources", [])):
         return None
     return rec
+
+
+def valu_roofline(cnt, ms):
+    """ALU roofline of a kernel from its executed vector instructions (a
+    counter record of the same kernel source) and its live time in ms."""
+    if cnt is None:
+        return {"bound": "alu", "achieved": None, "peak": VALU_ISSUE_PEAK / 1e12,
+                "unit": "T lane-instructions/s", "frac": None}
+    rate = cnt["valu_wave_insts"] * 64 / (ms * 1e-3)
+    return {"bound": "alu", "achieved": round(rate / 1e12, 2), "peak": round(VALU_ISSUE_PEAK / 1e12, 2),
+            "unit": "T lane-instructions/s", "frac": round(rate / VALU_ISSUE_PEAK, 4),
+            "valu_wave_insts": cnt["valu_wave_insts"]}
 
 
 def time_launches(fn, n, torch, warmup=2):
@@ -558,31 +569,21 @@ def search_leg(torch, qt, workloads, dev, legs):
     # per group: 64 candidates x 64 slots x 9 operations (divide, round, max,
     # min, multiply, subtract, multiply, multiply, add)
     ops = ngroups * 64 * 64 * 9
-    cnt = counters_for("search")
-    legs["quantize_search"] = {
-        "ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)), "bound": "alu",
-        # the roofline fraction: the share of the kernel's cycles in which the
-        # vector ALUs issue (rocprofv3 VALUBusy of this kernel; None if the
-        # kernel changed since the counters were taken)
-        "frac": None if cnt is None else cnt["valu_busy"],
-        "frac_basis": "VALUBusy counter (cycles the vector ALUs issue / kernel cycles)",
-        "ops_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
-        "op_count": "9 per slot per candidate (division as one)",
-        "ops_over_single_issue_peak": round(ops / (ms * 1e-3) / 1e12 / VALU_SINGLE_TOPS, 4)}
+    legs["quantize_search"] = dict(
+        {"ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)),
+         "ops_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
+         "op_count": "9 per slot per candidate (division as one)"},
+        **valu_roofline(counters_for("search"), ms))
     log(f"leg search: {legs['quantize_search']}")
     # two-stage signed search: 2 x 64 signed candidates, then 32 refinement points
     qt.qt_quantize_g64_signed(Wd, d, 64, 32, 0.5, 1.0, scales=s, codes=c)
     ms = time_launches(lambda i: qt.qt_quantize_g64_signed(Wd, d, 64, 32, 0.5, 1.0, scales=s,
                                                           codes=c), 3, torch)
     ops = ngroups * (2 * 64 + 32) * 64 * 9
-    cnt = counters_for("search_signed")
-    legs["quantize_search_signed"] = {
-        "ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)), "bound": "alu",
-        "frac": None if cnt is None else cnt["valu_busy"],
-        "frac_basis": "VALUBusy counter (cycles the vector ALUs issue / kernel cycles)",
-        "ops_Tops": round(ops / (ms * 1e-3) / 1e12, 2),
-        "ops_over_single_issue_peak": round(ops / (ms * 1e-3) / 1e12 / VALU_SINGLE_TOPS, 4),
-        "candidates": "2 x 64 + 32 per group"}
+    legs["quantize_search_signed"] = dict(
+        {"ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)),
+         "ops_Tops": round(ops / (ms * 1e-3) / 1e12, 2), "candidates": "2 x 64 + 32 per group"},
+        **valu_roofline(counters_for("search_signed"), ms))
     log(f"leg search signed: {legs['quantize_search_signed']}")
     del Wd, s, c, k, d
 
