@@ -236,7 +236,7 @@ qt_status qt_pack_i3(const int8_t* codes, int64_t O, int64_t I, uint8_t* packed,
     if (!codes || !packed) return QT_ERR_NULL;
     qt_status st = shape_ok(O, I);
     if (st != QT_OK) return st;
-    if (!aligned(packed, 16)) return QT_ERR_ALIGN;
+    if (!aligned(packed, 4)) return QT_ERR_ALIGN;
     if (overlap(packed, qt_packed_bytes(O, I), codes, O * I)) return QT_ERR_ALIAS;
     return launched(qt::launch_pack_i3(codes, O, I, packed, as_stream(stream)));
 }
@@ -258,7 +258,8 @@ qt_status matvec_bits(const uint8_t* packed, const float* scales, int64_t O, int
     const int64_t gbytes = bits == 3 ? kGroupBytes : kGroupBytesI4;
     qt_status st = shape_ok(O, I, gbytes);
     if (st != QT_OK) return st;
-    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(x, 4) || !aligned(y, 4))
+    if (!aligned(packed, bits == 3 ? 4 : 16) || !aligned(scales, 4) || !aligned(x, 4) ||
+        !aligned(y, 4))
         return QT_ERR_ALIGN;
     const int64_t G = qt_groups(I);
     if (overlap(y, O * 4, packed, O * G * gbytes) || overlap(y, O * 4, scales, O * G * 4) ||
@@ -291,7 +292,7 @@ qt_status qt_matmul_i4(const uint8_t* packed, const float* scales, int64_t O, in
     const int64_t xb = mul3(B, I, esz), yb = mul3(B, O, 4);
     if (xb < 0 || yb < 0) return QT_ERR_SHAPE;
     if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(Y, 4)) return QT_ERR_ALIGN;
-    if (!aligned(X, xt == QT_BF16 ? 16 : 4)) return QT_ERR_ALIGN;
+    if (!aligned(X, (uintptr_t)esz)) return QT_ERR_ALIGN;
     const int64_t G = qt_groups(I);
     if (overlap(Y, yb, packed, O * G * kGroupBytesI4) || overlap(Y, yb, scales, O * G * 4) ||
         overlap(Y, yb, X, xb))
@@ -311,8 +312,8 @@ qt_status qt_matmul_i3(const uint8_t* packed, const float* scales, int64_t O, in
     const int64_t esz = xt == QT_F32 ? 4 : 2;
     const int64_t xb = mul3(B, I, esz), yb = mul3(B, O, 4);
     if (xb < 0 || yb < 0) return QT_ERR_SHAPE;
-    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(Y, 4)) return QT_ERR_ALIGN;
-    if (!aligned(X, xt == QT_BF16 ? 16 : 4)) return QT_ERR_ALIGN;
+    if (!aligned(packed, 4) || !aligned(scales, 4) || !aligned(Y, 4)) return QT_ERR_ALIGN;
+    if (!aligned(X, (uintptr_t)esz)) return QT_ERR_ALIGN;
     const int64_t G = qt_groups(I);
     if (overlap(Y, yb, packed, O * G * kGroupBytes) || overlap(Y, yb, scales, O * G * 4) ||
         overlap(Y, yb, X, xb))
@@ -341,8 +342,8 @@ qt_status grouped_bits(const uint8_t* packed, const float* scales, int32_t E, in
     const int64_t pk = mul3(E, O * G, gbytes), sk = mul3(E, O * G, 4);
     const int64_t xb = mul3(n_x_rows, I, 4), yb = mul3(P, O, 4);
     if (pk < 0 || sk < 0 || xb < 0 || yb < 0) return QT_ERR_SHAPE;
-    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(X, 4) || !aligned(Y, 4) ||
-        !aligned(expert_offsets, 4) || (pair_row && !aligned(pair_row, 4)))
+    if (!aligned(packed, bits == 3 ? 4 : 16) || !aligned(scales, 4) || !aligned(X, 4) ||
+        !aligned(Y, 4) || !aligned(expert_offsets, 4) || (pair_row && !aligned(pair_row, 4)))
         return QT_ERR_ALIGN;
     if (overlap(Y, yb, packed, pk) || overlap(Y, yb, scales, sk) || overlap(Y, yb, X, xb) ||
         overlap(Y, yb, expert_offsets, (int64_t)(E + 1) * 4) ||

@@ -85,10 +85,20 @@ __device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t h16, u32x4_
     hi8 = u32x4_t{p89, p1011, p1213, p1415};
 }
 
+// Barrier that orders LDS accesses only.  __syncthreads() also waits for
+// every global load in flight, which would expose the latency of the
+// prefetches issued just before it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int32_t I,
-    int32_t G, const uint16_t* __restrict__ X, int32_t B, float* __restrict__ Y) {
+    int32_t G, const uint16_t* __restrict__ X, int32_t B, float* __restrict__ Y, int32_t ntok,
+    int32_t nb) {
     __shared__ __attribute__((aligned(16))) uint8_t ws[2][WS_BYTES];
     __shared__ float ss[2][BN];
     __shared__ __attribute__((aligned(16))) uint8_t raw[2][kThreads * 8];  // rows 0..BN-1: 24 B each
@@ -99,8 +109,13 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     const int wave = tid >> 6;
     const int h4 = lane >> 4;  // which 8-element slice of an MFMA operand
     const int l16 = lane & 15;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int32_t m0 = blockIdx.y * BM;
+    // Consecutive block ids run on different XCDs (8 of them, each with its
+    // own L2): the ids are remapped so that the token blocks of one row block
+    // run on one XCD and share its weight lines in that L2.
+    int32_t lin = blockIdx.x;
+    if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);
+    const int64_t n0 = (int64_t)(lin / ntok) * BN;
+    const int32_t m0 = (lin % ntok) * BM;
 
     // ---- activations: buffer over this launch's X, offsets per A slice
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
@@ -286,25 +301,25 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     load_raw(min(1, glast), rb);
     write_raw(0, ra);
     write_raw(1, rb);
-    __syncthreads();
+    lds_barrier();
     store_task(0, 0, 0);
     if (wave == 0) store_task(0, 0, 1);
     load_raw(min(2, glast), ra);
-    __syncthreads();
+    lds_barrier();
     for (int32_t g = 0;; g += 2) {
         load_a(min(g + 1, glast), a1);
         load_raw(min(g + 3, glast), rb);
         step(0, a0);
         if (wave == 0) store_task(1, 1, 1);
         write_raw(0, ra);
-        __syncthreads();
+        lds_barrier();
         if (g + 1 >= G) break;
         load_a(min(g + 2, glast), a0);
         load_raw(min(g + 4, glast), ra);
         step(1, a1);
         if (wave == 0) store_task(0, 0, 1);
         write_raw(1, rb);
-        __syncthreads();
+        lds_barrier();
         if (g + 2 >= G) break;
     }
 
@@ -337,15 +352,18 @@ hipError_t launch_gemm_mfma(const uint8_t* packed, const float* scales, int64_t 
     const bool vec = (I % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     for (int64_t t0 = 0; t0 < B; t0 += slab) {
         const int64_t bt = min(slab, B - t0);
-        const dim3 grid((unsigned)((O + BN - 1) / BN), (unsigned)((bt + BM - 1) / BM));
+        const int32_t ntok = (int32_t)((bt + BM - 1) / BM);
+        const int64_t nb = ((O + BN - 1) / BN) * ntok;
+        if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)nb);
         if (vec)
             hipLaunchKernelGGL((gemm_i3_mfma_kernel<true>), grid, dim3(kThreads), 0, s, packed,
                                scales, O, (int32_t)I, (int32_t)G, X + t0 * I, (int32_t)bt,
-                               Y + t0 * O);
+                               Y + t0 * O, ntok, (int32_t)nb);
         else
             hipLaunchKernelGGL((gemm_i3_mfma_kernel<false>), grid, dim3(kThreads), 0, s, packed,
                                scales, O, (int32_t)I, (int32_t)G, X + t0 * I, (int32_t)bt,
-                               Y + t0 * O);
+                               Y + t0 * O, ntok, (int32_t)nb);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

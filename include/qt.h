@@ -29,8 +29,16 @@
  *     enqueued and a nonzero qt_status is returned.  A failed launch returns
  *     QT_ERR_LAUNCH.  Faults inside a kernel surface at the caller's next
  *     synchronisation.  No exception crosses this interface.
- *   - Alignment: `packed` 16 bytes; f32 and int32 buffers 4 bytes; bf16
- *     buffers 16 bytes.  Outputs must not overlap inputs (QT_ERR_ALIAS).
+ *   - Alignment: f32 and int32 buffers 4 bytes, bf16 buffers 2 bytes, int3
+ *     `packed` buffers 4 bytes (qt_pack_i3, qt_matvec_i3, qt_matmul_i3,
+ *     qt_matvec_i3_grouped).  The int4 calls, qt_gptq_proxy and qt_moe_layer
+ *     take `packed` at 16 bytes.
+ *     Narrower alignment than the kernels' natural one costs speed, not
+ *     correctness: the multiply kernels switch to element loads for inputs
+ *     that are not 16-byte aligned, and read 4-byte-aligned packed groups
+ *     with multi-dword loads at 4-byte alignment (the unaligned access mode
+ *     that the ROCm runtime sets on gfx9 and later).  Outputs must not
+ *     overlap inputs (QT_ERR_ALIAS).
  *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
  *   - Results are deterministic: no kernel uses floating-point atomics, and
  *     repeated calls on the same inputs give bit-identical outputs.

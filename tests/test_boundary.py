@@ -100,16 +100,19 @@ def test_pack_rejects():
     f = L.qt_pack_i3
     assert f(None, 2, 64, B, None) == QT_ERR_NULL
     assert f(A, -1, 64, B, None) == QT_ERR_SHAPE
-    assert f(A, 2, 64, B + 8, None) == QT_ERR_ALIGN
+    assert f(A, 2, 64, B + 2, None) == QT_ERR_ALIGN
     assert f(A, 2, 64, A + 16, None) == QT_ERR_ALIAS
+    # packed at 4 bytes passes the alignment check (the overlap is caught next)
+    assert f(A, 2, 64, A + 4, None) == QT_ERR_ALIAS
 
 
 def test_matvec_rejects():
     f = L.qt_matvec_i3
     assert f(A, B, 4, 64, Cc, None, None) == QT_ERR_NULL
     assert f(A, B, 4, 0, Cc, D, None) == QT_ERR_SHAPE
-    assert f(A + 8, B, 4, 64, Cc, D, None) == QT_ERR_ALIGN
+    assert f(A + 2, B, 4, 64, Cc, D, None) == QT_ERR_ALIGN
     assert f(A, B + 2, 4, 64, Cc, D, None) == QT_ERR_ALIGN
+    assert f(A + 4, B, 4, 64, Cc, A + 36, None) == QT_ERR_ALIAS  # packed at 4 bytes is accepted
     assert f(A, B, 4, 64, Cc, A + 32, None) == QT_ERR_ALIAS
     assert f(A, B, 4, 64, Cc, Cc + 4, None) == QT_ERR_ALIAS
 
@@ -120,8 +123,12 @@ def test_matmul_rejects():
     assert f(A, B, 4, 64, Cc, 7, 2, D, None) == QT_ERR_DTYPE
     assert f(A, B, 4, 64, Cc, 0, 0, D, None) == QT_ERR_SHAPE
     assert f(A, B, 4, 64, Cc, 0, 65535 * 128 + 1, D, None) == QT_ERR_SHAPE
-    assert f(A, B, 4, 64, Cc + 8, 1, 32, D, None) == QT_ERR_ALIGN
+    assert f(A, B, 4, 64, Cc + 1, 1, 32, D, None) == QT_ERR_ALIGN  # bf16 needs 2 bytes
+    assert f(A, B, 4, 64, Cc + 2, 0, 32, D, None) == QT_ERR_ALIGN  # f32 needs 4 bytes
+    assert f(A + 2, B, 4, 64, Cc, 1, 32, D, None) == QT_ERR_ALIGN
     assert f(A, B, 4, 64, Cc, 1, 32, Cc + 64, None) == QT_ERR_ALIAS
+    # bf16 X at 2 bytes and packed at 4 bytes pass the alignment check
+    assert f(A + 4, B, 4, 64, Cc + 2, 1, 32, Cc + 64, None) == QT_ERR_ALIAS
 
 
 def test_grouped_rejects():
@@ -174,7 +181,7 @@ def test_int4_rejects():
     f = L.qt_matmul_i4
     assert f(A, B, 4, 64, Cc, 7, 2, D, None) == QT_ERR_DTYPE
     assert f(A, B, 4, 64, Cc, 0, 0, D, None) == QT_ERR_SHAPE
-    assert f(A, B, 4, 64, Cc + 8, 1, 32, D, None) == QT_ERR_ALIGN
+    assert f(A, B, 4, 64, Cc + 1, 1, 32, D, None) == QT_ERR_ALIGN
     assert f(A, B, 4, 64, Cc, 0, 2, A + 100, None) == QT_ERR_ALIAS
 
 

@@ -295,6 +295,62 @@ def test_matmul_b1_equals_matvec():
     assert np.array_equal(bits(y1), bits(y2[0]))
 
 
+# ---------------------------------------------------------------- pointer alignment
+def _at_offset(t, off):
+    """A device copy of t whose first byte lies `off` bytes past a 256-byte
+    boundary (torch allocations start on such a boundary)."""
+    esz = t.element_size()
+    assert off % esz == 0
+    n = t.numel()
+    buf = torch.empty(n + 256 // esz, dtype=t.dtype, device=t.device)
+    k = ((off - buf.data_ptr()) % 256) // esz
+    v = buf[k:k + n]
+    v.copy_(t.reshape(-1))
+    assert v.data_ptr() % 256 == off
+    return v.view(t.shape)
+
+
+@pytest.mark.parametrize("poff", [4, 12])
+def test_unaligned_packed_and_bf16_inputs(poff):
+    # packed at 4 (not 8) and 12 (not 16) bytes, bf16 X at 2 bytes: every
+    # int3 entry point gives the bytes / bits of the aligned call
+    O, I = 70, 650  # G = 11: 24-byte groups alternate between 8- and 16-byte offsets
+    W = workloads.generic_weights(O, I, seed=900 + poff)
+    so, co, _ = oracle.quantize_g64(W)
+    po = oracle.pack_i3(co)
+    say(f"unaligned packed +{poff}: pack")
+    pko = _at_offset(torch.zeros(po.size, dtype=torch.uint8, device="cuda:0"), poff)
+    qt.qt_pack_i3(dev(co), pko)
+    assert np.array_equal(host(pko), po)
+    pk, sc = dev(po), dev(so)
+    say(f"unaligned packed +{poff}: matvec")
+    x = dev(workloads.generic_vector(I, seed=5))
+    assert np.array_equal(bits(host(qt.qt_matvec_i3(pko, sc, O, I, x))),
+                          bits(host(qt.qt_matvec_i3(pk, sc, O, I, x))))
+    for B in (7, 20):  # exact path, MFMA path
+        say(f"unaligned packed +{poff}, bf16 X +2: matmul B={B}")
+        Xb = dev_bf16(workloads.bf16_bits_rne(workloads.generic_matrix(B, I, seed=B)))
+        Xo = _at_offset(Xb, 2)
+        ref = host(qt.qt_matmul_i3(pk, sc, O, I, Xb))
+        for pp, xx in ((pko, Xb), (pk, Xo), (pko, Xo)):
+            assert np.array_equal(bits(host(qt.qt_matmul_i3(pp, sc, O, I, xx))), bits(ref))
+        yr, ar = _matmul_ref(po, so, O, I, workloads.bf16_bits_to_f32(host(Xb)))
+        assert componentwise_err(ref, yr, ar) <= (TOL_F32 if B < 16 else TOL_MFMA)
+    say(f"unaligned packed +{poff}: grouped")
+    E, T = 3, 5
+    tok = np.array([0, 2, 4, 1, 3, 4], np.int32)
+    offs = np.array([0, 2, 4, 6], np.int32)
+    pe = np.concatenate([po] * E)
+    se = np.concatenate([so] * E)
+    X = workloads.generic_matrix(T, I, seed=31)
+    pke = dev(pe)
+    pkeo = _at_offset(pke, poff)
+    args = (dev(se), E, O, I, dev(X), dev(offs), tok.size)
+    y1 = host(qt.qt_matvec_i3_grouped(pke, *args, pair_row=dev(tok)))
+    y2 = host(qt.qt_matvec_i3_grouped(pkeo, *args, pair_row=dev(tok)))
+    assert np.array_equal(bits(y1), bits(y2))
+
+
 # ---------------------------------------------------------------- grouped (MoE)
 def _grouped_case(E, O, I, T, topk, seed):
     rng = workloads.rng_for("generic", 500 + seed, E, O, I)
