@@ -48,7 +48,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int64_t qt_groups(int64_t I) { return I < 1 ? 0 : (I + kGroup - 1) / kGroup; }
+int64_t qt_groups(int64_t I) { return I < 1 ? 0 : (I - 1) / kGroup + 1; }  // no overflow at INT64_MAX
 
 int64_t qt_packed_bytes(int64_t O, int64_t I) {
     if (O < 1 || I < 1) return 0;
@@ -374,6 +374,8 @@ qt_status qt_matvec_i4_grouped(const uint8_t* packed, const float* scales, int32
 // ---------------------------------------------------------------- MoE layer
 size_t qt_moe_layer_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t D, int64_t F) {
     if (T < 1 || k < 1 || E < 1 || D < 1 || F < 1) return 0;
+    // the layer's own limits, so that T * k and D + 2 F cannot overflow below
+    if (T > (1 << 22) || k > 32 || E > 512 || D > QT_MAX_I || F > QT_MAX_I) return 0;
     if (mul3(T * k, D + 2 * F, 4) < 0) return 0;
     return qt::moe_layer_workspace(T, k, E, D, F);
 }
