@@ -84,6 +84,8 @@ def test_prefill_gemm_full_size():
     say(f"  all {nslab} slabs bit-exact; {16 * nslab} sampled outputs, componentwise err "
         f"{worst:.3e}")
     assert worst <= TOL_MFMA
+    # the kernel's own bound (exact products, f32 sums): see test_gpu_parity
+    assert worst <= (64 + G + 2) * 2.0 ** -24
 
 
 def test_moe_grouped_full_size():
