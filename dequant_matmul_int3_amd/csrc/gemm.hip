@@ -85,15 +85,6 @@ __device__ __forceinline__ void dequant_quarter(uint32_t L, uint32_t h16, u32x4_
     hi8 = u32x4_t{p89, p1011, p1213, p1415};
 }
 
-// Barrier that orders LDS accesses only.  __syncthreads() also waits for
-// every global load in flight, which would expose the latency of the
-// prefetches issued just before it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ scales, int64_t O, int32_t I,

@@ -547,9 +547,10 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
         }
         const float acc = lane_group_sum<64>(rowacc[0]);
         // the two waves of a row in a fixed order; part is double-buffered by
-        // tile parity, so one barrier per tile suffices
+        // tile parity, so one barrier per tile suffices (an LDS-only one: the
+        // next tiles' weight loads stay in flight across it)
         if (lane == 0) part[it & 1][w] = acc;
-        __syncthreads();
+        lds_barrier();
         if (q == 0 && r < O) y[r] = part[it & 1][w] + part[it & 1][w + 1];
     };
     GroupBits<BITS> cur[NG];
@@ -559,18 +560,26 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
         read_x();
         mul_tile(blockIdx.x, 0, cur, cs);
     } else {
-        GroupBits<BITS> nxt[NG];
-        float ns[NG];
+        // the next three tiles' weights in flight while this one is multiplied
+        GroupBits<BITS> n1[NG], n2[NG], n3[NG];
+        float s1[NG], s2[NG], s3[NG];
+        const int step = gridDim.x;
         int tile = blockIdx.x;
         load_tile(tile, cur, cs);
+        if (tile + step < ntiles) load_tile(tile + step, n1, s1);
+        if (tile + 2 * step < ntiles) load_tile(tile + 2 * step, n2, s2);
         read_x();
-        for (int it = 0; tile < ntiles; tile += gridDim.x, ++it) {
-            if (tile + (int)gridDim.x < ntiles) load_tile(tile + gridDim.x, nxt, ns);
+        for (int it = 0; tile < ntiles; tile += step, ++it) {
+            if (tile + 3 * step < ntiles) load_tile(tile + 3 * step, n3, s3);
             mul_tile(tile, it, cur, cs);
 #pragma unroll
             for (int m = 0; m < NG; ++m) {
-                cur[m] = nxt[m];
-                cs[m] = ns[m];
+                cur[m] = n1[m];
+                cs[m] = s1[m];
+                n1[m] = n2[m];
+                s1[m] = s2[m];
+                n2[m] = n3[m];
+                s2[m] = s3[m];
             }
         }
     }
@@ -623,13 +632,16 @@ static hipError_t run_decode(const uint8_t* packed, const float* scales, int64_t
                              const float* x, float* y, hipStream_t s) {
     const int G = (int)((I + kGroup - 1) / kGroup);
     const int ntiles = (int)((O + kDecRows - 1) / kDecRows);
-    // up to two blocks per CU on a 256-CU device; more tiles loop
+    // one tile per block up to 512 tiles (two one-tile blocks fit on each of
+    // the 256 CUs); more tiles loop, one block per CU (the looping kernel's
+    // registers leave room for one 1024-thread block per CU)
     const int blocks = std::min(ntiles, 512);
     const size_t lds = (size_t)((G + 3) / 4) * kDecChunk;
     const dim3 grid((unsigned)blocks), block(1024);
-#define QT_DEC(NG, LOOP)                                                                   \
-    hipLaunchKernelGGL((gemv_decode_kernel<BITS, NG, LOOP>), grid, block, lds, s, packed, \
-                       scales, (int)O, (int)I, G, x, y, ntiles)
+    const dim3 loop_grid((unsigned)std::min(ntiles, 256));
+#define QT_DEC(NG, LOOP)                                                                      \
+    hipLaunchKernelGGL((gemv_decode_kernel<BITS, NG, LOOP>), LOOP ? loop_grid : grid, block, \
+                       lds, s, packed, scales, (int)O, (int)I, G, x, y, ntiles)
     if (G <= 128) {
         if (ntiles <= blocks)
             hipLaunchKernelGGL((gemv_decode1_kernel<BITS>), grid, block, lds, s, packed, scales,

@@ -207,6 +207,22 @@ def test_pack_random_codes(O, I):
 
 
 # ---------------------------------------------------------------- matvec properties
+@pytest.mark.parametrize("O,I", [(4104, 7168), (6000, 1000), (5000, 130)])
+def test_matvec_many_row_tiles(O, I):
+    # more than 512 tiles of 8 rows: the decode kernel's looping form (each
+    # block takes several tiles, the next ones in flight), with a partly
+    # used last tile and, for I = 130, a short tail group
+    W = workloads.generic_weights(O, I, seed=O + I)
+    so, co, po, (pd, sd) = check_quantize(W)
+    x = workloads.generic_vector(I, seed=7)
+    say(f"matvec many tiles O={O} I={I}")
+    y = host(qt.qt_matvec_i3(pd, sd, O, I, dev(x)))
+    yr, ar = oracle.matvec_f64(po, so, O, I, x)
+    assert componentwise_err(y, yr, ar) <= TOL_F32
+    y2 = host(qt.qt_matvec_i3(pd, sd, O, I, dev(x)))
+    assert np.array_equal(bits(y), bits(y2)), "matvec is not deterministic"
+
+
 def test_matvec_one_hot_is_exact():
     O, I = 64, 300
     W = workloads.generic_weights(O, I, seed=12)
