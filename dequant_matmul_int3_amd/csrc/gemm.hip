@@ -28,6 +28,7 @@
 //
 // For B x O shapes that are not multiples of the tile, out-of-range rows read
 // a valid row (their results are discarded) and are never stored.
+#include "lds_barrier.h"
 #include "qt_internal.h"
 
 namespace qt {

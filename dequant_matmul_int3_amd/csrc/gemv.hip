@@ -45,6 +45,7 @@
 //    number of rows with the input staged once per block.
 #include <algorithm>
 
+#include "lds_barrier.h"
 #include "qt_internal.h"
 
 namespace qt {

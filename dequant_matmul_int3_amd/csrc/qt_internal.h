@@ -6,16 +6,6 @@
 
 namespace qt {
 
-// Barrier that orders LDS accesses only: global loads in flight stay in
-// flight.  __syncthreads() also waits for every outstanding global load,
-// which would expose the latency of prefetches issued just before it.
-// (LDS-direct loads still in flight are waited for: they write LDS.)
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 constexpr int kGroup = 64;       // inputs per group
 constexpr int kGroupBytes = 24;  // int3: 16 B low plane + 8 B high plane
 constexpr int kGroupBytesI4 = 32;  // int4: 64 nibbles
