@@ -115,6 +115,9 @@ def valu_roofline(cnt, ms):
             "valu_wave_insts": cnt["valu_wave_insts"]}
 
 
+MOE_ROUNDS, MOE_CALLS = 9, 4  # interleaved timing rounds of the MoE steps
+
+
 def time_launches(fn, n, torch, warmup=2):
     """Average time per fn() call over n back-to-back calls, from a pair of
     events on the current stream (the stream the kernels run on), after
@@ -635,7 +638,7 @@ def moe_leg(torch, qt, workloads, dev, legs, int3_step=True, int4_steps=False):
         steps.append(("moe_grouped", 3, 3))
     if int4_steps:
         steps += [("moe_grouped_int4", 4, 4), ("moe_grouped_int4_up3", 3, 4)]
-    for name, bu, bd in steps:
+    def make_step(bu, bd):
         pu, su = store["up", bu]
         pdn, sdn = store["down", bd]
 
@@ -643,12 +646,27 @@ def moe_leg(torch, qt, workloads, dev, legs, int3_step=True, int4_steps=False):
             grouped[bu](pu, su, E, Ou, Iu, Xmd, offd, P, pair_row=tokd, Y=h)
             grouped[bd](pdn, sdn, E, Od, Id, h, offd, P, Y=yo)
 
-        for i in range(5):
-            moe_step(i)
-        ms = time_launches(moe_step, 20, torch)
         per_exp = pu.shape[1] + su[0].numel() * 4 + pdn.shape[1] + sdn[0].numel() * 4
-        mb = hit * per_exp + Xm.nbytes + P * (Ou + Od) * 4 * 2
-        legs[name] = {"ms": round(ms, 4), "experts_hit": hit, "pairs": int(P),
+        return moe_step, per_exp
+
+    fns = {name: make_step(bu, bd) for name, bu, bd in steps}
+    for fn, _ in fns.values():
+        for i in range(5):
+            fn(i)
+    # the steps are timed in interleaved rounds (each round times every step
+    # over MOE_CALLS calls), and each reports its median round: the GPU's
+    # clock settles during the first hundreds of milliseconds of load, which
+    # would otherwise slow whichever step is timed first
+    rounds = {name: [] for name in fns}
+    for r in range(MOE_ROUNDS):
+        for name, (fn, _) in fns.items():
+            rounds[name].append(time_launches(fn, MOE_CALLS, torch, warmup=1))
+    for name, bu, bd in steps:
+        ms = float(np.median(rounds[name]))
+        mb = hit * fns[name][1] + Xm.nbytes + P * (Ou + Od) * 4 * 2
+        legs[name] = {"ms": round(ms, 4), "ms_rounds_min_max": [round(min(rounds[name]), 4),
+                                                                round(max(rounds[name]), 4)],
+                      "experts_hit": hit, "pairs": int(P),
                       "up_bits": bu, "down_bits": bd,
                       "GB_s": round(mb / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
                       "frac": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -281,7 +281,8 @@ __device__ __forceinline__ void tile_bits(TileLds<WROW, CG>& L, int e, int64_t r
                                           const int32_t* prow, const int32_t* offs, int32_t P,
                                           float* Y) {
     const int32_t G = (I + kGroup - 1) / kGroup;
-    grouped_tile<BITS, true, true>(L, e, rb, packed, scales, O, I, G, X, nx, prow, offs, P, Y);
+    grouped_tile<BITS, true, true, WROW, CG, false>(L, e, rb, packed, scales, O, I, G, X, nx, prow,
+                                                   offs, P, Y);
 }
 
 // Routing tables the items look up, copied to LDS at the start (a global
