@@ -1,37 +1,22 @@
-// A mixture-of-experts expert layer in two launches: a one-block routing
-// kernel, then a persistent kernel for the gate and up projections, SwiGLU,
-// the down projection and the combine of every token's experts (the pull
-// request page's MoE decode setting: every routed expert's weights read once
-// per step; its per-projection ablation names gate_proj, up_proj and
-// down_proj, each at int3-g64 or grouped int4).
+// A mixture-of-experts expert layer as a sequence of launches on the
+// caller's stream (the pull request page's MoE decode setting: every routed
+// expert's weights read once per step; its per-projection ablation names
+// gate_proj, up_proj and down_proj, each at int3-g64 or grouped int4):
 //
-//  0. routing (its own launch, one block): per token the k largest logits
-//     (equal logits: lower expert first), combine weights a softmax over
-//     them; the (expert, token) pairs sorted by expert, then token; the
-//     expert work order; the phase counters of the layer kernel zeroed.
-// Then phases separated by grid-wide barriers (a cooperative launch, so
-// every block of the grid is resident; no block leaves before the last
-// barrier):
-//  1. items (expert, 64-row block of gate and up): the grouped matrix-core
-//     tile for gate, then for up, then h = silu(g) * u for those rows of
-//     every pair of the expert.
-//  2. items (expert, 64-row block of down): the same tile on h.
-//  3. out[t] = sum_j w_tj y_{pair(t, j)} in j order.
-// A block's first item of a phase is its block index; later ones come from
-// the phase's shared counter as blocks finish, in the routing's expert order
-// (the most pairs first, so the longest items start early); experts without
-// pairs have no items.  Each item writes its own outputs, so the results do
-// not depend on which block ran it.  (Routing inside the persistent kernel
-// cost a grid barrier that every block reached at once, which measured
-// tens of microseconds.)
-#include <hip/hip_cooperative_groups.h>
-
+//  0. routing (one block): per token the k largest logits (equal logits:
+//     lower expert first), combine weights a softmax over them; the
+//     (expert, token) pairs sorted by expert, then token.
+//  1. gate and up: the grouped matrix-core tile (grouped_tile.h) over
+//     (64-row block, expert, projection), g and u for every pair.
+//  2. h = silu(g) * u for every pair and row.
+//  3. down: the grouped launch on h (a pair's row of h is its input).
+//  4. out[t] = sum_j w_tj y_{pair(t, j)} in j order.
+// Every output is written once by one thread, in a fixed order, so the
+// results do not depend on scheduling.
 #include "grouped_tile.h"
 
 namespace qt {
 namespace {
-
-namespace cg = cooperative_groups;
 
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 512;  // routing keeps a token's keys in registers (32 per lane)
@@ -54,15 +39,13 @@ struct MoeArgs {
     int32_t* slot;   // [T k] pair index of (t, j)
     int32_t* prow;   // [P] token of pair p
     int32_t* offs;   // [E + 1]
-    int32_t* order;  // [E] experts with pairs, most pairs first (ties: lower index)
-    int32_t* ctr;    // [4] next gate/up item, next down item, experts with pairs
     float* Yg;       // [P x F]
     float* Yu;       // [P x F]
     float* H;        // [P x F] silu(g) * u
     float* Yd;       // [P x D]
 };
 
-// Phase 0, one block of NT threads: 16 lanes per token, NT / 16 tokens per
+// Stage 0, one block of NT threads: 16 lanes per token, NT / 16 tokens per
 // pass (NT falls as the experts per lane, and so the registers, grow).  Each pick is the largest key below the previous pick
 // (keys order (logit, expert): larger logit first, then lower expert), a
 // lane's maximum over its experts, then over the 16 lanes.  Each pair's
@@ -115,7 +98,6 @@ __global__ __launch_bounds__(NT) void moe_route_kernel(MoeArgs a) {
     __shared__ int cnt[kMaxExperts];                 // pairs per expert so far (0 past E)
     __shared__ int loffs[kMaxExperts + 1];
     __shared__ int lpk[kRouteLdsPairs];              // packed pairs if they fit
-    __shared__ int s_ne;
     const int tid = threadIdx.x;
     const int sub = tid & 15;  // lane within the token's 16-lane row
     const int row = tid >> 4;  // token of the pass
@@ -212,7 +194,6 @@ __global__ __launch_bounds__(NT) void moe_route_kernel(MoeArgs a) {
             base += cnt[e];
         }
         if (tid == 63) loffs[E] = inc;
-        if (tid == 0) s_ne = 0;
     }
     __syncthreads();
     for (int e = tid; e <= E; e += NT) a.offs[e] = loffs[e];
@@ -222,135 +203,52 @@ __global__ __launch_bounds__(NT) void moe_route_kernel(MoeArgs a) {
         a.prow[pos] = q / k;
         a.slot[q] = pos;
     }
-    // the work order of the expert phases: experts with pairs, the most
-    // first (their items take longest), ties by index
-    for (int e = tid; e < E; e += NT) {
-        const int c = cnt[e];
-        if (c > 0) {
-            int rank = 0;
-            for (int e2 = 0; e2 < E4; e2 += 4) {  // four counts per LDS read
-                const int4 c4 = *reinterpret_cast<const int4*>(cnt + e2);
-                rank += (c4.x > c) || (c4.x == c && e2 < e);
-                rank += (c4.y > c) || (c4.y == c && e2 + 1 < e);
-                rank += (c4.z > c) || (c4.z == c && e2 + 2 < e);
-                rank += (c4.w > c) || (c4.w == c && e2 + 3 < e);
-            }
-            a.order[rank] = e;
-            atomicAdd(&s_ne, 1);
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {  // the layer kernel's phase counters
-        a.ctr[0] = 0;
-        a.ctr[1] = 0;
-        a.ctr[2] = s_ne;
-    }
 }
 
-// Work items of a phase come from the phase's shared counter as blocks
-// finish (uneven items leave no long tail).  The counter is read one step
-// ahead: ask() issues the atomic in thread 0 and keeps the result in a
-// register, take() hands it to the block, so the atomic's latency overlaps
-// the work issued in between.
-struct ItemCounter {
-    int32_t* ctr;
-    int32_t pending;  // thread 0 only
-    __device__ __forceinline__ void ask() {
-        if (threadIdx.x == 0) pending = atomicAdd(ctr, 1);
-    }
-    __device__ __forceinline__ int64_t take() {
-        __shared__ int32_t s_item;
-        if (threadIdx.x == 0) s_item = pending;
-        __syncthreads();
-        const int64_t it = s_item;
-        __syncthreads();  // everyone has read it before the next take()
-        return it;
-    }
-};
+// Stage 1 blocks (row block, expert, projection: z = 0 gate, 1 up); the
+// tile's chunks of 8 groups and four blocks per CU as in the grouped launch.
+constexpr int kLayerCG = 8;
 
-// Sixteen groups per chunk: the layer's kernel holds two blocks per CU either
-// way (its registers), so fewer chunk barriers win (eight-group chunks for
-// the down tiles, a second tile instantiation in the kernel, raised its
-// registers to one block per CU for some formats).
-constexpr int kLayerCG = 16;
-
-template <int BITS, int WROW, int CG>
-__device__ __forceinline__ void tile_bits(TileLds<WROW, CG>& L, int e, int64_t rb,
-                                          const uint8_t* packed, const float* scales, int64_t O,
-                                          int32_t I, const float* X, int64_t nx,
-                                          const int32_t* prow, const int32_t* offs, int32_t P,
-                                          float* Y) {
-    const int32_t G = (I + kGroup - 1) / kGroup;
-    grouped_tile<BITS, true, true, WROW, CG, false>(L, e, rb, packed, scales, O, I, G, X, nx, prow,
-                                                   offs, P, Y);
-}
-
-// Routing tables the items look up, copied to LDS at the start (a global
-// read each time put its latency on every item's critical path): the expert
-// order, the offsets and, up to this many pairs, the pairs' token rows.
-constexpr int kLayerLdsPairs = 1024;
-
-// GB, UB, DB: the formats (3 or 4 bits) of gate, up and down.
-template <int GB, int UB, int DB>
-__global__ __launch_bounds__(kThreads, 2) void moe_layer_kernel(MoeArgs a) {
-    constexpr int kW = (GB == 4 || UB == 4 || DB == 4) ? Geo<4, kLayerCG>::kWRow
-                                                       : Geo<3, kLayerCG>::kWRow;
+template <int GB, int UB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+moe_gate_up_kernel(MoeArgs a) {
+    constexpr int kW = (GB == 4 || UB == 4) ? Geo<4, kLayerCG>::kWRow : Geo<3, kLayerCG>::kWRow;
     __shared__ TileLds<kW, kLayerCG> lds;
-    __shared__ int32_t s_order[kMaxExperts];
-    __shared__ int32_t s_offs[kMaxExperts + 1];
-    __shared__ int32_t s_prow[kLayerLdsPairs];
-    cg::grid_group grid = cg::this_grid();
     const int P = a.T * a.k;
-    const int tid = threadIdx.x;
-
-    const int64_t nf = (a.F + kRows - 1) / kRows, nd = (a.D + kRows - 1) / kRows;
-    const int64_t ne = a.ctr[2];
-    ItemCounter c1{&a.ctr[0], 0};
-    for (int i = tid; i < ne; i += kThreads) s_order[i] = a.order[i];
-    for (int i = tid; i <= a.E; i += kThreads) s_offs[i] = a.offs[i];
-    const bool prow_lds = P <= kLayerLdsPairs;
-    if (prow_lds)
-        for (int i = tid; i < P; i += kThreads) s_prow[i] = a.prow[i];
-    const int32_t* prow = prow_lds ? s_prow : a.prow;
-    __syncthreads();
-
-    const int64_t items1 = ne * nf;
-    for (int64_t it = blockIdx.x; it < items1;) {
-        const int e = s_order[it / nf];
-        const int64_t rb = it % nf;
-        tile_bits<GB>(lds, e, rb, a.gp, a.gs, a.F, a.D, a.X, a.T, prow, s_offs, P, a.Yg);
-        tile_bits<UB>(lds, e, rb, a.up, a.us, a.F, a.D, a.X, a.T, prow, s_offs, P, a.Yu);
-        // h for this block's rows of every pair of the expert (the tiles'
-        // stores above come from this block: a barrier makes them visible);
-        // the next item is asked for first (items here are long: asking
-        // earlier could leave a block holding one while others idle); every
-        // answer is taken below, so no item is skipped
-        c1.ask();
-        const int p0 = s_offs[e], p1 = s_offs[e + 1];
-        __syncthreads();
-        const int64_t r0 = rb * kRows;
-        for (int q = tid; q < (p1 - p0) * kRows; q += kThreads) {
-            const int64_t p = p0 + q / kRows, r = r0 + q % kRows;
-            if (r < a.F) a.H[p * a.F + r] = silu(a.Yg[p * a.F + r]) * a.Yu[p * a.F + r];
-        }
-        it = gridDim.x + c1.take();
+    const int32_t G = (a.D + kGroup - 1) / kGroup;
+    const bool up = blockIdx.z == 1;
+    const uint8_t* pk = up ? a.up : a.gp;
+    const float* sc = up ? a.us : a.gs;
+    float* Y = up ? a.Yu : a.Yg;
+    if constexpr (GB == UB) {
+        grouped_tile<GB, true, true>(lds, blockIdx.y, blockIdx.x, pk, sc, a.F, a.D, G, a.X, a.T,
+                                     a.prow, a.offs, P, Y);
+    } else if (up) {
+        grouped_tile<UB, true, true>(lds, blockIdx.y, blockIdx.x, pk, sc, a.F, a.D, G, a.X, a.T,
+                                     a.prow, a.offs, P, Y);
+    } else {
+        grouped_tile<GB, true, true>(lds, blockIdx.y, blockIdx.x, pk, sc, a.F, a.D, G, a.X, a.T,
+                                     a.prow, a.offs, P, Y);
     }
-    grid.sync();
+}
 
-    const int64_t items2 = ne * nd;
-    ItemCounter c2{&a.ctr[1], 0};
-    for (int64_t it = blockIdx.x; it < items2;) {
-        c2.ask();  // short items: the next one is asked for as this one starts (taken below)
-        const int e = s_order[it / nd];
-        const int64_t rb = it % nd;
-        tile_bits<DB>(lds, e, rb, a.dp, a.ds, a.D, a.F, a.H, P, nullptr, s_offs, P, a.Yd);
-        it = gridDim.x + c2.take();
+// Stage 2: h = silu(g) * u, four elements per thread (P * F % 4 == 0).
+__global__ __launch_bounds__(256) void moe_swiglu_kernel(const float4* __restrict__ g,
+                                                         const float4* __restrict__ u,
+                                                         float4* __restrict__ h, int64_t n4) {
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4;
+         q += (int64_t)gridDim.x * 256) {
+        const float4 gv = g[q], uv = u[q];
+        h[q] = make_float4(silu(gv.x) * uv.x, silu(gv.y) * uv.y, silu(gv.z) * uv.z,
+                           silu(gv.w) * uv.w);
     }
-    grid.sync();
+}
 
+// Stage 4: out[t][o] = sum_j w_tj * Yd[slot(t, j)][o], j in order.
+__global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
     const int64_t n = (int64_t)a.T * a.D;
-    for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < n;
-         q += (int64_t)gridDim.x * kThreads) {
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n;
+         q += (int64_t)gridDim.x * 256) {
         const int64_t t = q / a.D, o = q % a.D;
         float acc = 0.0f;
         for (int j = 0; j < a.k; ++j)
@@ -364,8 +262,8 @@ __global__ __launch_bounds__(kThreads, 2) void moe_layer_kernel(MoeArgs a) {
 size_t moe_layer_workspace(int64_t T, int64_t k, int64_t E, int64_t D, int64_t F) {
     const int64_t P = T * k;
     auto up16 = [](int64_t b) { return (b + 15) / 16 * 16; };
-    return (size_t)(4 * up16(P * 4) + up16((E + 1) * 4) + up16(E * 4) + up16(4 * 4) +
-                    up16(3 * P * F * 4) + up16(P * D * 4));
+    return (size_t)(4 * up16(P * 4) + up16((E + 1) * 4) + up16(3 * P * F * 4) +
+                    up16(P * D * 4));
 }
 
 hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
@@ -405,46 +303,47 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
     w += up16(P * 4);
     a.offs = reinterpret_cast<int32_t*>(w);
     w += up16((E + 1) * 4);
-    a.order = reinterpret_cast<int32_t*>(w);
-    w += up16(E * 4);
-    a.ctr = reinterpret_cast<int32_t*>(w);
-    w += up16(4 * 4);
     a.Yg = reinterpret_cast<float*>(w);
     a.Yu = a.Yg + P * F;
     a.H = a.Yu + P * F;
     w += up16(3 * P * F * 4);
     a.Yd = reinterpret_cast<float*>(w);
 
-    const int code = (gbits - 3) * 4 + (ubits - 3) * 2 + (dbits - 3);
-    const void* kernels[8] = {
-        reinterpret_cast<const void*>(moe_layer_kernel<3, 3, 3>),
-        reinterpret_cast<const void*>(moe_layer_kernel<3, 3, 4>),
-        reinterpret_cast<const void*>(moe_layer_kernel<3, 4, 3>),
-        reinterpret_cast<const void*>(moe_layer_kernel<3, 4, 4>),
-        reinterpret_cast<const void*>(moe_layer_kernel<4, 3, 3>),
-        reinterpret_cast<const void*>(moe_layer_kernel<4, 3, 4>),
-        reinterpret_cast<const void*>(moe_layer_kernel<4, 4, 3>),
-        reinterpret_cast<const void*>(moe_layer_kernel<4, 4, 4>)};
-    if (code < 0 || code > 7) return hipErrorInvalidValue;
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernels[code], kThreads, 0);
-    if (e != hipSuccess) return e;
-    if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+    if (gbits < 3 || gbits > 4 || ubits < 3 || ubits > 4 || dbits < 3 || dbits > 4)
+        return hipErrorInvalidValue;
     if (E <= 128)
         moe_route_kernel<8, 1024><<<1, 1024, 0, s>>>(a);
     else if (E <= 256)
         moe_route_kernel<16, 512><<<1, 512, 0, s>>>(a);
     else
         moe_route_kernel<32, 256><<<1, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    const dim3 grid1((unsigned)((F + kRows - 1) / kRows), (unsigned)E, 2);
+    if (gbits == 3 && ubits == 3)
+        moe_gate_up_kernel<3, 3><<<grid1, kThreads, 0, s>>>(a);
+    else if (gbits == 3)
+        moe_gate_up_kernel<3, 4><<<grid1, kThreads, 0, s>>>(a);
+    else if (ubits == 3)
+        moe_gate_up_kernel<4, 3><<<grid1, kThreads, 0, s>>>(a);
+    else
+        moe_gate_up_kernel<4, 4><<<grid1, kThreads, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    void* args[] = {&a};
-    return hipLaunchCooperativeKernel(kernels[code], dim3((unsigned)(per_cu * cus)), dim3(kThreads),
-                                      args, 0, s);
+
+    const int64_t n4 = P * F / 4;  // F % 128 == 0
+    moe_swiglu_kernel<<<(unsigned)std::min<int64_t>((n4 + 255) / 256, 4096), 256, 0, s>>>(
+        reinterpret_cast<const float4*>(a.Yg), reinterpret_cast<const float4*>(a.Yu),
+        reinterpret_cast<float4*>(a.H), n4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    e = launch_gemv_grouped(dp, ds, E, D, F, a.H, P, nullptr, a.offs, (int32_t)P, a.Yd, s, dbits);
+    if (e != hipSuccess) return e;
+
+    moe_combine_kernel<<<(unsigned)std::min<int64_t>((T * D + 255) / 256, 4096), 256, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace qt

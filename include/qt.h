@@ -365,9 +365,10 @@ qt_status qt_gptq_proxy(const float* W, const uint8_t* packed, const float* scal
                         void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * Mixture-of-experts expert layer: a one-block routing launch, then one
- * persistent (cooperative) launch for the gate and up projections, SwiGLU,
- * the down projection and the combine of each token's experts (the pull request page's MoE decode setting; its
+ * Mixture-of-experts expert layer, as five launches on the stream: a
+ * one-block routing, the gate and up projections (one grouped launch), h =
+ * SwiGLU(g, u), the down projection (the grouped launch) and the combine of
+ * each token's experts (the pull request page's MoE decode setting; its
  * per-projection ablation names gate_proj, up_proj and down_proj, each at
  * int3-g64 or grouped int4).  The pages give no expert formula or combine
  * rule; this library reads them as
@@ -383,10 +384,9 @@ qt_status qt_gptq_proxy(const float* W, const uint8_t* packed, const float* scal
  *   [E][rows x cols/64]; out [T x D] f32 (16-byte aligned).
  *   D and F multiples of 128; 1 <= k <= min(32, E); E <= 512; T <= 2^22.
  *   workspace: qt_moe_layer_workspace_bytes(T, k, E, D, F) bytes (the f32
- *   products g, u, h and the down outputs, (T k)(3F + D) * 4, plus small
- *   tables: routing, expert work order, work counters).
- * The persistent launch keeps every block of its grid resident until its
- * last barrier; results are deterministic.
+ *   products g, u, h and the down outputs, (T k)(3F + D) * 4, plus the
+ *   routing tables).
+ * Every output is written once, in a fixed order: results are deterministic.
  */
 size_t qt_moe_layer_workspace_bytes(int64_t T, int32_t k, int32_t E, int64_t D, int64_t F);
 qt_status qt_moe_layer(const float* X, int64_t T, int64_t D, int64_t F, const float* logits,
