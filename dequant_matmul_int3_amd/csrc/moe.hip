@@ -244,16 +244,24 @@ __global__ __launch_bounds__(256) void moe_swiglu_kernel(const float4* __restric
     }
 }
 
-// Stage 4: out[t][o] = sum_j w_tj * Yd[slot(t, j)][o], j in order.
+// Stage 4: out[t][o] = sum_j w_tj * Yd[slot(t, j)][o], j in order; blocks
+// (column block, tokens y, y + gridDim.y, ...), four columns per thread
+// (D % 128 == 0).
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
-    const int64_t n = (int64_t)a.T * a.D;
-    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n;
-         q += (int64_t)gridDim.x * 256) {
-        const int64_t t = q / a.D, o = q % a.D;
-        float acc = 0.0f;
-        for (int j = 0; j < a.k; ++j)
-            acc += a.wgt[t * a.k + j] * a.Yd[(int64_t)a.slot[t * a.k + j] * a.D + o];
-        a.out[q] = acc;
+    const int32_t o4 = blockIdx.x * 256 + threadIdx.x;
+    if (4 * o4 >= a.D) return;
+    for (int64_t t = blockIdx.y; t < a.T; t += gridDim.y) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < a.k; ++j) {
+            const float w = a.wgt[t * a.k + j];
+            const float4 y =
+                reinterpret_cast<const float4*>(a.Yd + (int64_t)a.slot[t * a.k + j] * a.D)[o4];
+            acc.x += w * y.x;
+            acc.y += w * y.y;
+            acc.z += w * y.z;
+            acc.w += w * y.w;
+        }
+        reinterpret_cast<float4*>(a.out + t * a.D)[o4] = acc;
     }
 }
 
@@ -342,7 +350,8 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
     e = launch_gemv_grouped(dp, ds, E, D, F, a.H, P, nullptr, a.offs, (int32_t)P, a.Yd, s, dbits);
     if (e != hipSuccess) return e;
 
-    moe_combine_kernel<<<(unsigned)std::min<int64_t>((T * D + 255) / 256, 4096), 256, 0, s>>>(a);
+    moe_combine_kernel<<<dim3((unsigned)((D / 4 + 255) / 256), (unsigned)std::min<int64_t>(T, 65535)),
+                         256, 0, s>>>(a);
     return hipGetLastError();
 }
 
