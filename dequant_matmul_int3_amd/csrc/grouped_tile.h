@@ -381,12 +381,10 @@ __device__ __forceinline__ void zero_columns(uint8_t* pl, int nt, int tid) {
 // One item: the pairs of expert e against its rows [64 rb, 64 rb + 64).
 // W16: every row's chunk bytes start on a 16-byte boundary (int4, or int3
 // with G even); else 8-byte pieces.  XV: inputs allow 16-byte loads
-// (I % 4 == 0, X 16-byte aligned).  SPLIT: full chunks take loads and
-// stores without clamping, in code of their own (more registers; a kernel
-// that runs several tiles, near its register limit, takes the clamped code
-// for every chunk).  Starts with a barrier, so items can follow one another
-// in a block.
-template <int BITS, bool W16, bool XV, int WROW, int CG, bool SPLIT = true>
+// (I % 4 == 0, X 16-byte aligned).  Full chunks take loads and stores
+// without clamping, in code of their own.  Starts with a barrier, so items
+// can follow one another in a block.
+template <int BITS, bool W16, bool XV, int WROW, int CG>
 __device__ __forceinline__ void grouped_tile(
     TileLds<WROW, CG>& L, int e, int64_t rb, const uint8_t* __restrict__ packed,
     const float* __restrict__ scales, int64_t O, int32_t I, int32_t G,
@@ -475,7 +473,7 @@ __device__ __forceinline__ void grouped_tile(
     // loads of chunk c0 into registers, and their stores to LDS, with the
     // clamping of a short last chunk only where it is one (a uniform branch)
     auto load_chunk = [&](int32_t c0, int nt) {
-        if (SPLIT && is_full(c0)) {
+        if (is_full(c0)) {
             load_w(c0, std::true_type{});
             load_sx<BITS, CG, XV, true>(sx, ro, c0, nt, xrow, I, G, tid);
         } else {
@@ -486,7 +484,7 @@ __device__ __forceinline__ void grouped_tile(
     auto store_chunk = [&](int32_t c0, int nt) {
 #pragma unroll
         for (int i = 0; i < kWPer; ++i) *reinterpret_cast<u32x4_t*>(wl + wdst[i]) = wv[i];
-        if (SPLIT && is_full(c0))
+        if (is_full(c0))
             store_sx<BITS, CG, true>(sx, ro, c0, nt, L.sl, L.pl, I, G, tid);
         else
             store_sx<BITS, CG, false>(sx, ro, c0, nt, L.sl, L.pl, I, G, tid);
