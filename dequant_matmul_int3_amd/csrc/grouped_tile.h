@@ -219,7 +219,7 @@ __device__ __forceinline__ void load_sx(SxRegs<CG>& c, const SxRoles<CG>& ro, in
     const int32_t k0 = c0 * kGroup;
     // offset of input k of the chunk from the chunk's start (clamped: past
     // the row, the row's first input)
-    auto at = [&](int k) { return FULL || k0 + k < I ? k : -k0; };
+    auto at = [&](int k) { return FULL || (int64_t)k0 + k < I ? k : -k0; };
 #pragma unroll
     for (int t = 0; t < kTok; ++t) {
         if (t >= nt) break;  // uniform
@@ -269,7 +269,7 @@ __device__ __forceinline__ void store_sx(const SxRegs<CG>& c, const SxRoles<CG>&
         float x[E];
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            x[e] = FULL || k0 + staged_input<BITS>(E * tid + e) < I ? c.x[t][e] : 0.0f;
+            x[e] = FULL || (int64_t)k0 + staged_input<BITS>(E * tid + e) < I ? c.x[t][e] : 0.0f;
         uint32_t w[3][E / 2];
         split3<E>(x, w);
 #pragma unroll
