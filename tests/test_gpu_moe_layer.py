@@ -1,5 +1,5 @@
-"""The MoE expert layer (a routing launch, then one cooperative launch for
-gate/up, SwiGLU, down, combine) against the oracle's f64 layer: every output
+"""The MoE expert layer (routing, gate/up, SwiGLU, down and combine
+launches) against the oracle's f64 layer: every output
 within 1e-5 of the error budget the oracle derives from the grouped
 multiply's tolerance."""
 import numpy as np
