@@ -350,8 +350,8 @@ hipError_t launch_moe_layer(const float* X, int64_t T, int64_t D, int64_t F,
     e = launch_gemv_grouped(dp, ds, E, D, F, a.H, P, nullptr, a.offs, (int32_t)P, a.Yd, s, dbits);
     if (e != hipSuccess) return e;
 
-    moe_combine_kernel<<<dim3((unsigned)((D / 4 + 255) / 256), (unsigned)std::min<int64_t>(T, 65535)),
-                         256, 0, s>>>(a);
+    const dim3 grid4((unsigned)((D / 4 + 255) / 256), (unsigned)std::min<int64_t>(T, 65535));
+    moe_combine_kernel<<<grid4, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
