@@ -231,11 +231,17 @@ def main():
     stack_bytes = packs.numel() + scs.numel() * 4 + I * 4 + Ostack * 4
     for _ in range(3):
         qt.qt_matvec_i3(packs.view(-1), scs.view(-1), Ostack, I, xd, ystack)
-    ms = time_launches(lambda i: qt.qt_matvec_i3(packs.view(-1), scs.view(-1), Ostack, I, xd,
-                                                 ystack), 20, torch)
+    # seven rounds of five launches, the median round (single rounds of this
+    # 412 MB stream spread by 10-20 %)
+    rounds = [time_launches(lambda i: qt.qt_matvec_i3(packs.view(-1), scs.view(-1), Ostack, I,
+                                                      xd, ystack), 5, torch, warmup=1)
+              for _ in range(7)]
+    ms = float(np.median(rounds))
     gbs = stack_bytes / (ms * 1e-3) / 1e9
     legs["gemv_stacked_one_launch"] = {
-        "us": round(ms * 1e3, 2), "GB_s": round(gbs, 1), "bound": "hbm",
+        "us": round(ms * 1e3, 2),
+        "us_rounds_min_max": [round(min(rounds) * 1e3, 2), round(max(rounds) * 1e3, 2)],
+        "GB_s": round(gbs, 1), "bound": "hbm",
         "frac": round(gbs / HBM_PEAK_GBS, 4), "O": Ostack, "I": I,
         "bytes_per_launch": int(stack_bytes), "traffic": traffic_for("gemv_stacked", stack_bytes)}
     log(f"leg gemv_stacked_one_launch: {legs['gemv_stacked_one_launch']}")
