@@ -561,26 +561,47 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
         read_x();
         mul_tile(blockIdx.x, 0, cur, cs);
     } else {
-        // the next three tiles' weights in flight while this one is multiplied
-        GroupBits<BITS> n1[NG], n2[NG], n3[NG];
-        float s1[NG], s2[NG], s3[NG];
+        // a ring of four tiles' weights: the next three in flight while one
+        // is multiplied.  The loop is unrolled by the ring's size, so every
+        // step names its buffers statically: rotating them by copies instead
+        // made each copy of a register still being loaded wait for that load,
+        // and the loop head waited for every load in flight.
+        //   Every step issues the same loads, so the compiler can tell which
+        // are still in flight and waits only for the tile it multiplies:
+        // lanes past G and rows past O load a valid group (unused), and
+        // steps past the block's last tile re-read that tile (unused; its
+        // lines were just read).
+        GroupBits<BITS> ring[4][NG];
+        float rs[4][NG];
         const int step = gridDim.x;
         int tile = blockIdx.x;
-        load_tile(tile, cur, cs);
-        if (tile + step < ntiles) load_tile(tile + step, n1, s1);
-        if (tile + 2 * step < ntiles) load_tile(tile + 2 * step, n2, s2);
-        read_x();
-        for (int it = 0; tile < ntiles; tile += step, ++it) {
-            if (tile + 3 * step < ntiles) load_tile(tile + 3 * step, n3, s3);
-            mul_tile(tile, it, cur, cs);
+        const int last = tile + (ntiles - 1 - tile) / step * step;  // this block's last tile
+        const int64_t tile_groups = (int64_t)kDecRows * G;          // groups of one tile
+        int64_t gi0[NG];  // group index of this lane's group in the block's first tile
+#pragma unroll
+        for (int m = 0; m < NG; ++m)
+            gi0[m] = (int64_t)min(tile * kDecRows + rl, O - 1) * G + min(q + 128 * m, G - 1);
+        auto load_ring = [&](int t, GroupBits<BITS> (&gb)[NG], float (&sc)[NG]) {
+            // rows of tile t past O: the block's first tile's row (unused)
+            const int64_t dt = t * kDecRows + rl < O ? (int64_t)(t - blockIdx.x) * tile_groups : 0;
 #pragma unroll
             for (int m = 0; m < NG; ++m) {
-                cur[m] = n1[m];
-                cs[m] = s1[m];
-                n1[m] = n2[m];
-                s1[m] = s2[m];
-                n2[m] = n3[m];
-                s2[m] = s3[m];
+                const int64_t gi = gi0[m] + dt;
+                gb[m] = load_group<BITS>(packed + gi * GroupBits<BITS>::kBytes);
+                sc[m] = scales[gi];
+            }
+        };
+        load_ring(tile, ring[0], rs[0]);
+        load_ring(min(tile + step, last), ring[1], rs[1]);
+        load_ring(min(tile + 2 * step, last), ring[2], rs[2]);
+        read_x();
+        for (int it = 0; tile < ntiles;) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                load_ring(min(tile + 3 * step, last), ring[(k + 3) % 4], rs[(k + 3) % 4]);
+                if (tile < ntiles) mul_tile(tile, it, ring[k], rs[k]);  // uniform
+                tile += step;
+                ++it;
             }
         }
     }
