@@ -569,8 +569,8 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
         //   Every step issues the same loads, so the compiler can tell which
         // are still in flight and waits only for the tile it multiplies:
         // lanes past G and rows past O load a valid group (unused), and
-        // steps past the block's last tile re-read that tile (unused; its
-        // lines were just read).
+        // steps past the block's last tile load group 0 in every lane
+        // (unused; one line, which stays cached).
         GroupBits<BITS> ring[4][NG];
         float rs[4][NG];
         const int step = gridDim.x;
@@ -586,19 +586,19 @@ __global__ __launch_bounds__(1024) void gemv_decode_kernel(
             const int64_t dt = t * kDecRows + rl < O ? (int64_t)(t - blockIdx.x) * tile_groups : 0;
 #pragma unroll
             for (int m = 0; m < NG; ++m) {
-                const int64_t gi = gi0[m] + dt;
+                const int64_t gi = t <= last ? gi0[m] + dt : 0;
                 gb[m] = load_group<BITS>(packed + gi * GroupBits<BITS>::kBytes);
                 sc[m] = scales[gi];
             }
         };
         load_ring(tile, ring[0], rs[0]);
-        load_ring(min(tile + step, last), ring[1], rs[1]);
-        load_ring(min(tile + 2 * step, last), ring[2], rs[2]);
+        load_ring(tile + step, ring[1], rs[1]);
+        load_ring(tile + 2 * step, ring[2], rs[2]);
         read_x();
         for (int it = 0; tile < ntiles;) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                load_ring(min(tile + 3 * step, last), ring[(k + 3) % 4], rs[(k + 3) % 4]);
+                load_ring(tile + 3 * step, ring[(k + 3) % 4], rs[(k + 3) % 4]);
                 if (tile < ntiles) mul_tile(tile, it, ring[k], rs[k]);  // uniform
                 tile += step;
                 ++it;
