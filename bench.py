@@ -116,12 +116,31 @@ def valu_roofline(cnt, ms):
 
 
 MOE_ROUNDS, MOE_CALLS = 9, 4  # interleaved timing rounds of the MoE steps
+SETTLE_S = 1.0  # untimed sustained run before a leg is timed
 
 
-def time_launches(fn, n, torch, warmup=2):
+def settle(fns, torch, seconds=SETTLE_S):
+    """Run the leg's own work (each fn in turn) for about `seconds`, untimed:
+    a sustained load runs at a drifting rate for its first second or so (the
+    clock and power settling after the host-side set-up of the leg), so the
+    timed rounds start from the steady state."""
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while True:
+        for fn in fns:
+            fn(i)
+        i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
+
+
+def time_launches(fn, n, torch, warmup=2, settle_s=0.0):
     """Average time per fn() call over n back-to-back calls, from a pair of
     events on the current stream (the stream the kernels run on), after
-    `warmup` untimed calls."""
+    `warmup` untimed calls (and, with settle_s, a sustained untimed run)."""
+    if settle_s > 0:
+        settle([fn], torch, settle_s)
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i in range(warmup):
@@ -229,10 +248,13 @@ def main():
     Ostack = O * N_COPIES
     ystack = torch.empty(Ostack, dtype=torch.float32, device=dev)
     stack_bytes = packs.numel() + scs.numel() * 4 + I * 4 + Ostack * 4
-    for _ in range(3):
-        qt.qt_matvec_i3(packs.view(-1), scs.view(-1), Ostack, I, xd, ystack)
-    # seven rounds of five launches, the median round (single rounds of this
-    # 412 MB stream spread by 10-20 %)
+    # untimed warm-up: the first second or so of a sustained stream like this
+    # one runs at a drifting rate (113-140 us per launch, then a steady
+    # 106-109 us on the same data), while short launches like the decode
+    # graph's hold their rate from the start
+    settle([lambda i: qt.qt_matvec_i3(packs.view(-1), scs.view(-1), Ostack, I, xd, ystack)],
+           torch, 1.5)
+    # seven rounds of five launches, the median round
     rounds = [time_launches(lambda i: qt.qt_matvec_i3(packs.view(-1), scs.view(-1), Ostack, I,
                                                       xd, ystack), 5, torch, warmup=1)
               for _ in range(7)]
@@ -411,9 +433,7 @@ def moe_layer_leg(torch, qt, workloads, dev, legs):
         return step, sum(a[0].shape[1] + a[1][0].numel() * 4 for a in (g, u, d))
 
     fns = {name: make_step(*bits) for name, bits in schemes}
-    for fn, _ in fns.values():
-        for i in range(3):
-            fn(i)
+    settle([fn for fn, _ in fns.values()], torch)
     rounds = {name: [] for name in fns}  # interleaved, as the MoE steps
     for r in range(MOE_ROUNDS):
         for name, (fn, _) in fns.items():
@@ -446,14 +466,14 @@ def gptq_leg(torch, qt, workloads, dev, legs):
     ws = torch.empty(qt.qt_hessian_full_workspace_bytes(T, I, qt.QT_BF16), dtype=torch.uint8,
                      device=dev)
     qt.qt_hessian_full(Xd, H, workspace=ws)
-    ms_h = time_launches(lambda i: qt.qt_hessian_full(Xd, H, workspace=ws), 3, torch)
+    ms_h = time_launches(lambda i: qt.qt_hessian_full(Xd, H, workspace=ws), 3, torch,
+                        settle_s=SETTLE_S)
     del ws, Xd
     fl_h = T * I * (I + 1)  # the symmetric product: T I (I + 1) / 2 multiply-adds
     U = torch.empty((I, I), dtype=torch.float32, device=dev)
     info = torch.empty(1, dtype=torch.int32, device=dev)
     ws = torch.empty(qt.qt_gptq_factor_workspace_bytes(I), dtype=torch.uint8, device=dev)
-    qt.qt_gptq_factor(H, 0.01, U, info, workspace=ws)
-    torch.cuda.synchronize()
+    settle([lambda i: qt.qt_gptq_factor(H, 0.01, U, info, workspace=ws)], torch)
     t0 = time.perf_counter()
     qt.qt_gptq_factor(H, 0.01, U, info, workspace=ws)
     torch.cuda.synchronize()
@@ -469,14 +489,15 @@ def gptq_leg(torch, qt, workloads, dev, legs):
     c = torch.empty((O, I), dtype=torch.int8, device=dev)
     ws = torch.empty(qt.qt_gptq_workspace_bytes(O, I), dtype=torch.uint8, device=dev)
     qt.qt_gptq_i3(Wd, U, s, c, workspace=ws)
-    ms_s = time_launches(lambda i: qt.qt_gptq_i3(Wd, U, s, c, workspace=ws), 2, torch, warmup=0)
+    ms_s = time_launches(lambda i: qt.qt_gptq_i3(Wd, U, s, c, workspace=ws), 2, torch, warmup=0,
+                         settle_s=SETTLE_S)
     fl_s = O * I * I  # block propagation: sum over blocks of 2 O 128 (I - b1)
     del ws
     p = qt.qt_pack_i3(c)
     ws = torch.empty(qt.qt_gptq_proxy_workspace_bytes(O, I), dtype=torch.uint8, device=dev)
     terms = qt.qt_gptq_proxy(Wd, p, s, H, workspace=ws)
     ms_p = time_launches(lambda i: qt.qt_gptq_proxy(Wd, p, s, H, terms, workspace=ws), 2, torch,
-                         warmup=0)
+                         warmup=0, settle_s=SETTLE_S)
     fl_p = 2 * 2 * O * I * I
     s0, c0, _ = qt.qt_quantize_g64(Wd, want_grid_idx=False)
     t_rtn = qt.qt_gptq_proxy(Wd, qt.qt_pack_i3(c0), s0, H, workspace=ws).cpu().numpy()
@@ -512,8 +533,9 @@ def int4_leg(torch, qt, workloads, dev, legs, args):
     p = qt.qt_pack_i4(c)
     torch.cuda.synchronize()
     ms_q = time_launches(lambda i: qt.qt_quantize_g64_i4(Wd, scales=s, codes=c,
-                                                         want_grid_idx=False), 20, torch)
-    ms_p = time_launches(lambda i: qt.qt_pack_i4(c, p), 50, torch)
+                                                         want_grid_idx=False), 20, torch,
+                         settle_s=SETTLE_S)
+    ms_p = time_launches(lambda i: qt.qt_pack_i4(c, p), 50, torch, settle_s=SETTLE_S)
     packs = torch.empty((N_COPIES, p.numel()), dtype=torch.uint8, device=dev)
     scs = torch.empty((N_COPIES, O, G), dtype=torch.float32, device=dev)
     packs.copy_(p.expand(N_COPIES, -1))
@@ -547,12 +569,13 @@ def quant_leg(torch, qt, workloads, dev, legs):
     c = torch.empty((O, I), dtype=torch.int8, device=dev)
     p = torch.empty(qt.qt_packed_bytes(O, I), dtype=torch.uint8, device=dev)
     ms = time_launches(lambda i: qt.qt_quantize_g64(Wd, None, 0, scales=s, codes=c,
-                                                   want_grid_idx=False), 50, torch)
+                                                   want_grid_idx=False), 50, torch,
+                       settle_s=SETTLE_S)
     bytes_q = O * I * 4 + O * I + O * G * 4
     legs["quantize_rtn_decode"] = {"ms": round(ms, 5), "groups_per_s": round(O * G / (ms * 1e-3)),
                                    "GB_s": round(bytes_q / (ms * 1e-3) / 1e9, 1),
                                    "bound": "hbm", "frac": round(bytes_q / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    ms = time_launches(lambda i: qt.qt_pack_i3(c, p), 50, torch)
+    ms = time_launches(lambda i: qt.qt_pack_i3(c, p), 50, torch, settle_s=SETTLE_S)
     bytes_p = O * I + p.numel()
     legs["pack_decode"] = {"ms": round(ms, 5), "GB_s": round(bytes_p / (ms * 1e-3) / 1e9, 1),
                            "bound": "hbm", "frac": round(bytes_p / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -569,7 +592,8 @@ def search_leg(torch, qt, workloads, dev, legs):
     T, I = Xd.shape
     d = torch.empty(I, dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, qt.qt_hessian_workspace_bytes(T, I)), dtype=torch.uint8, device=dev)
-    ms = time_launches(lambda i: qt.qt_hessian_diag(Xd, d, workspace=ws), 20, torch)
+    ms = time_launches(lambda i: qt.qt_hessian_diag(Xd, d, workspace=ws), 20, torch,
+                       settle_s=SETTLE_S)
     hb = T * I * 4 + I * 4
     legs["hessian_diag"] = {"ms": round(ms, 5), "GB_s": round(hb / (ms * 1e-3) / 1e9, 1),
                             "bound": "hbm", "frac": round(hb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -585,7 +609,7 @@ def search_leg(torch, qt, workloads, dev, legs):
     k = torch.empty((O, G), dtype=torch.uint8, device=dev)
     qt.qt_quantize_g64(Wd, d, 64, 0.5, 1.0, scales=s, codes=c, grid_idx=k)
     ms = time_launches(lambda i: qt.qt_quantize_g64(Wd, d, 64, 0.5, 1.0, scales=s, codes=c,
-                                                   grid_idx=k), 3, torch)
+                                                   grid_idx=k), 3, torch, settle_s=SETTLE_S)
     ngroups = O * G
     # per group: 64 candidates x 64 slots x 9 operations (divide, round, max,
     # min, multiply, subtract, multiply, multiply, add)
@@ -599,7 +623,7 @@ def search_leg(torch, qt, workloads, dev, legs):
     # two-stage signed search: 2 x 64 signed candidates, then 32 refinement points
     qt.qt_quantize_g64_signed(Wd, d, 64, 32, 0.5, 1.0, scales=s, codes=c)
     ms = time_launches(lambda i: qt.qt_quantize_g64_signed(Wd, d, 64, 32, 0.5, 1.0, scales=s,
-                                                          codes=c), 3, torch)
+                                                          codes=c), 3, torch, settle_s=SETTLE_S)
     ops = ngroups * (2 * 64 + 32) * 64 * 9
     legs["quantize_search_signed"] = dict(
         {"ms": round(ms, 4), "groups_per_s": round(ngroups / (ms * 1e-3)),
@@ -668,9 +692,7 @@ def moe_leg(torch, qt, workloads, dev, legs, int3_step=True, int4_steps=False):
         return moe_step, per_exp
 
     fns = {name: make_step(bu, bd) for name, bu, bd in steps}
-    for fn, _ in fns.values():
-        for i in range(5):
-            fn(i)
+    settle([fn for fn, _ in fns.values()], torch)
     # the steps are timed in interleaved rounds (each round times every step
     # over MOE_CALLS calls), and each reports its median round: the GPU's
     # clock settles during the first hundreds of milliseconds of load, which
@@ -711,7 +733,8 @@ def prefill_leg(torch, qt, workloads, dev, legs):
     Y = torch.empty((B, O), dtype=torch.float32, device=dev)
     for i in range(3):
         qt.qt_matmul_i3(pp, sp, O, I, Xbd, Y)
-    ms = time_launches(lambda i: qt.qt_matmul_i3(pp, sp, O, I, Xbd, Y), 20, torch)
+    ms = time_launches(lambda i: qt.qt_matmul_i3(pp, sp, O, I, Xbd, Y), 20, torch,
+                       settle_s=SETTLE_S)
     flops = 2.0 * B * O * I
     tf = flops / (ms * 1e-3) / 1e12
     legs["prefill_gemm"] = {"ms": round(ms, 4), "TFLOP_s": round(tf, 1), "bound": "mfma",
