@@ -15,12 +15,16 @@
 // at a time; wave w owns tokens [32w, 32w+32) against all 144 rows (2 x 9 MFMA
 // tiles of 16x16, two 32-deep MFMAs per tile and group).
 //   * Weights: the group's 144 x 64 codes are dequantized once per block into
-//     LDS as bf16 in natural k order (one 16-code quarter per task:
-//     byte-parallel unpack, then v_perm_b32 table lookups), with the 144
-//     scales; every wave reads its B operands from there.
+//     LDS as bf16 (one 16-code quarter per task: byte-parallel unpack, then
+//     v_perm_b32 table lookups), with the 144 scales; every wave reads its B
+//     operands from there.  The tile is laid out in operand order: the 16 B
+//     that lane l takes for row tile nt and 32-deep step ks sit at slot
+//     (2 nt + ks) * 64 + l, so each operand read is one contiguous 1 KB, and
+//     wave w dequantizes row tile w, 16 lanes per contiguous 256 B.
 //   * Activations never touch LDS: each lane loads its A-operand slices
 //     (8 consecutive bf16 of one token) straight from global memory into
-//     registers with buffer loads, one group ahead.  Tokens past the batch and
+//     registers with buffer loads, two groups ahead (one on the element-load
+//     path for unaligned rows).  Tokens past the batch and
 //     inputs past the row use an offset outside the buffer, for which the
 //     hardware returns zeros.
 // Double-buffered LDS, one barrier per group; packed weights are fetched two
@@ -45,8 +49,7 @@ constexpr int NTN = BN / 16;            // MFMA tiles along the rows
 constexpr int NTM = 2;                  // MFMA tiles along the tokens, per wave
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int ROWB = 64 * 2 + 16;       // LDS bytes per 64-element row (+16: conflict-free reads)
-constexpr int WS_BYTES = BN * ROWB;     // one dequantized-weight buffer
+constexpr int WS_BYTES = BN * 64 * 2;   // one dequantized-weight buffer (bf16, operand order)
 constexpr int kWTasks = BN * 4;         // 16-code quarters of weights per group (576)
 constexpr int kWPer = (kWTasks + kThreads - 1) / kThreads;  // 2 (the second: wave 0 only)
 constexpr uint32_t kOutside = 0x80000000u;  // buffer offset that reads as zero
@@ -188,18 +191,23 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
         reinterpret_cast<u32x2_t*>(raw[slot])[tid] = rl.w;
         rawsc[slot][tid] = rl.s;
     };
-    // dequantize task i (quarter q of tile row n) from raw slot into LDS
-    // buffer buf; the four lanes of a row all write its scale
+    // dequantize task i from raw slot into LDS buffer buf.  The 64 tasks of
+    // chunk c = task / 64 are the quarters q = (task % 64) / 16 of the rows
+    // n = 16 c + task % 16 (row tile c).  Codes 16q..16q+7 and 16q+8..16q+15
+    // are the operand slices h4 = 2 (q & 1) and 2 (q & 1) + 1 of step
+    // ks = q / 2; the four lanes of a row all write its scale.
     auto store_task = [&](int buf, int slot, int i) {
         const int task = tid + kThreads * i;
-        const int n = task >> 2, q = task & 3;
+        const int c = task >> 6, q = (task >> 4) & 3, r16 = task & 15;
+        const int n = 16 * c + r16;
         const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw[slot]) + 6 * n;
         const uint32_t lo = rw[q], hw = rw[4 + (q >> 1)];
         u32x4_t lo8, hi8;
         dequant_quarter(lo, (hw >> (16 * (q & 1))) & 0xFFFFu, lo8, hi8);
-        uint8_t* r = &ws[buf][n * ROWB + 32 * q];
-        *reinterpret_cast<u32x4_t*>(r) = lo8;
-        *reinterpret_cast<u32x4_t*>(r + 16) = hi8;
+        u32x4_t* r = reinterpret_cast<u32x4_t*>(ws[buf]) + (2 * c + (q >> 1)) * 64 +
+                     32 * (q & 1) + r16;
+        r[0] = lo8;
+        r[16] = hi8;
         ss[buf][n] = rawsc[slot][n];
     };
     static_assert(kWPer == 2 && kThreads <= kWTasks && kWTasks - kThreads <= 64,
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     // every MFMA, so the FMAs and the dequantization fill the matrix core's
     // shadow.
     auto step = [&](int cb, const ALoad& a) {
-        const uint8_t* wb = &ws[cb][l16 * ROWB + 16 * h4];
+        const u32x4_t* wb = reinterpret_cast<const u32x4_t*>(ws[cb]) + lane;
         const float* sb = &ss[cb][l16];
         bf16x8_t aop[NTM][2];
 #pragma unroll
@@ -228,9 +236,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) aop[mt][ks] = __builtin_bit_cast(bf16x8_t, a.v[mt][ks]);
         auto read_b = [&](int nt, bf16x8_t (&bb)[2]) {
-            const uint8_t* wr = wb + nt * 16 * ROWB;
-            bb[0] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(wr));
-            bb[1] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(wr + 64));
+            bb[0] = __builtin_bit_cast(bf16x8_t, wb[(2 * nt) * 64]);
+            bb[1] = __builtin_bit_cast(bf16x8_t, wb[(2 * nt + 1) * 64]);
         };
         float sc[NTN];
 #pragma unroll
@@ -280,15 +287,23 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     // Software pipeline.  Step k: the A slices of group k are in registers
     // and its weights in LDS buffer k&1; the raw weights of group k+1 wait in
     // raw slot (k+1)&1 and those of k+2 in registers.  It issues the loads of
-    // A(k+1) and of the raw weights of k+3, multiplies group k, dequantizes
-    // k+1 into the other buffer and parks the raw weights of k+2 in slot k&1.
-    // The loop body is straight-line (prefetches past the last group re-read
-    // group G-1 and land where nobody reads): loads issued under conditions
-    // keep the compiler from telling which are still in flight.
-    ALoad a0, a1;
+    // A(k+kAhead) and of the raw weights of k+3, multiplies group k,
+    // dequantizes k+1 into the other buffer and parks the raw weights of k+2
+    // in slot k&1.  With 16-byte activation loads the A slices come from a
+    // ring of three, two groups in flight (a load waits for the loads issued
+    // before it, raw weights from HBM among them): 3 % faster at the prefill
+    // shape than one group ahead.  The element-load path keeps one group in
+    // flight, which fits its registers.  The loop is unrolled so that every
+    // ring slot is a fixed register set, and its body is straight-line
+    // (prefetches past the last group re-read group G-1 and land where nobody
+    // reads): loads issued under conditions keep the compiler from telling
+    // which are still in flight.
+    constexpr int kAhead = VEC ? 2 : 1;
+    ALoad a0, a1, a2;
     RawLoad ra, rb;
     const int32_t glast = G - 1;
     load_a(0, a0);
+    if constexpr (kAhead == 2) load_a(min(1, glast), a1);
     load_raw(0, ra);
     load_raw(min(1, glast), rb);
     write_raw(0, ra);
@@ -298,21 +313,33 @@ __global__ __launch_bounds__(kThreads) void gemm_i3_mfma_kernel(
     if (wave == 0) store_task(0, 0, 1);
     load_raw(min(2, glast), ra);
     lds_barrier();
-    for (int32_t g = 0;; g += 2) {
-        load_a(min(g + 1, glast), a1);
-        load_raw(min(g + 3, glast), rb);
-        step(0, a0);
-        if (wave == 0) store_task(1, 1, 1);
-        write_raw(0, ra);
+    // group g (LDS buffer cb = g & 1) with A slices acur; A(g+kAhead) into
+    // anext, raw(g+3) into rload; rwrite holds raw(g+2).  True after the
+    // last group.
+    auto group = [&](int32_t g, int cb, const ALoad& acur, ALoad& anext, RawLoad& rload,
+                     const RawLoad& rwrite) {
+        load_a(min(g + kAhead, glast), anext);
+        load_raw(min(g + 3, glast), rload);
+        step(cb, acur);
+        if (wave == 0) store_task(1 - cb, 1 - cb, 1);
+        write_raw(cb, rwrite);
         lds_barrier();
-        if (g + 1 >= G) break;
-        load_a(min(g + 2, glast), a0);
-        load_raw(min(g + 4, glast), ra);
-        step(1, a1);
-        if (wave == 0) store_task(0, 0, 1);
-        write_raw(1, rb);
-        lds_barrier();
-        if (g + 2 >= G) break;
+        return g + 1 >= G;
+    };
+    if constexpr (kAhead == 2) {
+        for (int32_t g = 0;; g += 6) {
+            if (group(g + 0, 0, a0, a2, rb, ra)) break;
+            if (group(g + 1, 1, a1, a0, ra, rb)) break;
+            if (group(g + 2, 0, a2, a1, rb, ra)) break;
+            if (group(g + 3, 1, a0, a2, ra, rb)) break;
+            if (group(g + 4, 0, a1, a0, rb, ra)) break;
+            if (group(g + 5, 1, a2, a1, ra, rb)) break;
+        }
+    } else {
+        for (int32_t g = 0;; g += 2) {
+            if (group(g + 0, 0, a0, a1, rb, ra)) break;
+            if (group(g + 1, 1, a1, a0, ra, rb)) break;
+        }
     }
 
     // C layout of a 16x16 tile: register r of lane l holds token row

@@ -294,9 +294,12 @@ def test_matmul_bf16_small_batch_exact_path(B):
     assert componentwise_err(Y, yr, ar) <= TOL_F32
 
 
+# The 16-byte-load path runs its group loop in rounds of six; G = 1, 2, 3,
+# 5, 6, 7, 10, 16 and 112 end a round at every position.
 @pytest.mark.parametrize("B,O,I", [(16, 128, 64), (17, 200, 300), (130, 129, 640),
                                    (300, 64, 1000), (256, 256, 7168), (33, 40, 68),
-                                   (20, 31, 5)])
+                                   (20, 31, 5), (24, 48, 128), (40, 96, 192),
+                                   (260, 150, 320), (64, 80, 384), (18, 144, 448)])
 def test_matmul_bf16_mfma_path(B, O, I):
     so, po = _packed_for(O, I, seed=B + O + I)
     Xb = workloads.bf16_bits_rne(workloads.generic_matrix(B, I, seed=B + I))
