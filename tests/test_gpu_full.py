@@ -9,6 +9,9 @@ products are compared on outputs the oracle computes one by one (all 256
 prefill slab).  The oracle runs on a pool of host threads: each call is a C
 function reached through ctypes, which releases the interpreter lock.
 
+The full Hessian of the GPTQ leg (bf16 X[8192x17408]) is compared on a
+64 x 64 block of H whose rows and columns straddle its 256-wide tile borders.
+
 Decode (W[2048x7168] and the 7200 tail variant) is compared in full in
 test_gpu_parity.py.
 """
@@ -192,3 +195,28 @@ def test_search_and_hessian_full_size():
         assert a, f"signed scales differ in rows {slabs[i]}"
         assert b, f"signed codes differ in rows {slabs[i]}"
     say(f"  all {O} rows bit-exact; negative scales {np.mean(s2 < 0):.3f}")
+
+
+def test_hessian_full_full_size():
+    # H = X^T X of the GPTQ leg's bf16 X[8192x17408]: the oracle's Hessian of
+    # 64 chosen columns is the 64 x 64 block of H on those rows and columns
+    I = workloads.SEARCH_SHAPE[1]
+    say(f"full Hessian: bf16 X[{workloads.SEARCH_TOKENS}x{I}]")
+    Xb = workloads.bf16_bits_rne(workloads.search_x())
+    Hd = qt.qt_hessian_full(dev_bf16(Xb))
+    edges = [0, 1, 255, 256, 257, 511, 512, 8191, 8192, 8447, 8448, 17151, 17152, 17406, 17407]
+    rng = np.random.default_rng(17408)
+    rest = rng.choice(np.setdiff1d(np.arange(I), edges), 64 - len(edges), replace=False)
+    cols = np.sort(np.concatenate([edges, rest]))
+    idx = torch.from_numpy(cols).to(Hd.device)
+    Hs = host(Hd.index_select(0, idx).index_select(1, idx))
+    del Hd
+    Xf = workloads.bf16_bits_to_f32(np.ascontiguousarray(Xb[:, cols]))
+    del Xb
+    Href = oracle.hessian_full(Xf)
+    A = np.abs(Xf.astype(np.float64))
+    bound = A.T @ A
+    err = np.abs(Hs.astype(np.float64) - Href) / np.maximum(bound, 1e-300)
+    say(f"  64 x 64 block: max componentwise err {err.max():.3e}")
+    assert err.max() <= 2e-5
+    assert np.array_equal(bits(Hs), bits(np.ascontiguousarray(Hs.T))), "not exactly symmetric"

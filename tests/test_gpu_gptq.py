@@ -27,7 +27,7 @@ def correlated_x(T, I, seed):
 
 # ---------------------------------------------------------------- full Hessian
 @pytest.mark.parametrize("T,I", [(100, 64), (300, 200), (1000, 333), (64, 1), (129, 513),
-                                 (7, 130)])
+                                 (7, 130), (520, 600), (200, 1100)])
 @pytest.mark.parametrize("xt", ["f32", "bf16"])
 def test_hessian_full(T, I, xt):
     X = correlated_x(T, I, T + I)
