@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const void* __restric
         }
 }
 
-// ---- bf16: 256 x 256 tiles from LDS-direct operand stages
+// ---- bf16: 256 x 256 tiles, operand stages through registers into LDS
 constexpr int kBT = 256;                 // output tile
 constexpr int kBThreads = 512;           // 8 waves: 2 (rows) x 4 (columns), 128 x 64 each
 constexpr int kBK = 32;                  // tokens per stage (one MFMA step)
@@ -299,7 +299,8 @@ __global__ __launch_bounds__(kBThreads) void syrk_bf16_kernel(const uint16_t* __
     // a stage's 16 bytes per lane and block, in registers between its loads
     // and its stores into the stage's LDS slot.  Every step loads one stage,
     // so each wave always has the same number of loads in flight; stages
-    // past the end re-read the last one and are never stored.
+    // past the end re-read the last one (the last step stores one of them
+    // into the slot not being read, which nobody reads again).
     struct Stage {
         u32x4_t v[4];
     };
