@@ -426,7 +426,9 @@ qt_status qt_moe_layer(const float* X, int64_t T, int64_t D, int64_t F, const fl
 
 // ---------------------------------------------------------------- GPTQ
 size_t qt_hessian_full_workspace_bytes(int64_t T, int64_t I, qt_dtype xt) {
-    if (T < 1 || I < 1 || I > 65535 * 128LL || (xt != QT_F32 && xt != QT_BF16)) return 0;
+    // rows pad to a multiple of 256 and the f32 kernel takes 128-row tiles on
+    // a grid of at most 65535 x 65535
+    if (T < 1 || I < 1 || I > 32767 * 256LL || (xt != QT_F32 && xt != QT_BF16)) return 0;
     const int64_t b = mul3(qt::hessian_full_rows(I), qt::hessian_full_tokens(T),
                            xt == QT_F32 ? 4 : 2);
     return b < 0 ? 0 : (size_t)b;
@@ -436,7 +438,7 @@ qt_status qt_hessian_full(const void* X, qt_dtype xt, int64_t T, int64_t I, floa
                           int accumulate, void* workspace, size_t ws_bytes, void* stream) {
     if (!X || !H || !workspace) return QT_ERR_NULL;
     if (xt != QT_F32 && xt != QT_BF16) return QT_ERR_DTYPE;
-    if (T < 1 || I < 1 || I > 65535 * 128LL) return QT_ERR_SHAPE;
+    if (T < 1 || I < 1 || I > 32767 * 256LL) return QT_ERR_SHAPE;
     const int64_t esz = xt == QT_F32 ? 4 : 2;
     const int64_t xb = mul3(T, I, esz), hb = mul3(I, I, 4);
     if (xb < 0 || hb < 0) return QT_ERR_SHAPE;

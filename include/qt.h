@@ -315,7 +315,7 @@ qt_status qt_matvec_i4_grouped(const uint8_t* packed, const float* scales,
  * the T rows of X of x^T x, or H += that (accumulate = 1).  X [T x I] f32 or
  * bf16 (16-byte aligned).  bf16 products are exact (f32 sums); f32 inputs use
  * the f32 matrix cores.  workspace: qt_hessian_full_workspace_bytes(T, I, xt)
- * bytes (16-byte aligned; holds the transposed, padded X).  I <= 8388480.
+ * bytes (16-byte aligned; holds the transposed, padded X).  I <= 8388352.
  */
 size_t qt_hessian_full_workspace_bytes(int64_t T, int64_t I, qt_dtype xt);
 qt_status qt_hessian_full(const void* X, qt_dtype xt, int64_t T, int64_t I, float* H,

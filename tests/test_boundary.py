@@ -117,6 +117,25 @@ def test_matvec_rejects():
     assert f(A, B, 4, 64, Cc, Cc + 4, None) == QT_ERR_ALIAS
 
 
+def test_hessian_full_limits_and_rejects():
+    # rows pad to 256 and the f32 kernel's 128-row tiles fit a 65535-wide grid
+    lim = 32767 * 256
+    assert qt.qt_hessian_full_workspace_bytes(100, 300, 0) == 512 * 128 * 4
+    assert qt.qt_hessian_full_workspace_bytes(64, lim, 1) == lim * 64 * 2
+    assert qt.qt_hessian_full_workspace_bytes(64, lim + 1, 1) == 0
+    assert qt.qt_hessian_full_workspace_bytes(0, 64, 1) == 0
+    f = L.qt_hessian_full
+    ws = 1 << 30
+    assert f(None, 1, 64, 64, B, 0, Cc, ws, None) == QT_ERR_NULL
+    assert f(A, 1, 64, 64, None, 0, Cc, ws, None) == QT_ERR_NULL
+    assert f(A, 7, 64, 64, B, 0, Cc, ws, None) == QT_ERR_DTYPE
+    assert f(A, 1, 0, 64, B, 0, Cc, ws, None) == QT_ERR_SHAPE
+    assert f(A, 1, 64, lim + 1, B, 0, Cc, ws, None) == QT_ERR_SHAPE
+    assert f(A, 1, 64, 64, B, 2, Cc, ws, None) == QT_ERR_ARG
+    assert f(A, 1, 64, 64, B, 0, Cc, 100, None) == QT_ERR_WORKSPACE
+    assert f(A + 2, 1, 64, 64, B, 0, Cc, ws, None) == QT_ERR_ALIGN
+
+
 def test_matmul_rejects():
     f = L.qt_matmul_i3
     assert f(A, B, 4, 64, None, 0, 2, D, None) == QT_ERR_NULL
