@@ -257,3 +257,11 @@ def test_hessian_noalloc_rejects():
     assert qt.qt_hessian_workspace_bytes(128 * 128, 32768) == 16 << 20
     assert f(A, 0, 128 * 128, 32769, B, 0, None) == QT_ERR_SCRATCH
     assert "scratch" in qt.qt_status_str(QT_ERR_SCRATCH)
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    # no fallback: without libqt.so every call raises instead of computing
+    monkeypatch.setattr(qtmod, "_SO", str(tmp_path / "libqt.so"))
+    monkeypatch.setattr(qtmod, "_lib", None)
+    with pytest.raises(ImportError):
+        qtmod.qt_groups(64)
