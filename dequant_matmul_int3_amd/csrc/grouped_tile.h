@@ -208,7 +208,7 @@ __device__ __forceinline__ void token_rows(const int32_t* trow, const float* __r
 // outside the row since I % 4 == 0; one past the row reads the row's first
 // inputs instead (zeroed when stored).
 template <int BITS, int CG, bool XV, bool FULL>
-__device__ __forceinline__ void load_sx(SxRegs<CG>& c, const SxRoles<CG>& ro, int32_t c0, int nt,
+__device__ __forceinline__ void load_sx(SxRegs<CG>& c, const SxRoles<CG>& ro, int32_t c0,
                                         const float* const (&xrow)[kTok], int32_t I, int32_t G,
                                         int tid) {
     constexpr int E = kXPer<CG>;
@@ -220,9 +220,12 @@ __device__ __forceinline__ void load_sx(SxRegs<CG>& c, const SxRoles<CG>& ro, in
     // offset of input k of the chunk from the chunk's start (clamped: past
     // the row, the row's first input)
     auto at = [&](int k) { return FULL || (int64_t)k0 + k < I ? k : -k0; };
+    // Every token slot loads (slots past nt read token 0's row, unused): with
+    // an early exit at nt the compiler copied the loaded registers between
+    // the exit paths, and such a copy waits for every load in flight, the
+    // next chunk's weights included, before the multiply could start.
 #pragma unroll
     for (int t = 0; t < kTok; ++t) {
-        if (t >= nt) break;  // uniform
         const float* src = xrow[t] + k0;  // uniform
         if constexpr (XV && BITS == 4 && E == 4) {
             const float4 v = *reinterpret_cast<const float4*>(src + at(4 * tid));
@@ -472,13 +475,13 @@ __device__ __forceinline__ void grouped_tile(
     const float* xrow[kTok];
     // loads of chunk c0 into registers, and their stores to LDS, with the
     // clamping of a short last chunk only where it is one (a uniform branch)
-    auto load_chunk = [&](int32_t c0, int nt) {
+    auto load_chunk = [&](int32_t c0) {
         if (is_full(c0)) {
             load_w(c0, std::true_type{});
-            load_sx<BITS, CG, XV, true>(sx, ro, c0, nt, xrow, I, G, tid);
+            load_sx<BITS, CG, XV, true>(sx, ro, c0, xrow, I, G, tid);
         } else {
             load_w(c0, std::false_type{});
-            load_sx<BITS, CG, XV, false>(sx, ro, c0, nt, xrow, I, G, tid);
+            load_sx<BITS, CG, XV, false>(sx, ro, c0, xrow, I, G, tid);
         }
     };
     auto store_chunk = [&](int32_t c0, int nt) {
@@ -499,13 +502,13 @@ __device__ __forceinline__ void grouped_tile(
 
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         token_rows(L.trow, X, I, nt, xrow);
-        load_chunk(0, nt);
+        load_chunk(0);
         for (int32_t c0 = 0; c0 < G; c0 += kCG) {
             __syncthreads();  // everyone is done with the previous chunk
             store_chunk(c0, nt);
             __syncthreads();
             // next chunk in flight while this one is multiplied
-            if (c0 + kCG < G) load_chunk(c0 + kCG, nt);
+            if (c0 + kCG < G) load_chunk(c0 + kCG);
             mma_chunk<BITS, CG>(wl, L.pl, L.sl, min(kCG, G - c0), wave, l16, j4, acc);
         }
         store_rows<BITS>(acc, nt, L.tout, r0, O, wave, l16, j4, Y);
