@@ -549,7 +549,7 @@ def int4_leg(torch, qt, workloads, dev, legs, args):
     legs["gemv_decode_int4"] = {"us": round(ms * 1e3, 3), "GB_s": round(gbs, 1), "bound": "hbm",
                                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                                 "bytes_per_launch": int(bytes_step),
-                                "kernel": "gemv_batch_kernel<128,16,1,128,f32,vec,int4>"}
+                                "kernel": "gemv_decode1_kernel<4>"}
     legs["quantize_rtn_decode_int4"] = {"ms": round(ms_q, 5),
                                         "groups_per_s": round(O * G / (ms_q * 1e-3))}
     bytes_p = O * I + p.numel()
